@@ -1,0 +1,150 @@
+/*
+ * moedecode.h - C ABI of libmoedecode: the decode step of a fine-grained
+ * Mixture-of-Experts transformer layer on AMD MI355X (gfx950).
+ *
+ * The layer (per token t, activation x_t of width H):
+ *   xhat    = x_t / sqrt(mean(x_t^2) + eps) * gamma                 (RMSNorm)
+ *   l_e     = <Wr[e], xhat> (+ bias_e)        for all E experts      (router)
+ *   S       = the k largest l_e, ties to the lower e                 (top-k)
+ *   w_e     = softmax(l)_e / sum_{e' in S} softmax(l)_e'             (renormalised)
+ *   f_W(v)  = Wd (SiLU(Wg v) * (Wu v))                               (SwiGLU FFN)
+ *   y_t     = x_t + f_shared(xhat) + sum_{e in S} w_e f_e(xhat)
+ * Decode is a chain of normalisation, matmul, activation and routing ops
+ * (openai-hub.com "Kimi K3 ... 1.68x", section on why decode suits a
+ * megakernel); the MoE has router scores and a shared expert (smzdm.com
+ * post, section "what changed", MoE de-duplication item); Kimi K3 sends each
+ * token to 16 of its 896 experts (aiposthub.com article, section on what the
+ * K3 decode path changed); the specialised path covers decode batches 1-64
+ * and falls back to the stock path elsewhere (smzdm.com post, section on who
+ * can use it). The pages give no formula; the one above, its rounding points
+ * and tie rule are this library's reading of them.
+ *
+ * Precision: the router consumes fp32 xhat; the FFNs consume xhat rounded to
+ * the activation dtype; SiLU(g)*u is stored in the activation dtype; all dot
+ * products accumulate in fp32; y is rounded once to the activation dtype.
+ *
+ * Conventions for every entry point:
+ *   - Pointers inside moe_layer_weights, and x, y, the optional outputs and
+ *     the workspace, are DEVICE pointers (hipMalloc or torch memory) on the
+ *     current HIP device. desc, weights and the layers array are HOST structs,
+ *     read during the call only.
+ *   - The caller owns all memory. The library allocates nothing and does not
+ *     synchronise: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream) and pointers must stay valid until it completes.
+ *   - Validation is synchronous and happens before any launch. Errors are
+ *     returned as moe_status; moe_last_error() gives a thread-local detail.
+ *     Device errors of a launch return MOE_ERR_DEVICE.
+ *   - Layouts are row-major, [out][in]: the router [E][H]; expert gate/up
+ *     [E][2I][H] with the gate rows first, then the up rows; expert down
+ *     [E][H][I]; shared gate/up [2Is][H]; shared down [H][Is].
+ *   - All device pointers must be 16-byte aligned.
+ *   - The workspace must be zero-filled by the caller once, before the first
+ *     call that uses it; the library leaves it reusable (its barrier counters
+ *     are generation-based). Calls that share one workspace must not overlap
+ *     in time (enqueue them on one stream).
+ *   - y may be exactly x (in place); any other overlap between inputs and
+ *     outputs is an error.
+ *   - Routing outputs list each token's k experts by descending logit, ties
+ *     to the lower expert index; weights match that order and sum to 1.
+ */
+#ifndef MOEDECODE_H
+#define MOEDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,    /* null/misaligned pointer, bad size, partial overlap */
+  MOE_ERR_UNSUPPORTED = 2,         /* outside the envelope below: the caller falls back */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes < moe_workspace_bytes(...) */
+  MOE_ERR_DEVICE = 4,              /* a HIP call or kernel launch failed */
+  MOE_ERR_TIMEOUT = 5              /* a previous launch hit its grid-barrier watchdog */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Shape and dtypes of one layer (host struct).
+ * Envelope (else MOE_ERR_UNSUPPORTED):
+ *   hidden % 256 == 0, 256 <= hidden <= 16384; expert_inter % 128 == 0 and
+ *   <= 4096; shared_inter == 0 or a multiple of expert_inter (<= 8192);
+ *   1 <= top_k <= 32; top_k <= num_experts <= 1024; batch 1..64; layers 1..8;
+ *   dtype sets: {act F32, router F32, expert F32, shared F32},
+ *   {act BF16, router F32 or BF16, expert BF16, shared BF16},
+ *   {act BF16, router F32 or BF16, expert FP8_E4M3 with scale_group 128, shared BF16}. */
+typedef struct {
+  int32_t hidden;        /* H */
+  int32_t num_experts;   /* E */
+  int32_t top_k;         /* k */
+  int32_t expert_inter;  /* I: each routed expert's intermediate width */
+  int32_t shared_inter;  /* Is: the shared expert's intermediate width (0 = none) */
+  float rms_eps;         /* e.g. 1e-6 */
+  moe_dtype act;         /* x, y and gamma */
+  moe_dtype router;      /* router weight */
+  moe_dtype expert;      /* routed expert weights */
+  moe_dtype shared;      /* shared expert weights */
+  int32_t scale_group;   /* FP8 experts: output rows per bf16 scale (128); else 0 */
+} moe_layer_desc;
+
+/* Device pointers of one layer's weights (host struct). */
+typedef struct {
+  const void *rms_gamma;             /* [H], act dtype */
+  const void *router_w;              /* [E][H], router dtype */
+  const float *router_bias;          /* [E] fp32 added to the logits, or NULL */
+  const void *expert_gate_up;        /* [E][2I][H], expert dtype */
+  const void *expert_down;           /* [E][H][I], expert dtype */
+  const uint16_t *expert_gate_up_scale; /* FP8: bf16 [E][2I/scale_group]; else NULL */
+  const uint16_t *expert_down_scale;    /* FP8: bf16 [E][H/scale_group]; else NULL */
+  const void *shared_gate_up;        /* [2Is][H], shared dtype (NULL if Is == 0) */
+  const void *shared_down;           /* [H][Is], shared dtype (NULL if Is == 0) */
+} moe_layer_weights;
+
+/* Bytes of workspace needed for up to max_tokens tokens and num_layers layers
+ * of this shape; 0 if desc is invalid or outside the envelope. */
+size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens, int32_t num_layers);
+
+/* Routing only: RMSNorm + router + softmax/top-k/renormalisation for B tokens.
+ *   x        [B][H] act dtype
+ *   topk_idx [B][k] int32 out; topk_w [B][k] fp32 out
+ *   logits   [B][E] fp32 out (router logits incl. bias), or NULL
+ * One kernel launch on `stream`. */
+moe_status moe_route(const moe_layer_desc *desc, const moe_layer_weights *weights, const void *x,
+                     int32_t B, int32_t *topk_idx, float *topk_w, float *logits, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* The whole layer for B tokens in one persistent kernel launch:
+ *   x [B][H] act dtype in; y [B][H] act dtype out (y == x allowed);
+ *   topk_idx [B][k] / topk_w [B][k]: the routing used, or NULL. */
+moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *weights,
+                            const void *x, void *y, int32_t B, int32_t *topk_idx, float *topk_w,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* L layers of the same shape, each with its own weights (layers: host array of
+ * L structs), in one persistent launch: y = layer_{L-1}(... layer_0(x)), each
+ * layer's bf16 output feeding the next layer's RMSNorm. While a layer finishes,
+ * the kernel already streams the next layer's router and shared-expert weights.
+ *   topk_idx [L][B][k] / topk_w [L][B][k]: the routing of every layer, or NULL. */
+moe_status moe_decode_stack(const moe_layer_desc *desc, const moe_layer_weights *layers, int32_t L,
+                            const void *x, void *y, int32_t B, int32_t *topk_idx, float *topk_w,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* Synchronises `stream`, then reads and clears the workspace's error word:
+ * MOE_ERR_TIMEOUT if a launch on this workspace stopped at its barrier
+ * watchdog, MOE_OK otherwise. A debugging aid, not for the hot path. */
+moe_status moe_check_workspace(void *ws, size_t ws_bytes, void *stream);
+
+/* Static English name of a status. */
+const char *moe_status_string(moe_status status);
+
+/* Thread-local detail of the last non-OK status returned on this thread. */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEDECODE_H */

@@ -1,0 +1,112 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented statuses before
+any HIP call."""
+import ctypes
+import re
+
+import pytest
+
+import moe_decode_02_amd as md
+import synth
+from synth.device import desc_of
+
+
+@pytest.fixture(scope="module")
+def lib():
+    md.build(force=False)
+    return md.lib()
+
+
+def header_functions():
+    text = open(md.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert set(names) == set(md.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARGUMENT"), (2, "MOE_ERR_UNSUPPORTED"),
+                       (3, "MOE_ERR_WORKSPACE_TOO_SMALL"), (4, "MOE_ERR_DEVICE"), (5, "MOE_ERR_TIMEOUT")]:
+        assert md.moe_status_string(code) == name
+
+
+def test_workspace_bytes_and_envelope(lib):
+    d = desc_of(synth.WORKLOADS["k3_b1"])
+    n1 = md.moe_workspace_bytes(d, 1, 1)
+    n64 = md.moe_workspace_bytes(d, 64, 1)
+    n64s = md.moe_workspace_bytes(d, 64, 4)
+    assert 0 < n1 < n64 < n64s
+    assert md.moe_workspace_bytes(d, 0, 1) == 0
+    assert md.moe_workspace_bytes(d, 65, 1) == 0
+    assert md.moe_workspace_bytes(d, 1, 9) == 0
+    bad = desc_of(synth.WORKLOADS["k3_b1"])
+    bad.hidden = 7000
+    assert md.moe_workspace_bytes(bad, 1, 1) == 0
+    bad = desc_of(synth.WORKLOADS["k3_b1"])
+    bad.act = md.MOE_F32  # fp32 activations with bf16 experts: not a supported set
+    assert md.moe_workspace_bytes(bad, 1, 1) == 0
+
+
+FAKE = 1 << 40  # a 16-byte aligned address; validation fails before anything touches it
+
+
+def _weights():
+    return md.moe_layer_weights(FAKE, FAKE, None, FAKE, FAKE, None, None, FAKE, FAKE)
+
+
+@pytest.mark.parametrize("case,status", [
+    ("batch0", md.MOE_ERR_UNSUPPORTED), ("batch65", md.MOE_ERR_UNSUPPORTED),
+    ("misaligned_x", md.MOE_ERR_INVALID_ARGUMENT), ("null_x", md.MOE_ERR_INVALID_ARGUMENT),
+    ("small_ws", md.MOE_ERR_WORKSPACE_TOO_SMALL), ("partial_overlap", md.MOE_ERR_INVALID_ARGUMENT),
+    ("bad_hidden", md.MOE_ERR_UNSUPPORTED), ("fp8_no_scales", md.MOE_ERR_INVALID_ARGUMENT),
+    ("k_too_big", md.MOE_ERR_UNSUPPORTED), ("null_desc", md.MOE_ERR_INVALID_ARGUMENT),
+])
+def test_layer_argument_errors(lib, case, status):
+    w = synth.WORKLOADS["k3_b1"]
+    d = desc_of(w)
+    wt = _weights()
+    B, x, y = 1, FAKE + (1 << 30), FAKE + (2 << 30)
+    ws, wsb = FAKE + (3 << 30), md.moe_workspace_bytes(d, 64, 1)
+    if case == "batch0":
+        B = 0
+    elif case == "batch65":
+        B = 65
+    elif case == "misaligned_x":
+        x += 2
+    elif case == "null_x":
+        x = None
+    elif case == "small_ws":
+        wsb = 1024
+    elif case == "partial_overlap":
+        y = x + 16
+    elif case == "bad_hidden":
+        d.hidden = 7000
+    elif case == "fp8_no_scales":
+        d = desc_of(synth.WORKLOADS["k3_stack4_fp8"])
+    elif case == "k_too_big":
+        d.top_k = 33
+    if case == "null_desc":
+        st = lib.moe_decode_layer(None, ctypes.byref(wt), x, y, B, None, None, ws, wsb, None)
+    else:
+        st = md.moe_decode_layer(d, wt, x, y, B, None, None, ws, wsb, check=False)
+    assert st == status, (case, md.moe_last_error())
+    assert md.moe_last_error()
+
+
+def test_route_and_stack_argument_errors(lib):
+    w = synth.WORKLOADS["k3_b1"]
+    d = desc_of(w)
+    wt = _weights()
+    ws, wsb = FAKE + (3 << 30), md.moe_workspace_bytes(d, 64, 4)
+    x = FAKE + (1 << 30)
+    assert md.moe_route(d, wt, x, 1, None, FAKE, None, ws, wsb, check=False) == md.MOE_ERR_INVALID_ARGUMENT
+    assert md.moe_decode_stack(d, [wt] * 9, x, x, 1, None, None, ws, wsb, check=False) == md.MOE_ERR_UNSUPPORTED
+    assert md.moe_decode_stack(d, [wt, wt], x, x, 1, None, None, ws, 4096, check=False) == \
+        md.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert md.moe_check_workspace(None, 0) == md.MOE_ERR_INVALID_ARGUMENT

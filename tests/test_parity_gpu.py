@@ -1,0 +1,350 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: expert indices bit-exact (tokens drawn so that the oracle's router margin
+l_(k) - l_(k+1) is >= 1e-3); outputs within max relative error 2e-2 for bf16 /
+fp8 weights and 1e-4 for the fp32 workload (error = max |a-r| / max(|r|, rms r));
+routing weights within 1e-4 relative; router logits within 2e-4 absolute
+(a fifth of the margin).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_decode_02_amd as md
+import oracle
+import synth
+from helpers import draw_tokens_with_margin, host_layer, margin, max_rel_err, small_workload, to_f64
+from synth.device import DeviceLayer, act_tensor, desc_of, to_device, to_host, workspace
+
+pytestmark = pytest.mark.gpu
+
+TOL = {synth.F32: 1e-4, synth.BF16: 2e-2}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    md.build(force=False)
+    synth.build(force=False, device=True)
+    md.lib()
+    return torch.device("cuda:0")
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def oracle_routes(w, Lh, x):
+    """Oracle routing of every token (RMSNorm + router + top-k only)."""
+    d = oracle.desc_of(w)
+    idx = np.zeros((x.shape[0], w.k), np.int32)
+    wts = np.zeros((x.shape[0], w.k), np.float32)
+    lg = np.zeros((x.shape[0], w.E), np.float32)
+    for t in range(x.shape[0]):
+        xhat, _ = oracle.rmsnorm(d, x[t], Lh.gamma)
+        lg[t] = oracle.router_logits(d, Lh, xhat)
+        idx[t], wts[t] = oracle.route(d, lg[t])
+    return idx, wts, lg
+
+
+def add_experts(w, Lh, ids, layer=0):
+    for e in sorted(set(int(i) for i in np.ravel(ids))):
+        if e not in Lh.gate_up:
+            Lh.gate_up[e], s1 = synth.expert_gate_up(w, e, layer)
+            Lh.down[e], s2 = synth.expert_down(w, e, layer)
+            if s1 is not None:
+                Lh.gate_up_scale[e], Lh.down_scale[e] = s1, s2
+
+
+def gpu_layer(w, dl, x, B, dev, route=False):
+    d = desc_of(w)
+    xd = to_device(x, dev)
+    yd = act_tensor(w, B, dev)
+    idx = torch.full((B, w.k), -1, dtype=torch.int32, device=dev)
+    wts = torch.zeros((B, w.k), dtype=torch.float32, device=dev)
+    ws = workspace(d, B, 1, dev)
+    md.moe_decode_layer(d, dl.weights, xd, yd, B, idx, wts, ws)
+    out = {"y": to_host(yd), "idx": idx.cpu().numpy(), "w": wts.cpu().numpy()}
+    if route:
+        ridx = torch.full((B, w.k), -1, dtype=torch.int32, device=dev)
+        rw = torch.zeros((B, w.k), dtype=torch.float32, device=dev)
+        lg = torch.zeros((B, w.E), dtype=torch.float32, device=dev)
+        md.moe_route(d, dl.weights, xd, B, ridx, rw, lg, ws)
+        out.update(ridx=ridx.cpu().numpy(), rw=rw.cpu().numpy(), logits=lg.cpu().numpy())
+    torch.cuda.synchronize()
+    assert md.moe_check_workspace(ws) == md.MOE_OK
+    return out
+
+
+def check_layer(w, got, y_ref, idx_ref, w_ref, tokens=None):
+    tokens = range(len(idx_ref)) if tokens is None else tokens
+    for t in tokens:
+        assert np.array_equal(got["idx"][t], idx_ref[t]), (t, got["idx"][t], idx_ref[t])
+        assert np.allclose(got["w"][t], w_ref[t], rtol=1e-4, atol=1e-6), t
+        err = max_rel_err(to_f64(got["y"][t], w.act), to_f64(y_ref[t], w.act))
+        assert err <= TOL[w.act], (t, err)
+    return max(max_rel_err(to_f64(got["y"][t], w.act), to_f64(y_ref[t], w.act)) for t in tokens)
+
+
+def full_parity(w, B, dev, poison=True, random_gamma=False):
+    """Every token through the oracle and the GPU layer (+ moe_route)."""
+    Lh = host_layer(w, experts=[], random_gamma=random_gamma)
+    x, _ = draw_tokens_with_margin(w, B, [Lh])
+    idx_r, w_r, lg_r = oracle_routes(w, Lh, x)
+    add_experts(w, Lh, idx_r)
+    y_ref, idx_o, w_o, _ = oracle.layer(oracle.desc_of(w), Lh, x)
+    assert np.array_equal(idx_o, idx_r)
+    log(f"gpu: {w.name} B={B} poison={poison}")
+    dl = DeviceLayer(w, device=dev, experts=idx_r if poison else None, random_gamma=random_gamma)
+    got = gpu_layer(w, dl, x, B, dev, route=True)
+    err = check_layer(w, got, y_ref, idx_r, w_r)
+    assert np.array_equal(got["ridx"], idx_r)
+    assert np.allclose(got["rw"], w_r, rtol=1e-4, atol=1e-6)
+    assert np.max(np.abs(got["logits"] - lg_r)) <= 2e-4
+    del dl
+    free()
+    return err
+
+
+# ---- the generator's device fill ------------------------------------------------
+
+def test_device_fill_matches_host(dev):
+    for dtype, n in [(synth.BF16, 100003), (synth.F32, 4099)]:
+        k = synth.key(7, 1, synth.T_EXPERT_GU, 3)
+        h = synth.fill_host((n,), k, dtype, 0.02)
+        t = torch.empty(n, dtype=torch.bfloat16 if dtype == synth.BF16 else torch.float32, device=dev)
+        synth.fill_device(t, k, dtype, 0.02)
+        assert np.array_equal(to_host(t), h)
+    k, ck = synth.key(7, 1, synth.T_EXPERT_D, 3), synth.key(7, 1, synth.T_SCALE_D, 3)
+    codes, scales = synth.fill_host_fp8(256, 1024, k, ck, 0.02)
+    t = torch.empty((256, 1024), dtype=torch.uint8, device=dev)
+    s2 = synth.fill_device_fp8(t, 256, 1024, k, ck, 0.02)
+    assert np.array_equal(t.cpu().numpy(), codes) and np.array_equal(s2, scales)
+
+
+# ---- the five workloads ------------------------------------------------------------
+
+def test_tiny_f32_layer(dev):
+    w = synth.WORKLOADS["tiny_f32"]
+    err = full_parity(w, 1, dev, poison=False)
+    log(f"tiny_f32 B=1 max rel err {err:.2e}")
+
+
+@pytest.mark.parametrize("B", [2, 3, 8, 9, 17, 64])
+def test_tiny_f32_batches(dev, B):
+    w = synth.WORKLOADS["tiny_f32"]
+    full_parity(w, B, dev, poison=True)
+
+
+def test_small_bf16_random_gamma_zipf(dev):
+    w = small_workload(name="small_bf16", H=512, E=40, k=6, I=256, Is=512, act=synth.BF16, router=synth.F32,
+                       expert=synth.BF16, shared=synth.BF16, zipf_s=1.1, seed=21)
+    for B in (1, 5, 33):
+        full_parity(w, B, dev, poison=True, random_gamma=True)
+
+
+def test_k3_b1(dev):
+    err = full_parity(synth.WORKLOADS["k3_b1"], 1, dev, poison=True)
+    log(f"k3_b1 max rel err {err:.2e}")
+
+
+def test_k3_b1_all_experts_drawn(dev):
+    full_parity(synth.WORKLOADS["k3_b1"], 1, dev, poison=False)
+
+
+def test_k3_b8(dev):
+    err = full_parity(synth.WORKLOADS["k3_b8"], 8, dev, poison=True)
+    log(f"k3_b8 max rel err {err:.2e}")
+
+
+def test_k3_b64_zipf(dev):
+    """All 64 tokens' routing bit-exact; outputs of 4 sampled tokens vs the oracle."""
+    w = synth.WORKLOADS["k3_b64_zipf"]
+    B = 64
+    Lh = host_layer(w, experts=[])
+    x, _ = draw_tokens_with_margin(w, B, [Lh])
+    idx_r, w_r, lg_r = oracle_routes(w, Lh, x)
+    sample = [0, 21, 42, 63]
+    add_experts(w, Lh, idx_r[sample])
+    y_ref, idx_o, w_o, _ = oracle.layer(oracle.desc_of(w), Lh, x[sample])
+    log(f"gpu: {w.name} B={B}")
+    dl = DeviceLayer(w, device=dev, experts=idx_r)
+    got = gpu_layer(w, dl, x, B, dev, route=True)
+    assert np.array_equal(got["idx"], idx_r)
+    assert np.allclose(got["w"], w_r, rtol=1e-4, atol=1e-6)
+    assert np.array_equal(got["ridx"], idx_r)
+    assert np.max(np.abs(got["logits"] - lg_r)) <= 2e-4
+    sub = {"y": got["y"][sample], "idx": got["idx"][sample], "w": got["w"][sample]}
+    err = check_layer(w, sub, y_ref, idx_o, w_o)
+    assert np.all(np.isfinite(to_f64(got["y"], w.act)))
+    log(f"k3_b64_zipf sampled max rel err {err:.2e}, union {len(np.unique(idx_r))} experts")
+    del dl
+    free()
+
+
+@pytest.fixture(scope="module")
+def stack4(dev):
+    w = synth.WORKLOADS["k3_stack4_fp8"]
+    log(f"gpu: building {w.name} (4 layers, all experts drawn)")
+    dls = [DeviceLayer(w, layer=l, device=dev) for l in range(w.layers)]
+    hosts = [host_layer(w, experts=[], layer=l) for l in range(w.layers)]
+    yield w, dls, hosts
+    del dls
+    free()
+
+
+def oracle_stack_token(w, hosts, xt):
+    """Oracle stack on one token, materialising the experts each layer selects."""
+    d = oracle.desc_of(w)
+    cur = xt[None, :]
+    idx_all, w_all, lg_all = [], [], []
+    for l, Lh in enumerate(hosts):
+        xhat, _ = oracle.rmsnorm(d, cur[0], Lh.gamma)
+        lg = oracle.router_logits(d, Lh, xhat)
+        idx, _ = oracle.route(d, lg)
+        add_experts(w, Lh, idx, layer=l)
+        cur, i, ww, g = oracle.layer(d, Lh, cur)
+        idx_all.append(i[0]); w_all.append(ww[0]); lg_all.append(g[0])
+    return cur[0], np.array(idx_all), np.array(w_all), np.array(lg_all)
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 16, 64])
+def test_k3_stack4_fp8(dev, stack4, B):
+    """Persistent 4-layer fp8 stack: layer-0 routing of all tokens bit-exact; up
+    to two sampled tokens (redrawn until every layer's margin is >= 1e-3) through
+    all four layers vs the oracle stack."""
+    w, dls, hosts = stack4
+    d = oracle.desc_of(w)
+    sample = sorted({0, B - 1})
+    attempts = np.zeros(B, np.int64)
+    refs = {}
+    for t in sample:
+        for a in range(32):
+            xt = synth.fill_host((w.H,), synth.key(w.seed, 0, synth.T_X, t, a), w.act, synth.INPUT_SIGMA)
+            y, idx, ww, lg = oracle_stack_token(w, hosts, xt)
+            if all(margin(lg[l], w.k) >= 1e-3 for l in range(w.layers)):
+                attempts[t] = a
+                refs[t] = (y, idx, ww)
+                break
+        else:
+            raise RuntimeError("no draw with margins >= 1e-3")
+    x = synth.x_tokens(w, B, attempts)
+    idx0, w0, lg0 = oracle_routes(w, hosts[0], x)
+    ok0 = [t for t in range(B) if margin(lg0[t], w.k) >= 1e-3]
+    log(f"gpu: {w.name} stack B={B}")
+    dd = desc_of(w)
+    xd = to_device(x, dev)
+    yd = act_tensor(w, B, dev)
+    idx = torch.full((w.layers, B, w.k), -1, dtype=torch.int32, device=dev)
+    wts = torch.zeros((w.layers, B, w.k), dtype=torch.float32, device=dev)
+    ws = workspace(dd, B, w.layers, dev)
+    md.moe_decode_stack(dd, [dl.weights for dl in dls], xd, yd, B, idx, wts, ws)
+    torch.cuda.synchronize()
+    assert md.moe_check_workspace(ws) == md.MOE_OK
+    gi, gw, gy = idx.cpu().numpy(), wts.cpu().numpy(), to_host(yd)
+    assert np.array_equal(gi[0, ok0], idx0[ok0])
+    assert np.all(np.isfinite(to_f64(gy, w.act)))
+    for t in sample:
+        y, ridx, rw = refs[t]
+        assert np.array_equal(gi[:, t], ridx), (t, gi[:, t], ridx)
+        assert np.allclose(gw[:, t], rw, rtol=1e-4, atol=1e-6)
+        err = max_rel_err(to_f64(gy[t], w.act), to_f64(y, w.act))
+        log(f"stack B={B} token {t}: max rel err {err:.2e}")
+        assert err <= 2e-2
+    # every token's selected experts are distinct and in range, weights sum to 1
+    for l in range(w.layers):
+        for t in range(B):
+            assert len(set(gi[l, t].tolist())) == w.k and gi[l, t].min() >= 0 and gi[l, t].max() < w.E
+            assert abs(float(gw[l, t].sum()) - 1) < 1e-5
+
+
+# ---- properties -----------------------------------------------------------------------
+
+def test_exact_ties_lower_index_wins(dev):
+    """Duplicated router rows give bit-identical logits; the lower index ranks first
+    and wins the k-th place."""
+    for act in (synth.F32, synth.BF16):
+        w = small_workload(name="ties", H=256, E=32, k=4, I=128, Is=128, act=act, router=synth.F32,
+                           expert=act, shared=act, seed=31)
+        Lh = host_layer(w)
+        x = synth.x_tokens(w, 1)
+        d = oracle.desc_of(w)
+        xhat, _ = oracle.rmsnorm(d, x[0], Lh.gamma)
+        lg = oracle.router_logits(d, Lh, xhat)
+        order = np.argsort(-lg, kind="stable")
+        top, kth = int(order[0]), int(order[w.k - 1])
+        free_rows = [e for e in range(w.E) if e not in order[: w.k + 1]]
+        lo = min(free_rows)
+        hi = max(free_rows)
+        rw = Lh.router_w.copy()
+        rw[lo] = rw[top]      # a lower-index twin of the best expert: ranks before it
+        rw[hi] = rw[kth]      # a higher-index twin of the k-th expert: loses the k-th place
+        Lh.router_w = rw
+        y_ref, idx_ref, w_ref, lg_ref = oracle.layer(d, Lh, x)
+        assert lg_ref[0, lo] == lg_ref[0, top] and idx_ref[0, 0] == min(lo, top)
+        dl = DeviceLayer(w, device=dev, host_router=rw)
+        got = gpu_layer(w, dl, x, 1, dev, route=True)
+        assert got["logits"][0, lo] == got["logits"][0, top]
+        assert got["logits"][0, hi] == got["logits"][0, kth]
+        assert np.array_equal(got["idx"], idx_ref) and np.array_equal(got["ridx"], idx_ref)
+        assert max_rel_err(to_f64(got["y"], act), to_f64(y_ref, act)) <= TOL[act]
+
+
+def test_repeatable_inplace_and_batch_invariant(dev):
+    w = synth.WORKLOADS["k3_b8"]
+    B = 8
+    x = synth.x_tokens(w, B)
+    dl = DeviceLayer(w, device=dev)
+    a = gpu_layer(w, dl, x, B, dev)
+    b = gpu_layer(w, dl, x, B, dev)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["idx"], b["idx"])
+    # in place: y == x
+    d = desc_of(w)
+    xd = to_device(x, dev)
+    ws = workspace(d, B, 1, dev)
+    md.moe_decode_layer(d, dl.weights, xd, xd, B, None, None, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(xd), a["y"])
+    # a token alone gives the same routing and an output within tolerance
+    for t in (0, 5):
+        one = gpu_layer(w, dl, x[t:t + 1], 1, dev)
+        assert np.array_equal(one["idx"][0], a["idx"][t])
+        assert max_rel_err(to_f64(one["y"][0], w.act), to_f64(a["y"][t], w.act)) <= 2e-2
+    # a one-layer stack is the layer
+    ys = act_tensor(w, B, dev)
+    ws2 = workspace(d, B, 1, dev)
+    md.moe_decode_stack(d, [dl.weights], to_device(x, dev), ys, B, None, None, ws2)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(ys), a["y"])
+    del dl
+    free()
+
+
+def test_watchdog_reports_timeout_then_recovers(dev, monkeypatch):
+    """A host-set limit of 0 ticks makes each barrier wait give up at once; the
+    launch still completes, the workspace reports MOE_ERR_TIMEOUT once, and the
+    next call on the same workspace is correct."""
+    w = synth.WORKLOADS["tiny_f32"]
+    dl = DeviceLayer(w, device=dev)
+    d = desc_of(w)
+    x = synth.x_tokens(w, 2)
+    ref = gpu_layer(w, dl, x, 2, dev)
+    xd, yd = to_device(x, dev), act_tensor(w, 2, dev)
+    ws = workspace(d, 2, 1, dev)
+    monkeypatch.setenv("MOE_DEBUG_BARRIER_TIMEOUT_TICKS", "0")
+    md.moe_decode_layer(d, dl.weights, xd, yd, 2, None, None, ws)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("MOE_DEBUG_BARRIER_TIMEOUT_TICKS")
+    assert md.moe_check_workspace(ws) == md.MOE_ERR_TIMEOUT
+    assert md.moe_check_workspace(ws) == md.MOE_OK
+    md.moe_decode_layer(d, dl.weights, xd, yd, 2, None, None, ws)
+    torch.cuda.synchronize()
+    assert md.moe_check_workspace(ws) == md.MOE_OK
+    assert np.array_equal(to_host(yd), ref["y"])
