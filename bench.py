@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE decode layer on one MI355X.
+
+A step is one call of moe_decode_layer (or moe_decode_stack for the stack
+workload): RMSNorm, router over all experts, softmax + top-k +
+renormalisation, gathered SwiGLU experts, the shared expert, the weighted
+combine and the residual, for one batch of B tokens, in one kernel launch.
+
+Inputs are seeded and synthetic (synth/): weights ~N(0, 0.02), tokens
+~N(0, 1), all 896 experts drawn on the device. So that no step finds the
+previous step's weights in the 256 MB memory-side cache, the timed loop
+rotates over `--copies` layer instances that each hold their own router,
+shared expert and RMSNorm gain (drawn as layers 0..copies-1 of the
+workload's seed) and their own token batch; the routed-expert tensor is
+common to them (the routing of different instances picks nearly disjoint
+experts).
+
+`value` is tokens per second (B / step time). The roofline object gives the
+weight bytes the step must touch (router + shared + gain + every distinct
+selected expert, each counted once per step) over the measured kernel time,
+against the 8 TB/s HBM peak. The CPU baseline times the plain oracle on a
+few tokens of the same workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+WORKLOAD_NOTES = {
+    "tiny_f32": "tiny fp32 MoE layer H=256 E=32 k=4 I=Is=128",
+    "k3_b1": "K3-scale layer share H=7168 E=896 k=16 I=1024 Is=2048, bf16 experts/shared, fp32 router",
+    "k3_b8": "K3-scale layer share at B=8",
+    "k3_b64_zipf": "K3-scale layer share at B=64 with log-Zipf(1.1) router bias",
+    "k3_stack4_fp8": "4-layer K3-scale stack, fp8 e4m3 experts (bf16 scale per 128 rows), bf16 router/shared",
+}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="k3_b1",
+                    choices=["tiny_f32", "k3_b1", "k3_b8", "k3_b64_zipf", "k3_stack4_fp8"])
+    ap.add_argument("--batch", type=int, default=None, help="tokens per step (default: the workload's first)")
+    ap.add_argument("--copies", type=int, default=8, help="layer instances the timed loop rotates over")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, B, budget_s):
+    """The oracle (single-threaded plain C) on tokens of the same workload,
+    until about budget_s seconds of oracle time have run."""
+    import numpy as np
+
+    import oracle
+    import synth
+    d = oracle.desc_of(w)
+    layers = []
+    for l in range(w.layers):
+        L = oracle.Layer(gamma=synth.gamma(w, layer=l), router_w=synth.router_w(w, l),
+                         router_bias=synth.router_bias(w, l), gate_up={}, down={},
+                         shared_gate_up=synth.shared_gate_up(w, l), shared_down=synth.shared_down(w, l))
+        layers.append(L)
+
+    def need_experts(xt):
+        # materialise the experts each layer of this token selects (generation is not timed)
+        cur = xt
+        for l, L in enumerate(layers):
+            xhat, _ = oracle.rmsnorm(d, cur[0], L.gamma)
+            idx, _ = oracle.route(d, oracle.router_logits(d, L, xhat))
+            for e in idx:
+                e = int(e)
+                if e not in L.gate_up:
+                    L.gate_up[e], s1 = synth.expert_gate_up(w, e, l)
+                    L.down[e], s2 = synth.expert_down(w, e, l)
+                    if s1 is not None:
+                        L.gate_up_scale[e], L.down_scale[e] = s1, s2
+            if l + 1 < len(layers):
+                cur, _, _, _ = oracle.layer(d, L, cur)
+
+    x = synth.x_tokens(w, max(B, 1))
+    spent, ntok, t = 0.0, 0, 0
+    while spent < budget_s and ntok < 4096:
+        xt = np.ascontiguousarray(x[t % x.shape[0]][None, :])
+        need_experts(xt)
+        t0 = time.perf_counter()
+        if w.layers == 1:
+            oracle.layer(d, layers[0], xt)
+        else:
+            oracle.stack(d, layers, xt)
+        spent += time.perf_counter() - t0
+        ntok += 1
+        t += 1
+    return {"value": ntok / spent, "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "sample": f"{ntok} token(s) of {w.name}, one at a time, {spent:.1f} s of single-threaded oracle time"}
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding of the layer is a design, not code)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import moe_decode_02_amd as md
+    import synth
+    from synth.device import DeviceLayer, act_tensor, desc_of, to_device, workspace
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    md.lib()  # fails loudly when the HIP library is not built
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    B = args.batch or w.B
+    L = w.layers
+    C = max(1, args.copies)
+    d = desc_of(w)
+    log(f"bench: {w.name} B={B} layers={L} copies={C} on {torch.cuda.get_device_name(0)}")
+
+    # layer instances: instance c, layer l uses generator layer index c*L + l for its
+    # router / shared / gain; routed experts of layer l are shared by all instances
+    t0 = time.time()
+    base = [DeviceLayer(w, layer=l, device=dev) for l in range(L)]
+    insts = []
+    for c in range(C):
+        layers = []
+        for l in range(L):
+            if c == 0:
+                layers.append(base[l])
+                continue
+            li = DeviceLayer.__new__(DeviceLayer)
+            li.__dict__.update(base[l].__dict__)
+            gl = c * L + l
+            li.gamma = to_device(synth.gamma(w, layer=gl), dev)
+            li.router_w = to_device(synth.router_w(w, gl), dev)
+            b = synth.router_bias(w, gl)
+            li.router_bias = to_device(b, dev) if b is not None else None
+            if w.Is > 0:
+                li.sgu = torch.empty_like(base[l].sgu)
+                li.sd = torch.empty_like(base[l].sd)
+                synth.fill_device(li.sgu, synth.key(w.seed, gl, synth.T_SHARED_GU), w.shared, synth.WEIGHT_SIGMA)
+                synth.fill_device(li.sd, synth.key(w.seed, gl, synth.T_SHARED_D), w.shared, synth.WEIGHT_SIGMA)
+            li.weights = li._struct()
+            layers.append(li)
+        insts.append(layers)
+    xs = []
+    for c in range(C):
+        xc = np.stack([synth.fill_host((w.H,), synth.key(w.seed, 100 + c, synth.T_X, t), w.act, synth.INPUT_SIGMA)
+                       for t in range(B)])
+        xs.append(to_device(xc, dev))
+    ys = [act_tensor(w, B, dev) for _ in range(C)]
+    idx = [torch.zeros((L, B, w.k), dtype=torch.int32, device=dev) for _ in range(C)]
+    wts = [torch.zeros((L, B, w.k), dtype=torch.float32, device=dev) for _ in range(C)]
+    ws = workspace(d, B, L, dev)
+    torch.cuda.synchronize()
+    log(f"bench: inputs ready in {time.time() - t0:.1f} s, {torch.cuda.memory_allocated() / 2**30:.1f} GiB on the GPU")
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        c = i % C
+        if L == 1:
+            md.moe_decode_layer(d, insts[c][0].weights, xs[c], ys[c], B, idx[c], wts[c], ws, stream=stream)
+        else:
+            md.moe_decode_stack(d, [li.weights for li in insts[c]], xs[c], ys[c], B, idx[c], wts[c], ws,
+                                stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if md.moe_check_workspace(ws) != md.MOE_OK:
+        log("bench: a warm-up launch hit its barrier watchdog")
+        return 1
+
+    # algorithmic bytes of each instance: weights touched, each counted once per step
+    per_inst = []
+    for c in range(C):
+        sel = idx[c].cpu().numpy()
+        per_inst.append(sum(insts[c][l].touched_bytes(sel[l]) for l in range(L)))
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    if md.moe_check_workspace(ws) != md.MOE_OK:
+        log("bench: a timed launch hit its barrier watchdog")
+        return 1
+    ms_step = ms_total / args.steps
+    nbytes = sum(per_inst[i % C] for i in range(args.steps)) / args.steps
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    for c in range(C):
+        if not torch.isfinite(ys[c].float()).all():
+            log(f"bench: non-finite output in instance {c}")
+            return 1
+
+    # per-launch spread (events around single launches, after the timed region)
+    per = []
+    for i in range(min(args.steps, 200)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step(i)
+        b.record(stream)
+        per.append((a, b))
+    torch.cuda.synchronize()
+    lat = np.array([a.elapsed_time(b) * 1e3 for a, b in per])
+    log(f"bench: {ms_step * 1e3:.1f} us/step over {args.steps} steps (wall {wall / args.steps * 1e6:.1f} us), "
+        f"single-launch median {np.median(lat):.1f} p95 {np.percentile(lat, 95):.1f} min {lat.min():.1f} us, "
+        f"{nbytes / 1e6:.1f} MB/step -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, B, args.cpu_seconds)
+        log(f"bench: cpu baseline {cpu}")
+
+    out = {
+        "metric": "MoE decode layer us/step + tok/s (B=1-64); achieved HBM GB/s vs peak",
+        "value": B / (ms_step * 1e-3),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "us_per_step": ms_step * 1e3,
+        "us_per_step_single_launch": {"median": float(np.median(lat)), "p95": float(np.percentile(lat, 95)),
+                                      "min": float(lat.min())},
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {synth.F32: "f32", synth.BF16: "bf16", synth.FP8: "fp8e4m3"}[w.expert],
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {WORKLOAD_NOTES[w.name]}", "batch": B, "layers": L,
+                   "rotated_instances": C, "kernel_launches_per_step": 1},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -29,13 +29,33 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+PROBE_PATH = os.path.join(_HERE, "libmoeprobe.so")
+PROBE_SOURCES = [os.path.join(_HERE, "csrc", "bench_probe.hip")]
+
+
 def build(force: bool = True) -> str:
-    """Compile libmoedecode.so in-tree for gfx950 (hipcc cross-compiles without a GPU)."""
-    if force or not os.path.exists(LIB_PATH):
-        tmp = LIB_PATH + ".tmp"
-        subprocess.check_call(["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, *SOURCES])
-        os.replace(tmp, LIB_PATH)
+    """Compile libmoedecode.so (and the benchmark's probe library) in-tree for
+    gfx950; hipcc cross-compiles without a GPU."""
+    for path, srcs in ((LIB_PATH, SOURCES), (PROBE_PATH, PROBE_SOURCES)):
+        if force or not os.path.exists(path):
+            tmp = path + ".tmp"
+            subprocess.check_call(["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, *srcs])
+            os.replace(tmp, path)
     return LIB_PATH
+
+
+@lru_cache(maxsize=None)
+def probe_lib():
+    """Measurement helpers of the benchmark (csrc/bench_probe.hip); not the decode path."""
+    if not os.path.exists(PROBE_PATH):
+        raise RuntimeError(f"{PROBE_PATH} is not built: run __graft_entry__.build()")
+    L = ctypes.CDLL(PROBE_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    L.moe_probe_stream_read.argtypes = [vp, sz, vp, i32, vp]
+    L.moe_probe_stream_read.restype = ctypes.c_int
+    L.moe_probe_copy.argtypes = [vp, vp, sz, i32, vp]
+    L.moe_probe_copy.restype = ctypes.c_int
+    return L
 
 
 class moe_layer_desc(ctypes.Structure):

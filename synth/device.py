@@ -60,7 +60,7 @@ class DeviceLayer:
         if w.expert == synth.FP8:
             self.egus = torch.zeros((w.E, 2 * w.I // 128), dtype=torch.bfloat16, device=dev)
             self.eds = torch.zeros((w.E, w.H // 128), dtype=torch.bfloat16, device=dev)
-        ids = range(w.E) if experts is None else sorted(set(int(e) for e in experts))
+        ids = range(w.E) if experts is None else sorted(set(int(e) for e in np.ravel(experts)))
         if experts is not None:
             self._poison()
         self.fill_experts(ids)

@@ -215,49 +215,87 @@ def oracle_stack_token(w, hosts, xt):
     return cur[0], np.array(idx_all), np.array(w_all), np.array(lg_all)
 
 
+STACK_DEEP_MARGIN = 5e-3
+
+
+def gpu_stack(w, dls, x, B, L, dev):
+    """The first L layers of the stack on the GPU: (y, idx [L][B][k], w [L][B][k])."""
+    dd = desc_of(w)
+    xd = to_device(x, dev)
+    yd = act_tensor(w, B, dev)
+    idx = torch.full((L, B, w.k), -1, dtype=torch.int32, device=dev)
+    wts = torch.zeros((L, B, w.k), dtype=torch.float32, device=dev)
+    ws = workspace(dd, B, L, dev)
+    md.moe_decode_stack(dd, [dl.weights for dl in dls[:L]], xd, yd, B, idx, wts, ws)
+    torch.cuda.synchronize()
+    assert md.moe_check_workspace(ws) == md.MOE_OK
+    return to_host(yd), idx.cpu().numpy(), wts.cpu().numpy()
+
+
 @pytest.mark.parametrize("B", [1, 2, 4, 16, 64])
 def test_k3_stack4_fp8(dev, stack4, B):
-    """Persistent 4-layer fp8 stack: layer-0 routing of all tokens bit-exact; up
-    to two sampled tokens (redrawn until every layer's margin is >= 1e-3) through
-    all four layers vs the oracle stack."""
+    """Persistent 4-layer fp8 stack in one launch.
+
+    The parity bar (routing bit-exact, max relative error 2e-2) is the bar of
+    one layer call, so each layer is checked teacher-forced: the oracle's layer
+    l runs on the GPU's own input of layer l, which the prefix runs (the first
+    1..3 layers, same kernel, deterministic) return. Layer-0 routing of every
+    token whose margin is >= 1e-3 is checked too.
+
+    Free-running, the two sides diverge slowly: layer l >= 1 sees the previous
+    layer's bf16 output, which each side rounds from fp32 sums taken in a
+    different order, so a few elements differ by one bf16 ulp and layer l's
+    logits move by up to ~2e-3 (measured). The sampled tokens are redrawn until
+    the oracle's own trajectory has margin >= 1e-3 at layer 0 and
+    >= STACK_DEEP_MARGIN deeper, so that the GPU's trajectory keeps margin
+    >= 1e-3 at every layer; the free-running output is held to the composed
+    bound of L per-layer tolerances."""
     w, dls, hosts = stack4
     d = oracle.desc_of(w)
     sample = sorted({0, B - 1})
     attempts = np.zeros(B, np.int64)
     refs = {}
     for t in sample:
-        for a in range(32):
+        for a in range(64):
             xt = synth.fill_host((w.H,), synth.key(w.seed, 0, synth.T_X, t, a), w.act, synth.INPUT_SIGMA)
             y, idx, ww, lg = oracle_stack_token(w, hosts, xt)
-            if all(margin(lg[l], w.k) >= 1e-3 for l in range(w.layers)):
+            if margin(lg[0], w.k) >= 1e-3 and all(margin(lg[l], w.k) >= STACK_DEEP_MARGIN
+                                                   for l in range(1, w.layers)):
                 attempts[t] = a
-                refs[t] = (y, idx, ww)
+                refs[t] = y
                 break
         else:
-            raise RuntimeError("no draw with margins >= 1e-3")
+            raise RuntimeError("no draw with the required margins")
     x = synth.x_tokens(w, B, attempts)
     idx0, w0, lg0 = oracle_routes(w, hosts[0], x)
     ok0 = [t for t in range(B) if margin(lg0[t], w.k) >= 1e-3]
     log(f"gpu: {w.name} stack B={B}")
-    dd = desc_of(w)
-    xd = to_device(x, dev)
-    yd = act_tensor(w, B, dev)
-    idx = torch.full((w.layers, B, w.k), -1, dtype=torch.int32, device=dev)
-    wts = torch.zeros((w.layers, B, w.k), dtype=torch.float32, device=dev)
-    ws = workspace(dd, B, w.layers, dev)
-    md.moe_decode_stack(dd, [dl.weights for dl in dls], xd, yd, B, idx, wts, ws)
-    torch.cuda.synchronize()
-    assert md.moe_check_workspace(ws) == md.MOE_OK
-    gi, gw, gy = idx.cpu().numpy(), wts.cpu().numpy(), to_host(yd)
+    runs = [gpu_stack(w, dls, x, B, L, dev) for L in range(1, w.layers + 1)]
+    gy, gi, gw = runs[-1]
+    for L in range(1, w.layers):  # a prefix run is the start of the full run
+        assert np.array_equal(runs[L - 1][1], gi[:L]) and np.array_equal(runs[L - 1][2], gw[:L])
+    layer_in = [x] + [runs[L - 1][0] for L in range(1, w.layers)]
     assert np.array_equal(gi[0, ok0], idx0[ok0])
+    assert np.allclose(gw[0, ok0], w0[ok0], rtol=1e-4, atol=1e-6)
     assert np.all(np.isfinite(to_f64(gy, w.act)))
     for t in sample:
-        y, ridx, rw = refs[t]
-        assert np.array_equal(gi[:, t], ridx), (t, gi[:, t], ridx)
-        assert np.allclose(gw[:, t], rw, rtol=1e-4, atol=1e-6)
-        err = max_rel_err(to_f64(gy[t], w.act), to_f64(y, w.act))
-        log(f"stack B={B} token {t}: max rel err {err:.2e}")
-        assert err <= 2e-2
+        for l in range(w.layers):
+            xt = np.ascontiguousarray(layer_in[l][t:t + 1])
+            xhat, _ = oracle.rmsnorm(d, xt[0], hosts[l].gamma)
+            lg = oracle.router_logits(d, hosts[l], xhat)
+            assert margin(lg, w.k) >= 1e-3, (t, l, margin(lg, w.k))
+            ridx, _ = oracle.route(d, lg)
+            add_experts(w, hosts[l], ridx, layer=l)
+            yl, il, wl, _ = oracle.layer(d, hosts[l], xt)
+            assert np.array_equal(gi[l, t], il[0]), (t, l, gi[l, t], il[0])
+            assert np.allclose(gw[l, t], wl[0], rtol=1e-4, atol=1e-6), (t, l)
+            gout = runs[l][0][t]
+            err = max_rel_err(to_f64(gout, w.act), to_f64(yl[0], w.act))
+            log(f"stack B={B} token {t} layer {l} (teacher-forced): max rel err {err:.2e}")
+            assert err <= 2e-2
+        err = max_rel_err(to_f64(gy[t], w.act), to_f64(refs[t], w.act))
+        log(f"stack B={B} token {t} free-running {w.layers} layers: max rel err {err:.2e}")
+        assert err <= w.layers * 2e-2
     # every token's selected experts are distinct and in range, weights sum to 1
     for l in range(w.layers):
         for t in range(B):
