@@ -110,6 +110,30 @@ def cpu_baseline(w, B, budget_s):
             "sample": f"{ntok} token(s) of {w.name}, one at a time, {spent:.1f} s of single-threaded oracle time"}
 
 
+def stream_probe(torch, md, dev, stream, gib=4, reps=5):
+    """HBM read rate of a plain 16-byte streaming kernel over `gib` GiB (the
+    practical ceiling of a weight-streaming step on this GPU)."""
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    grid = torch.cuda.get_device_properties(dev).multi_processor_count * 16
+    lib = md.probe_lib()
+    best = 0.0
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        rc = lib.moe_probe_stream_read(buf.data_ptr(), n, sink.data_ptr(), grid, stream.cuda_stream)
+        b.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"moe_probe_stream_read failed: hip error {rc}")
+        torch.cuda.synchronize()
+        best = max(best, n / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del buf
+    return best
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -233,6 +257,10 @@ def main() -> int:
         f"single-launch median {np.median(lat):.1f} p95 {np.percentile(lat, 95):.1f} min {lat.min():.1f} us, "
         f"{nbytes / 1e6:.1f} MB/step -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
 
+    probe = stream_probe(torch, md, dev, stream)
+    log(f"bench: streaming-read probe {probe:.0f} GB/s ({probe / HBM_PEAK_GBS:.1%} of 8 TB/s); "
+        f"the step reaches {gbs / probe:.1%} of it")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, B, args.cpu_seconds)
@@ -260,6 +288,7 @@ def main() -> int:
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes_per_launch": nbytes},
         "cpu_baseline": cpu,
+        "stream_probe_GBs": probe,
     }
     print(json.dumps(out), flush=True)
     return 0

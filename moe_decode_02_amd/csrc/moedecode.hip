@@ -1,42 +1,51 @@
 // moedecode.hip - libmoedecode: the MoE decode layer for MI355X (gfx950).
 //
-// One persistent kernel per call (moe_route, moe_decode_layer, moe_decode_stack).
-// The kernel fuses what the stock decode path launches one by one -
-// normalisation, matmul, activation and routing ops (openai-hub.com "Kimi K3 ...
-// 1.68x", section on why decode suits a megakernel) - and keeps the steps of
-// one layer inside one launch, synchronised by grid barriers:
+// One persistent kernel per call (moe_route, moe_decode_layer, moe_decode_stack),
+// one 1024-thread workgroup per compute unit. The kernel fuses what the stock
+// decode path launches one by one - normalisation, matmul, activation and
+// routing ops (openai-hub.com "Kimi K3 ... 1.68x", section on why decode suits
+// a megakernel) - and keeps the steps of a layer inside one launch. Per layer:
 //
-//   P0a  x-hat producers: workgroup t computes RMSNorm of token t, writes the
-//        fp32 x-hat (router input) and its activation-dtype copy (FFN input).
-//   B0   barrier
-//   P0b  router GEMV, split over K (partial logits), then the shared expert's
-//        gate/up rows, which do not depend on routing and fill the time the
-//        router barrier takes (the pages move the shared expert onto its own
-//        stream beside routing: smzdm.com post, section "what changed", MoE
-//        de-duplication item).
-//   B1   barrier (arrival after the router rows, wait after the shared rows)
-//   P1   every workgroup redoes softmax + top-k + renormalisation (same inputs,
-//        same code, same result - no extra barrier), builds the expert gather
-//        tables in LDS (union of selected experts, each expert's token list),
-//        then streams the selected experts' gate/up rows: h = SiLU(g) * u.
-//   B2   barrier
-//   P2   down projections: each workgroup owns a block of output rows and
-//        reduces every selected expert and the shared expert for them, then
-//        combines in a fixed order with the routing weights and the residual.
-//   B3   barrier between layers of a stack.
+//   x-hat   RMSNorm. At B <= 2 every workgroup normalises all tokens into its
+//           own LDS (x is 14 KB per token), so no grid barrier is needed; at
+//           larger B workgroup t normalises token t into global memory and a
+//           barrier publishes it.
+//   P0      The router GEMV, split over K into slices of about 7 KB of weights
+//           (partial logits, summed later in a fixed order), then the shared
+//           expert's gate/up rows, which do not depend on routing; the pages
+//           run the shared expert on its own stream beside routing (smzdm.com
+//           post, section "what changed", MoE de-duplication item). Every wave
+//           announces "router done" before its shared rows, so the router
+//           barrier has completed by the time anyone waits on it.
+//   P1      Every workgroup redoes softmax + top-k + renormalisation (same
+//           inputs, same code, same result: no extra barrier), builds the
+//           expert gather tables in LDS (union of selected experts, each
+//           expert's token list), then streams the selected experts' gate/up
+//           rows: h = SiLU(g) * u.
+//   P2      Each workgroup owns a block of output rows. It first reduces the
+//           shared expert's down rows (their input is ready since P0), which
+//           fills the wait for the expert barrier, then every selected
+//           expert's down rows, then combines in a fixed order with the
+//           routing weights and the residual.
+//   stack   Between layers one more barrier; while waiting for it, a
+//           workgroup loads the next layer's router and shared-expert rows
+//           that it will read first, so they come from cache.
 //
+// Weight rows stream through 16-byte non-temporal loads, whole chunks of 64
+// lanes with no per-lane guard, all loads of a step in flight before the
+// first use. Cross-lane sums and the top-k argmax use DPP row operations.
 // All reductions are fixed-order (no float atomics), so identical router rows
 // give bit-identical logits and repeated runs give identical outputs.
 //
-// Memory ordering across the 8 XCDs: a wave publishes its stores with an
-// agent-scope release fence before it counts itself in; a workgroup's last
-// wave adds one to the global barrier counter; one wave per workgroup polls
-// the counter, acquires at agent scope and raises an LDS flag for the others,
-// which acquire again before they read what other workgroups wrote. Weights
-// are static and may be loaded before a barrier; activations are only read
-// after it (a compiler that hoisted an activation load above a sync wait was
-// one of the bugs found in the pages' review: aiposthub.com article, section on
-// how vLLM verifies AI-written kernels).
+// Memory ordering across the 8 XCDs: every wave releases its stores at
+// workgroup scope and counts itself in LDS; the workgroup's last wave releases
+// at agent scope (L2 write-back) and adds one to the barrier's global counter.
+// One wave per workgroup polls the counter, acquires at agent scope and raises
+// an LDS flag for the others. Weights are static and may be loaded before a
+// barrier; activations are read only after it (a compiler that hoisted an
+// activation load above a sync wait was one of the bugs found in the pages'
+// review: aiposthub.com article, section on how vLLM verifies AI-written
+// kernels).
 #include <hip/hip_runtime.h>
 
 #include <stdarg.h>
@@ -55,17 +64,21 @@ namespace {
 
 enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 
-constexpr int kThreads = 1024;            // one workgroup per CU, 16 waves
+constexpr int kThreads = 1024;  // one workgroup per CU, 16 waves
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxB = 64;
 constexpr int kMaxK = 32;
 constexpr int kMaxE = 1024;
 constexpr int kMaxL = 8;
-constexpr int kTokGroup = 8;              // tokens whose partial sums a lane holds at once
-constexpr int kRowBlock = 4;              // down-projection rows per unit
-constexpr int kMaxBarriers = 4 * kMaxL + 4;
-constexpr unsigned kCtrlBar = 0, kCtrlDone = 1, kCtrlErr = 2;
-constexpr size_t kCtrlBytes = 256;
+constexpr int kTokGroup = 4;    // tokens whose partial sums a lane holds at once
+constexpr int kRowBlock = 4;    // down-projection rows per unit
+constexpr int kSmallB = 2;      // B <= kSmallB: x-hat and h staged in each workgroup's LDS
+
+enum : int { BAR_XHAT = 0, BAR_ROUTER = 1, BAR_SHARED = 2, BAR_H = 3, BAR_LAYER = 4, kBarPerLayer = 5 };
+constexpr int kMaxBarriers = kBarPerLayer * kMaxL;
+constexpr int kCtrlStride = 16;  // words: each control word on its own 64-byte line
+enum : int { CTRL_DONE = 0, CTRL_ERR = 1, CTRL_BAR = 2 };
+constexpr size_t kCtrlBytes = (size_t)(CTRL_BAR + kMaxBarriers) * kCtrlStride * sizeof(unsigned);
 
 struct LayerPtrs {
   const void *x;          // layer input [B][H] (act)
@@ -87,44 +100,47 @@ struct LayerPtrs {
 struct Params {
   int H, E, k, I, Is, B, L;
   int route_only;
-  int NS;                 // router K-splits
+  int NSR;                // router K-slices
+  int NSS;                // shared gate/up K-slices (small regime), else 1
   int G;                  // workgroups
   int rows_per_wg;        // P2 output rows per workgroup (multiple of kRowBlock)
   int pass_rows;          // P2 rows per LDS pass
   float eps;
   long long timeout_ticks;  // s_memrealtime ticks (100 MHz) before a barrier wait gives up
-  unsigned *ctrl;         // [0] barrier counter, [1] exit counter, [2] error word
-  float *xhat;            // [B][H] fp32
-  void *xa;               // [B][H] act (== xhat for fp32 activations)
-  float *rpart;           // [NS][B][E]
+  unsigned *ctrl;         // control words, kCtrlStride apart
+  float *xhat;            // [B][H] fp32 (general regime)
+  void *xa;               // [B][H] act (general regime; == xhat for fp32 activations)
+  float *rpart;           // [NSR][B][E]
+  float *hspart;          // [NSS][B][2 Is] (small regime)
   void *hbuf;             // [B*k][I] act
-  void *hsbuf;            // [B][Is] act
+  void *hsbuf;            // [B][Is] act (general regime)
   void *xbuf[2];          // [B][H] act, stack intermediates
+  // LDS carve-up, byte offsets from the start of dynamic LDS
+  int o_sel_idx, o_sel_w, o_cnt, o_start, o_tmask, o_ulist, o_plist;
+  int o_xf, o_xa;         // small regime, P0-P1: x-hat fp32 / act [B][H]
+  int o_hs, o_h;          // small regime, P2: shared h [B][Is], expert h [B*k][I] (act)
+  int o_part;             // P2 partial sums [pass_rows][pstride] fp32
   LayerPtrs lp[kMaxL];
 };
 
-// LDS layout (dynamic shared memory)
-struct Smem {
-  int bar_cnt[kMaxBarriers];   // waves of this workgroup that arrived
-  int bar_claim[kMaxBarriers]; // one wave polls the global counter
-  int bar_flag[kMaxBarriers];  // raised once the barrier is passed
+// fixed head of the dynamic LDS
+struct SmemHead {
+  int bar_cnt[kMaxBarriers];    // waves of this workgroup that arrived
+  int bar_claim[kMaxBarriers];  // one wave polls the global counter
+  int bar_flag[kMaxBarriers];   // raised once the barrier is passed
   float red[kWaves];
-  int nU;
-  int sel_idx[kMaxB * kMaxK];
-  float sel_w[kMaxB * kMaxK];
-  int cnt[kMaxE];
-  int start[kMaxE];
-  unsigned long long tmask[kMaxE];
-  int ulist[kMaxE];
-  int plist[kMaxB * kMaxK];
   int scan_tmp[2 * kWaves];
-  float part[1];               // P2 partial sums, sized at launch
+  int nU;
+  unsigned sink;
 };
 
 // Kernel parameters are read in place from the kernarg segment (address space 4).
 #define KARG __attribute__((address_space(4)))
 typedef const KARG Params *KParams;
 typedef const KARG LayerPtrs *KLayer;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_t;
 
 // ---------------------------------------------------------------------------
 // numbers
@@ -164,25 +180,24 @@ template <int D> __device__ __forceinline__ void store_act(void *p, size_t i, fl
   else ((uint16_t *)p)[i] = f32_to_bf16(v);
 }
 
-// value of v once stored in dtype D
-template <int D> __device__ __forceinline__ float round_act(float v) {
-  if constexpr (D == DT_F32) return v;
-  else return __uint_as_float((uint32_t)f32_to_bf16(v) << 16);
+template <int D> __device__ __forceinline__ void store_act_lds(lds_t *p, size_t i, float v) {
+  if constexpr (D == DT_F32) ((__attribute__((address_space(3))) float *)p)[i] = v;
+  else ((__attribute__((address_space(3))) uint16_t *)p)[i] = f32_to_bf16(v);
 }
 
-__device__ __forceinline__ uint4 ld16(const void *p) { return *(const uint4 *)p; }
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+template <int D> constexpr int dsz() { return D == DT_F32 ? 4 : D == DT_BF16 ? 2 : 1; }
+template <int WD> constexpr int epl() { return 16 / dsz<WD>(); }  // weights per 16-byte chunk
 
 // ---------------------------------------------------------------------------
-// 16-byte weight chunk . activation chunk
-
-template <int WD> constexpr int elems16() { return WD == DT_F32 ? 4 : WD == DT_BF16 ? 8 : 16; }
-template <int XD> constexpr int xsize() { return XD == DT_F32 ? 4 : 2; }
+// 16-byte weight chunk . activation chunk (EPL values, NX 16-byte vectors)
 
 template <int WD, int XD> struct Chunk;
 
 template <> struct Chunk<DT_BF16, DT_BF16> {
   static constexpr int NX = 1;
-  __device__ static __forceinline__ float dot(const uint4 &w, const uint4 *x, float a) {
+  __device__ static __forceinline__ float dot(const u32x4 &w, const u32x4 *x, float a) {
     a = dot2_bf16(w.x, x[0].x, a);
     a = dot2_bf16(w.y, x[0].y, a);
     a = dot2_bf16(w.z, x[0].z, a);
@@ -193,7 +208,7 @@ template <> struct Chunk<DT_BF16, DT_BF16> {
 
 template <> struct Chunk<DT_F32, DT_F32> {
   static constexpr int NX = 1;
-  __device__ static __forceinline__ float dot(const uint4 &w, const uint4 *x, float a) {
+  __device__ static __forceinline__ float dot(const u32x4 &w, const u32x4 *x, float a) {
     a = fmaf(__uint_as_float(w.x), __uint_as_float(x[0].x), a);
     a = fmaf(__uint_as_float(w.y), __uint_as_float(x[0].y), a);
     a = fmaf(__uint_as_float(w.z), __uint_as_float(x[0].z), a);
@@ -204,7 +219,7 @@ template <> struct Chunk<DT_F32, DT_F32> {
 
 template <> struct Chunk<DT_BF16, DT_F32> {
   static constexpr int NX = 2;
-  __device__ static __forceinline__ float dot(const uint4 &w, const uint4 *x, float a) {
+  __device__ static __forceinline__ float dot(const u32x4 &w, const u32x4 *x, float a) {
     a = fmaf(bf_lo(w.x), __uint_as_float(x[0].x), a);
     a = fmaf(bf_hi(w.x), __uint_as_float(x[0].y), a);
     a = fmaf(bf_lo(w.y), __uint_as_float(x[0].z), a);
@@ -226,7 +241,7 @@ template <> struct Chunk<DT_FP8, DT_BF16> {
     a = fmaf(e4m3_to_f32(w >> 24), bf_hi(x23), a);
     return a;
   }
-  __device__ static __forceinline__ float dot(const uint4 &w, const uint4 *x, float a) {
+  __device__ static __forceinline__ float dot(const u32x4 &w, const u32x4 *x, float a) {
     a = dot4(w.x, x[0].x, x[0].y, a);
     a = dot4(w.y, x[0].z, x[0].w, a);
     a = dot4(w.z, x[1].x, x[1].y, a);
@@ -235,268 +250,263 @@ template <> struct Chunk<DT_FP8, DT_BF16> {
   }
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
+// weight chunk: streamed once, so loaded non-temporal
+__device__ __forceinline__ u32x4 ldw(const char *p) { return __builtin_nontemporal_load((const u32x4 *)p); }
+
+// activation chunk, from global memory (XL = false) or LDS (XL = true)
+template <bool XL> struct XSrc;
+template <> struct XSrc<false> {
+  typedef const char *ptr;
+  __device__ static __forceinline__ u32x4 ld(ptr p, size_t off) { return *(const u32x4 *)(p + off); }
+};
+template <> struct XSrc<true> {
+  typedef const lds_t *ptr;
+  __device__ static __forceinline__ u32x4 ld(ptr p, size_t off) {
+    return *(const __attribute__((address_space(3))) u32x4 *)(p + off);
+  }
+};
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
 __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
 
 // ---------------------------------------------------------------------------
-// grid barriers
+// DPP cross-lane operations (wave64). After the six steps below lane 63 holds
+// the reduction of the whole wave: quad swaps, half-row and row mirrors give
+// every lane its 16-lane row's result; row_bcast:15 folds row 0 into row 1 and
+// row 2 into row 3; row_bcast:31 folds rows 0-1 into rows 2-3.
 
-__device__ __forceinline__ long long rt_now() { return (long long)__builtin_amdgcn_s_memrealtime(); }
+constexpr int DPP_QUAD_1032 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_BCAST15 = 0x142;
+constexpr int DPP_ROW_BCAST31 = 0x143;
 
-// A wave is done with the work barrier b waits for.
-__device__ void bar_arrive(KParams p, Smem &sm, int b) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  if (lane_id() == 0) {
-    int old = __hip_atomic_fetch_add(&sm.bar_cnt[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (old == kWaves - 1)
-      __hip_atomic_fetch_add(&p->ctrl[kCtrlBar], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
 }
 
-// Wait until every workgroup arrived at barrier b (global barrier number nb).
-__device__ void bar_wait(KParams p, Smem &sm, int b, int nb) {
-  const unsigned target = (unsigned)p->G * (unsigned)(nb + 1);
-  if (lane_id() == 0) {
-    if (__hip_atomic_load(&sm.bar_flag[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
-      const bool poller = __hip_atomic_exchange(&sm.bar_claim[b], 1, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
-      const long long t0 = rt_now();
-      if (poller) {
-        while (__hip_atomic_load(&p->ctrl[kCtrlBar], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-          __builtin_amdgcn_s_sleep(2);
-          if (rt_now() - t0 > p->timeout_ticks) {
-            __hip_atomic_store(&p->ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        __hip_atomic_store(&sm.bar_flag[b], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      } else {
-        while (__hip_atomic_load(&sm.bar_flag[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
-          __builtin_amdgcn_s_sleep(1);
-          if (rt_now() - t0 > 2 * p->timeout_ticks) break;
-        }
-      }
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+// sum of v over the wave, valid in lane 63 (fixed order: deterministic)
+__device__ __forceinline__ float wave_sum63(float v) {
+  v += dpp_f<DPP_QUAD_1032, 0xF>(0.f, v);
+  v += dpp_f<DPP_QUAD_2301, 0xF>(0.f, v);
+  v += dpp_f<DPP_ROW_HALF_MIRROR, 0xF>(0.f, v);
+  v += dpp_f<DPP_ROW_MIRROR, 0xF>(0.f, v);
+  v += dpp_f<DPP_ROW_BCAST15, 0xA>(0.f, v);
+  v += dpp_f<DPP_ROW_BCAST31, 0xC>(0.f, v);
+  return v;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// (larger value, then lower index) wins
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void argmax_step(float &v, int &i) {
+  const float ov = dpp_f<CTRL, ROWS>(v, v);
+  const int oi = dpp_i<CTRL, ROWS>(i, i);
+  const bool take = ov > v || (ov == v && oi < i);
+  v = take ? ov : v;
+  i = take ? oi : i;
+}
+
+// wave-wide argmax of (v, i); the result is returned in every lane
+__device__ __forceinline__ void wave_argmax(float &v, int &i) {
+  argmax_step<DPP_QUAD_1032, 0xF>(v, i);
+  argmax_step<DPP_QUAD_2301, 0xF>(v, i);
+  argmax_step<DPP_ROW_HALF_MIRROR, 0xF>(v, i);
+  argmax_step<DPP_ROW_MIRROR, 0xF>(v, i);
+  argmax_step<DPP_ROW_BCAST15, 0xA>(v, i);
+  argmax_step<DPP_ROW_BCAST31, 0xC>(v, i);
+  v = readlane_f(v, 63);
+  i = __builtin_amdgcn_readlane(i, 63);
 }
 
 // ---------------------------------------------------------------------------
-// GEMV pieces. Lane l of a wave covers elements [c*64*EPL + l*EPL, +EPL) of a
-// K-long row for chunk c; rows are 16-byte aligned and K % EPL == 0.
+// GEMV core: NR weight rows times TG activation rows over columns [k0, k1).
+// Lane l covers chunk c0 + s*CH + l*EPL of each step; a step issues all
+// NR*SEG weight loads before the first use. Full steps carry no per-lane guard;
+// the remainder runs chunk by chunk with one. Rows are 16-byte aligned and
+// k0, k1 multiples of EPL. acc[r][t] receives lane partial sums.
 
-// Dot products of one weight row segment [k0, k1) with TG activation rows
-// xr[t] (element offsets as in the weight row), lane partials in acc[t].
-template <int WD, int XD, int SEG, int TG>
-__device__ __forceinline__ void row_dot(const void *wrow, int k0, int k1, const char *const *xr, float *acc) {
-  constexpr int EPL = elems16<WD>();
-  constexpr int NX = Chunk<WD, XD>::NX;
+template <int WD, int XD, bool XL, int NR, int SEG, int TG>
+__device__ __forceinline__ void rows_dot(const char *const (&wrow)[NR], int k0, int k1,
+                                         const typename XSrc<XL>::ptr (&xr)[TG], float (&acc)[NR][TG]) {
+  constexpr int EPL = epl<WD>(), NX = Chunk<WD, XD>::NX, CH = 64 * EPL;
+  constexpr int WB = dsz<WD>(), XB = dsz<XD>();
   const int lane = lane_id();
-  for (int c0 = k0; c0 < k1; c0 += SEG * 64 * EPL) {
-    uint4 w[SEG];
+  int c0 = k0;
+  for (; c0 + SEG * CH <= k1; c0 += SEG * CH) {
+    u32x4 w[NR][SEG];
+#pragma unroll
+    for (int s = 0; s < SEG; ++s)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) w[r][s] = ldw(wrow[r] + (size_t)(c0 + s * CH + lane * EPL) * WB);
 #pragma unroll
     for (int s = 0; s < SEG; ++s) {
-      const int e = c0 + (s * 64 + lane) * EPL;
-      w[s] = (e < k1) ? ld16((const char *)wrow + (size_t)e * (16 / EPL)) : make_uint4(0, 0, 0, 0);
+      const size_t e = (size_t)(c0 + s * CH + lane * EPL);
+#pragma unroll
+      for (int t = 0; t < TG; ++t) {
+        u32x4 xv[NX];
+#pragma unroll
+        for (int q = 0; q < NX; ++q) xv[q] = XSrc<XL>::ld(xr[t], e * XB + 16 * q);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[r][t] = Chunk<WD, XD>::dot(w[r][s], xv, acc[r][t]);
+      }
     }
+  }
+  for (; c0 < k1; c0 += CH) {
+    const int e = c0 + lane * EPL;
+    if (e < k1) {
+      u32x4 w[NR];
 #pragma unroll
-    for (int s = 0; s < SEG; ++s) {
-      const int e = c0 + (s * 64 + lane) * EPL;
-      if (e < k1) {
+      for (int r = 0; r < NR; ++r) w[r] = ldw(wrow[r] + (size_t)e * WB);
 #pragma unroll
-        for (int t = 0; t < TG; ++t) {
-          uint4 xv[NX];
+      for (int t = 0; t < TG; ++t) {
+        u32x4 xv[NX];
 #pragma unroll
-          for (int q = 0; q < NX; ++q) xv[q] = ld16(xr[t] + (size_t)e * xsize<XD>() + 16 * q);
-          acc[t] = Chunk<WD, XD>::dot(w[s], xv, acc[t]);
-        }
+        for (int q = 0; q < NX; ++q) xv[q] = XSrc<XL>::ld(xr[t], (size_t)e * XB + 16 * q);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[r][t] = Chunk<WD, XD>::dot(w[r], xv, acc[r][t]);
       }
     }
   }
 }
 
-// Run f.template operator()<TG>(t0, nt) over groups of up to 8 of n tokens,
-// with the smallest specialisation that holds each group.
+// chunks per step of a gate/up pair (2 rows), sized to the register budget
+template <int WD, int TG> constexpr int seg_gu() {
+  return WD == DT_FP8 ? (TG <= 2 ? 7 : 3) : WD == DT_BF16 ? 7 : 4;
+}
+// chunks per step of a 4-row down unit
+template <int WD, int TG> constexpr int seg_down() { return WD == DT_FP8 ? 1 : WD == DT_BF16 ? 2 : 2; }
+// chunks per step of a router row slice
+template <int WD, int TG> constexpr int seg_router() { return TG <= 2 ? 7 : 4; }
+
+// Run f.template operator()<TG>(t0, nt) over groups of up to kTokGroup of n
+// tokens, with the smallest specialisation that holds each group.
 template <class F>
 __device__ __forceinline__ void for_token_groups(int n, F &&f) {
   for (int t0 = 0; t0 < n; t0 += kTokGroup) {
     const int nt = min(kTokGroup, n - t0);
     if (nt == 1) f.template operator()<1>(t0, nt);
     else if (nt == 2) f.template operator()<2>(t0, nt);
-    else if (nt <= 4) f.template operator()<4>(t0, nt);
-    else f.template operator()<8>(t0, nt);
+    else f.template operator()<4>(t0, nt);
   }
 }
 
-// Gate/up pair task: rows j (gate) and inter+j (up) of a [2 inter][H] matrix
-// for n tokens; writes h[slot][j] = act(SiLU(g * gs) * (u * us)). Tokens are
-// list[q] / div with slot list[q] (expert pairs), or q with slot q (list null).
-template <int AD, int WD>
-__device__ __forceinline__ void gate_up_pair(KParams p, const void *gu, int inter, int j,
-                                                       float gs, float us, const int *list, int div, int n,
-                                                       void *hout, int hstride) {
-  const int H = p->H;
-  const size_t rowb = (size_t)H * (WD == DT_F32 ? 4 : WD == DT_BF16 ? 2 : 1);
-  const void *grow = (const char *)gu + (size_t)j * rowb;
-  const void *urow = (const char *)gu + (size_t)(inter + j) * rowb;
-  for_token_groups(n, [&]<int TG>(int t0, int nt) {
-    const char *xr[TG];
-    int slot[TG];
-#pragma unroll
-    for (int t = 0; t < TG; ++t) {
-      const int q = t0 + (t < nt ? t : 0);
-      slot[t] = list ? list[q] : q;
-      const int tok = list ? slot[t] / div : q;
-      xr[t] = (const char *)p->xa + (size_t)tok * H * xsize<AD>();
+// ---------------------------------------------------------------------------
+// grid barriers
+
+__device__ __forceinline__ long long rt_now() { return (long long)__builtin_amdgcn_s_memrealtime(); }
+
+__device__ __forceinline__ unsigned *ctrl_word(KParams p, int w) { return p->ctrl + (size_t)w * kCtrlStride; }
+
+// A wave is done with the work barrier b waits for.
+__device__ void bar_arrive(KParams p, SmemHead &sh, int b) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if (lane_id() == 0) {
+    const int old = __hip_atomic_fetch_add(&sh.bar_cnt[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (old == kWaves - 1) {
+      // the whole workgroup's stores are in this XCD's L2: write them back for the other XCDs
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_add(ctrl_word(p, CTRL_BAR + b), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    float ag[TG], au[TG];
-#pragma unroll
-    for (int t = 0; t < TG; ++t) ag[t] = au[t] = 0.f;
-    constexpr int SEG = (WD == DT_FP8) ? (TG <= 2 ? 4 : TG == 4 ? 2 : 1) : (TG <= 2 ? 7 : TG == 4 ? 4 : 2);
-    row_dot<WD, AD, SEG, TG>(grow, 0, H, xr, ag);
-    row_dot<WD, AD, SEG, TG>(urow, 0, H, xr, au);
-#pragma unroll
-    for (int t = 0; t < TG; ++t) {
-      if (t < nt) {
-        const float g = wave_sum(ag[t]) * gs;
-        const float u = wave_sum(au[t]) * us;
-        if (lane_id() == 0) store_act<AD>(hout, (size_t)slot[t] * hstride + j, g / (1.0f + expf(-g)) * u);
+  }
+}
+
+// Wait until every workgroup arrived at barrier b.
+__device__ void bar_wait(KParams p, SmemHead &sh, int b) {
+  if (lane_id() == 0) {
+    if (__hip_atomic_load(&sh.bar_flag[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
+      const bool poller =
+          __hip_atomic_exchange(&sh.bar_claim[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
+      const long long t0 = rt_now();
+      if (poller) {
+        unsigned *cnt = ctrl_word(p, CTRL_BAR + b);
+        while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)p->G) {
+          __builtin_amdgcn_s_sleep(1);
+          if (rt_now() - t0 > p->timeout_ticks) {
+            __hip_atomic_store(ctrl_word(p, CTRL_ERR), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(&sh.bar_flag[b], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        while (__hip_atomic_load(&sh.bar_flag[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
+          __builtin_amdgcn_s_sleep(1);
+          if (rt_now() - t0 > 2 * p->timeout_ticks) break;
+        }
       }
     }
-  });
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 // ---------------------------------------------------------------------------
-// top-k of one token (one wave): softmax over all E logits restricted to the
-// k largest (ties to the lower index), renormalised.
+// LDS views
 
-__device__ __attribute__((noinline)) void topk_token(KParams p, KLayer lp, Smem &sm, int t, bool write_out) {
-  const int lane = lane_id();
-  const int E = p->E, k = p->k;
-  constexpr int PER = kMaxE / 64;
-  float v[PER];
-  unsigned taken = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int e = lane + 64 * j;
-    float l = -INFINITY;
-    if (e < E) {
-      float s = 0.f;
-      for (int q = 0; q < p->NS; ++q) s += p->rpart[((size_t)q * p->B + t) * E + e];
-      if (lp->rb) s += lp->rb[e];
-      l = (s == s) ? s : -INFINITY;  // a NaN logit ranks last, so every pick is a valid expert
-      if (write_out && lp->logits_out) lp->logits_out[(size_t)t * E + e] = l;
-    } else {
-      taken |= 1u << j;
-    }
-    v[j] = l;
-  }
-  float lmax = 0.f, z = 0.f;
-  float selv = 0.f;
-  int seli = 0;
-  for (int i = 0; i < k; ++i) {
-    // lane-local best: larger value, then lower index
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = lane + 64 * j;
-      if (!(taken & (1u << j)) && (v[j] > bv || (v[j] == bv && e < bi))) { bv = v[j]; bi = e; }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (i == 0) lmax = bv;
-    const float ex = expf(bv - lmax);
-    z += ex;
-    if (lane == i) { selv = ex; seli = bi; }
-    if (lane == 0) sm.sel_idx[t * k + i] = bi;
-  }
-  if (lane < k) {
-    const float w = selv / z;
-    sm.sel_w[t * k + lane] = w;
-    if (write_out) {
-      if (lp->idx_out) lp->idx_out[(size_t)t * k + lane] = seli;
-      if (lp->w_out) lp->w_out[(size_t)t * k + lane] = w;
-    }
-  }
-}
+struct Lds {
+  unsigned char *base;
+  __device__ SmemHead &head() const { return *reinterpret_cast<SmemHead *>(base); }
+  template <class T> __device__ T *at(int off) const { return reinterpret_cast<T *>(base + off); }
+  __device__ lds_t *raw(int off) const { return (lds_t *)(base + off); }
+};
 
 // ---------------------------------------------------------------------------
-// gather tables: union U of selected experts (ascending), each expert's pairs
-// (t*k+i) in ascending token order.
+// x-hat
 
-__device__ __attribute__((noinline)) void build_tables(KParams p, Smem &sm) {
-  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
-  const int E = p->E, P = p->B * p->k;
-  for (int e = tid; e < E; e += kThreads) { sm.cnt[e] = 0; sm.tmask[e] = 0ull; }
-  __syncthreads();
-  for (int q = tid; q < P; q += kThreads) {
-    const int e = sm.sel_idx[q];
-    atomicAdd(&sm.cnt[e], 1);
-    atomicOr(&sm.tmask[e], 1ull << (q / p->k));
-  }
-  __syncthreads();
-  // block scan over e of (cnt, cnt > 0); E <= kThreads
-  int c = (tid < E) ? sm.cnt[tid] : 0;
-  int f = c > 0 ? 1 : 0;
-  int ci = c, fi = f;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int uc = __shfl_up(ci, o), uf = __shfl_up(fi, o);
-    if (lane >= o) { ci += uc; fi += uf; }
-  }
-  if (lane == 63) { sm.scan_tmp[wv] = ci; sm.scan_tmp[kWaves + wv] = fi; }
-  __syncthreads();
-  int bc = 0, bf = 0;
-  for (int w2 = 0; w2 < wv; ++w2) { bc += sm.scan_tmp[w2]; bf += sm.scan_tmp[kWaves + w2]; }
-  if (tid < E) {
-    sm.start[tid] = bc + ci - c;
-    if (f) sm.ulist[bf + fi - f] = tid;
-  }
-  if (tid == kThreads - 1) {
-    int tot = 0;
-    for (int w2 = 0; w2 < kWaves; ++w2) tot += sm.scan_tmp[kWaves + w2];
-    sm.nU = tot;
-  }
-  __syncthreads();
-  for (int q = tid; q < P; q += kThreads) {
-    const int e = sm.sel_idx[q];
-    const int t = q / p->k;
-    const unsigned long long below = (t == 0) ? 0ull : (sm.tmask[e] & ((1ull << t) - 1ull));
-    sm.plist[sm.start[e] + __popcll(below)] = q;
-  }
-  __syncthreads();
-}
-
-// ---------------------------------------------------------------------------
-// P0a: RMSNorm producers
-
+// Small regime: this workgroup normalises every token into its own LDS:
+// xf [B][H] fp32 (router input) and xa [B][H] act (FFN input).
 template <int AD>
-__device__ __attribute__((noinline)) void produce_xhat(KParams p, KLayer lp, Smem &sm) {
+__device__ __attribute__((noinline)) void stage_xhat(KParams p, KLayer lp, const Lds &L) {
   const int H = p->H, tid = threadIdx.x;
+  SmemHead &sh = L.head();
+  float *xf = L.at<float>(p->o_xf);
+  for (int t = 0; t < p->B; ++t) {
+    float ss = 0.f;
+    for (int h = tid; h < H; h += kThreads) {
+      const float v = load_act<AD>(lp->x, (size_t)t * H + h);
+      ss = fmaf(v, v, ss);
+    }
+    ss = readlane_f(wave_sum63(ss), 63);
+    if (lane_id() == 0) sh.red[wave_id()] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int w2 = 0; w2 < kWaves; ++w2) tot += sh.red[w2];
+    const float r = 1.0f / sqrtf(tot / (float)H + p->eps);
+    for (int h = tid; h < H; h += kThreads) {
+      const float xh = load_act<AD>(lp->x, (size_t)t * H + h) * r * load_act<AD>(lp->gamma, h);
+      xf[(size_t)t * H + h] = xh;
+      if constexpr (AD != DT_F32) store_act_lds<AD>(L.raw(p->o_xa), (size_t)t * H + h, xh);
+    }
+    __syncthreads();
+  }
+}
+
+// General regime: workgroup t normalises token t into global memory.
+template <int AD>
+__device__ __attribute__((noinline)) void produce_xhat(KParams p, KLayer lp, const Lds &L) {
+  const int H = p->H, tid = threadIdx.x;
+  SmemHead &sh = L.head();
   for (int t = blockIdx.x; t < p->B; t += p->G) {
     float ss = 0.f;
     for (int h = tid; h < H; h += kThreads) {
       const float v = load_act<AD>(lp->x, (size_t)t * H + h);
       ss = fmaf(v, v, ss);
     }
-    ss = wave_sum(ss);
-    if (lane_id() == 0) sm.red[wave_id()] = ss;
+    ss = readlane_f(wave_sum63(ss), 63);
+    if (lane_id() == 0) sh.red[wave_id()] = ss;
     __syncthreads();
     float tot = 0.f;
-    for (int w2 = 0; w2 < kWaves; ++w2) tot += sm.red[w2];
+    for (int w2 = 0; w2 < kWaves; ++w2) tot += sh.red[w2];
     const float r = 1.0f / sqrtf(tot / (float)H + p->eps);
     for (int h = tid; h < H; h += kThreads) {
       const float xh = load_act<AD>(lp->x, (size_t)t * H + h) * r * load_act<AD>(lp->gamma, h);
@@ -507,235 +517,497 @@ __device__ __attribute__((noinline)) void produce_xhat(KParams p, KLayer lp, Sme
   }
 }
 
-// ---------------------------------------------------------------------------
-// the kernel
-
-// ---------------------------------------------------------------------------
-// phases
-
-// P0b router: task tau = (row e, K-split s) -> partial logits rpart[s][t][e]
-template <int RD>
-__device__ __forceinline__ void router_phase(KParams p, KLayer lp, int W, int NW) {
-  const int H = p->H, E = p->E, B = p->B, lane = lane_id();
-  const int nrt = E * p->NS, Ks = H / p->NS;
-  for (int tau = W; tau < nrt; tau += NW) {
-    const int e = tau / p->NS, s = tau % p->NS;
-    const void *wrow = (const char *)lp->rw + (size_t)e * H * (RD == DT_F32 ? 4 : 2);
-    for_token_groups(B, [&]<int TG>(int t0, int nt) {
-      const char *xr[TG];
-#pragma unroll
-      for (int t = 0; t < TG; ++t) xr[t] = (const char *)(p->xhat + (size_t)(t0 + (t < nt ? t : 0)) * H);
-      float acc[TG];
-#pragma unroll
-      for (int t = 0; t < TG; ++t) acc[t] = 0.f;
-      constexpr int SEG = TG <= 2 ? 7 : TG == 4 ? 4 : 2;
-      row_dot<RD, DT_F32, SEG, TG>(wrow, s * Ks, (s + 1) * Ks, xr, acc);
-#pragma unroll
-      for (int t = 0; t < TG; ++t)
-        if (t < nt) {
-          const float v = wave_sum(acc[t]);
-          if (lane == 0) p->rpart[((size_t)s * B + t0 + t) * E + e] = v;
-        }
-    });
+// pointer to token t's row of x-hat (fp32 if F32X, else act) in LDS or global memory
+template <bool XL, int AD, bool F32X>
+__device__ __forceinline__ typename XSrc<XL>::ptr xhat_row(KParams p, const Lds &L, int t) {
+  constexpr int XB = F32X ? 4 : dsz<AD>();
+  if constexpr (XL) {
+    const int off = (F32X || AD == DT_F32) ? p->o_xf : p->o_xa;
+    return L.raw(off) + (size_t)t * p->H * XB;
+  } else {
+    const char *base = (F32X || AD == DT_F32) ? (const char *)p->xhat : (const char *)p->xa;
+    return base + (size_t)t * p->H * XB;
   }
 }
 
-// P0b shared expert gate/up: the P0 task list is [router tasks | shared pairs];
-// wave W takes every NW-th task.
-template <int AD, int SD>
-__device__ __forceinline__ void shared_phase(KParams p, KLayer lp, int W, int NW) {
-  const int nrt = p->E * p->NS;
-  int tau = W;
-  while (tau < nrt) tau += NW;
-  for (; tau < nrt + p->Is; tau += NW)
-    gate_up_pair<AD, SD>(p, lp->sgu, p->Is, tau - nrt, 1.f, 1.f, nullptr, 1, p->B, p->hsbuf, p->Is);
-}
+// ---------------------------------------------------------------------------
+// P0: router slices and shared gate/up rows
 
-// P1 expert gate/up: task tau = (expert u of U, pair j)
-template <int AD, int ED>
-__device__ __forceinline__ void expert_phase(KParams p, KLayer lp, Smem &sm, int W,
-                                                       int NW) {
-  const int H = p->H, I = p->I, k = p->k;
-  const int ntask = sm.nU * I;
-  const size_t exp_gu = (size_t)2 * I * H;  // elements per expert
-  for (int tau = W; tau < ntask; tau += NW) {
-    const int u = tau / I, j = tau % I;
-    const int e = sm.ulist[u];
-    const int n = sm.cnt[e];
-    const int *pl = &sm.plist[sm.start[e]];
-    float gs = 1.f, us = 1.f;
-    const void *gu;
-    if constexpr (ED == DT_FP8) {
-      // e4m3_to_f32 is exact, so the bf16 row scale multiplies the finished dot
-      gu = (const uint8_t *)lp->egu + (size_t)e * exp_gu;
-      const uint16_t *sc = lp->egus + (size_t)e * (2 * I / 128);
-      gs = __uint_as_float((uint32_t)sc[j / 128] << 16);
-      us = __uint_as_float((uint32_t)sc[(I + j) / 128] << 16);
-    } else {
-      gu = (const char *)lp->egu + (size_t)e * exp_gu * (ED == DT_F32 ? 4 : 2);
+// task (row e, slice s) -> rpart[s][t][e] for all tokens
+template <int RD, bool XL>
+__device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, int e, int s) {
+  const int H = p->H, E = p->E, B = p->B;
+  const int Ks = H / p->NSR;
+  const char *const wrow[1] = {(const char *)lp->rw + (size_t)e * H * dsz<RD>()};
+  for_token_groups(B, [&]<int TG>(int t0, int nt) {
+    typename XSrc<XL>::ptr xr[TG];
+#pragma unroll
+    for (int t = 0; t < TG; ++t) xr[t] = xhat_row<XL, DT_F32, true>(p, L, t0 + (t < nt ? t : 0));
+    float acc[1][TG];
+#pragma unroll
+    for (int t = 0; t < TG; ++t) acc[0][t] = 0.f;
+    rows_dot<RD, DT_F32, XL, 1, seg_router<RD, TG>(), TG>(wrow, s * Ks, (s + 1) * Ks, xr, acc);
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const float v = wave_sum63(acc[0][t]);
+      if (t < nt && lane_id() == 63) p->rpart[((size_t)s * B + t0 + t) * E + e] = v;
     }
-    gate_up_pair<AD, ED>(p, gu, I, j, gs, us, pl, k, n, p->hbuf, I);
+  });
+}
+
+// shared gate/up task (pair j, slice s). Small regime: partial g and u sums to
+// hspart[s][t][j] and hspart[s][t][Is + j]. General regime (one slice): h.
+template <int AD, int SD, bool XL>
+__device__ __forceinline__ void shared_gu_task(KParams p, KLayer lp, const Lds &L, int j, int s) {
+  const int H = p->H, B = p->B, Is = p->Is;
+  const int Ks = H / p->NSS;
+  const size_t rowb = (size_t)H * dsz<SD>();
+  const char *const wrow[2] = {(const char *)lp->sgu + (size_t)j * rowb, (const char *)lp->sgu + (size_t)(Is + j) * rowb};
+  for_token_groups(B, [&]<int TG>(int t0, int nt) {
+    typename XSrc<XL>::ptr xr[TG];
+#pragma unroll
+    for (int t = 0; t < TG; ++t) xr[t] = xhat_row<XL, AD, false>(p, L, t0 + (t < nt ? t : 0));
+    float acc[2][TG];
+#pragma unroll
+    for (int t = 0; t < TG; ++t) acc[0][t] = acc[1][t] = 0.f;
+    rows_dot<SD, AD, XL, 2, seg_gu<SD, TG>(), TG>(wrow, s * Ks, (s + 1) * Ks, xr, acc);
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const float g = wave_sum63(acc[0][t]);
+      const float u = wave_sum63(acc[1][t]);
+      if (t < nt && lane_id() == 63) {
+        if (p->NSS > 1 || XL) {
+          float *hp = p->hspart + ((size_t)s * B + t0 + t) * 2 * Is;
+          hp[j] = g;
+          hp[Is + j] = u;
+        } else {
+          store_act<AD>(p->hsbuf, (size_t)(t0 + t) * Is + j, silu_mul(g, u));
+        }
+      }
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// top-k of one token (one wave): softmax over all E logits restricted to the
+// k largest (ties to the lower index), renormalised.
+
+__device__ __attribute__((noinline)) void topk_token(KParams p, KLayer lp, const Lds &L, int t, bool write_out) {
+  const int lane = lane_id();
+  const int E = p->E, k = p->k, B = p->B, NSR = p->NSR;
+  constexpr int PER = kMaxE / 64;
+  const float qnan = __builtin_nanf("");
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = lane + 64 * j;
+    float l = qnan;  // not an expert: never selected (NaN compares false)
+    if (e < E) {
+      float s = 0.f;
+      for (int q = 0; q < NSR; ++q) s += p->rpart[((size_t)q * B + t) * E + e];
+      if (lp->rb) s += lp->rb[e];
+      l = (s == s) ? s : -INFINITY;  // a NaN logit ranks last but stays selectable
+      if (write_out && lp->logits_out) lp->logits_out[(size_t)t * E + e] = l;
+    }
+    v[j] = l;
+  }
+  int *sel_idx = L.at<int>(p->o_sel_idx);
+  float *sel_w = L.at<float>(p->o_sel_w);
+  float lmax = 0.f, z = 0.f, selv = 0.f;
+  int seli = 0;
+  for (int i = 0; i < k; ++i) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = lane + 64 * j;
+      if (v[j] > bv || (v[j] == bv && e < bi)) { bv = v[j]; bi = e; }
+    }
+    wave_argmax(bv, bi);
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (lane + 64 * j == bi) v[j] = qnan;  // taken
+    if (i == 0) lmax = bv;
+    const float ex = expf(bv - lmax);
+    z += ex;
+    if (lane == i) { selv = ex; seli = bi; }
+  }
+  if (lane < k) {
+    const float w = selv / z;
+    sel_idx[t * k + lane] = seli;
+    sel_w[t * k + lane] = w;
+    if (write_out) {
+      if (lp->idx_out) lp->idx_out[(size_t)t * k + lane] = seli;
+      if (lp->w_out) lp->w_out[(size_t)t * k + lane] = w;
+    }
   }
 }
 
-// One P2 unit: rows [o0, o0+nr) of one expert's down matrix (or one I-wide
-// column block hf of the shared down matrix) for its tokens; lane-reduced
-// results go to LDS partials part[(o - pr0) * pstride + column].
-template <int AD, int ED, int SD>
-__device__ __forceinline__ void down_unit(KParams p, KLayer lp, Smem &sm, int s,
-                                                    int o0, int nr, int pr0, int pstride) {
-  const int H = p->H, I = p->I, Is = p->Is, B = p->B, lane = lane_id();
-  const int nU = sm.nU, P = B * p->k;
-  const int nsh = Is / I;
-  if (s < nU) {
-    const int e = sm.ulist[s];
-    const int n = sm.cnt[e];
-    const int *pl = &sm.plist[sm.start[e]];
-    const size_t wexp = (size_t)H * I;
-    for_token_groups(n, [&]<int TG>(int t0, int nt) {
-      int slot[TG];
-      const char *xr[TG];
+// gather tables: union U of selected experts (ascending), each expert's pairs
+// (t*k+i) in ascending token order.
+__device__ __attribute__((noinline)) void build_tables(KParams p, const Lds &L) {
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  const int E = p->E, P = p->B * p->k;
+  SmemHead &sh = L.head();
+  int *cnt = L.at<int>(p->o_cnt), *start = L.at<int>(p->o_start), *ulist = L.at<int>(p->o_ulist);
+  int *plist = L.at<int>(p->o_plist);
+  const int *sel_idx = L.at<int>(p->o_sel_idx);
+  unsigned long long *tmask = L.at<unsigned long long>(p->o_tmask);
+  for (int e = tid; e < E; e += kThreads) { cnt[e] = 0; tmask[e] = 0ull; }
+  __syncthreads();
+  for (int q = tid; q < P; q += kThreads) {
+    const int e = sel_idx[q];
+    atomicAdd(&cnt[e], 1);
+    atomicOr(&tmask[e], 1ull << (q / p->k));
+  }
+  __syncthreads();
+  // block scan over e of (cnt, cnt > 0); E <= kThreads
+  const int c = (tid < E) ? cnt[tid] : 0;
+  const int f = c > 0 ? 1 : 0;
+  int ci = c, fi = f;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int uc = __shfl_up(ci, o), uf = __shfl_up(fi, o);
+    if (lane >= o) { ci += uc; fi += uf; }
+  }
+  if (lane == 63) { sh.scan_tmp[wv] = ci; sh.scan_tmp[kWaves + wv] = fi; }
+  __syncthreads();
+  int bc = 0, bf = 0;
+  for (int w2 = 0; w2 < wv; ++w2) { bc += sh.scan_tmp[w2]; bf += sh.scan_tmp[kWaves + w2]; }
+  if (tid < E) {
+    start[tid] = bc + ci - c;
+    if (f) ulist[bf + fi - f] = tid;
+  }
+  if (tid == kThreads - 1) {
+    int tot = 0;
+    for (int w2 = 0; w2 < kWaves; ++w2) tot += sh.scan_tmp[kWaves + w2];
+    sh.nU = tot;
+  }
+  __syncthreads();
+  for (int q = tid; q < P; q += kThreads) {
+    const int e = sel_idx[q];
+    const int t = q / p->k;
+    const unsigned long long below = (t == 0) ? 0ull : (tmask[e] & ((1ull << t) - 1ull));
+    plist[start[e] + __popcll(below)] = q;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// P1: expert gate/up, task (expert u of U, pair j)
+
+template <int AD, int ED, bool XL>
+__device__ __forceinline__ void expert_gu_task(KParams p, KLayer lp, const Lds &L, int u, int j) {
+  const int H = p->H, I = p->I, k = p->k;
+  const int *cnt = L.at<int>(p->o_cnt), *start = L.at<int>(p->o_start), *ulist = L.at<int>(p->o_ulist);
+  const int *plist = L.at<int>(p->o_plist);
+  const int e = ulist[u];
+  const int n = cnt[e];
+  const int *pl = plist + start[e];
+  const size_t rowb = (size_t)H * dsz<ED>();
+  const char *gu = (const char *)lp->egu + (size_t)e * 2 * I * rowb;
+  const char *const wrow[2] = {gu + (size_t)j * rowb, gu + (size_t)(I + j) * rowb};
+  float gs = 1.f, us = 1.f;
+  if constexpr (ED == DT_FP8) {
+    // e4m3_to_f32 is exact, so the bf16 row scale multiplies the finished dot
+    const uint16_t *sc = lp->egus + (size_t)e * (2 * I / 128);
+    gs = __uint_as_float((uint32_t)sc[j / 128] << 16);
+    us = __uint_as_float((uint32_t)sc[(I + j) / 128] << 16);
+  }
+  for_token_groups(n, [&]<int TG>(int t0, int nt) {
+    typename XSrc<XL>::ptr xr[TG];
+    int slot[TG];
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      slot[t] = pl[t0 + (t < nt ? t : 0)];
+      xr[t] = xhat_row<XL, AD, false>(p, L, slot[t] / k);
+    }
+    float acc[2][TG];
+#pragma unroll
+    for (int t = 0; t < TG; ++t) acc[0][t] = acc[1][t] = 0.f;
+    rows_dot<ED, AD, XL, 2, seg_gu<ED, TG>(), TG>(wrow, 0, H, xr, acc);
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const float g = wave_sum63(acc[0][t]) * gs;
+      const float uu = wave_sum63(acc[1][t]) * us;
+      if (t < nt && lane_id() == 63) store_act<AD>(p->hbuf, (size_t)slot[t] * I + j, silu_mul(g, uu));
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// P2: down projections of this workgroup's rows
+
+// shared h for every token from the slice partials, into LDS (small regime)
+template <int AD>
+__device__ __attribute__((noinline)) void finish_shared_h(KParams p, const Lds &L) {
+  const int Is = p->Is, B = p->B, NSS = p->NSS;
+  lds_t *hs = L.raw(p->o_hs);
+  for (int c = threadIdx.x; c < B * Is; c += kThreads) {
+    const int t = c / Is, j = c % Is;
+    float g = 0.f, u = 0.f;
+    for (int s = 0; s < NSS; ++s) {
+      const float *hp = p->hspart + ((size_t)s * B + t) * 2 * Is;
+      g += hp[j];
+      u += hp[Is + j];
+    }
+    store_act_lds<AD>(hs, (size_t)t * Is + j, silu_mul(g, u));
+  }
+}
+
+// expert h of every selected (token, expert) pair into LDS (small regime)
+__device__ __attribute__((noinline)) void stage_h(KParams p, const Lds &L, int act_bytes) {
+  const size_t n16 = (size_t)p->B * p->k * p->I * act_bytes / 16;
+  const u32x4 *src = (const u32x4 *)p->hbuf;
+  __attribute__((address_space(3))) u32x4 *dst = (__attribute__((address_space(3))) u32x4 *)L.raw(p->o_h);
+  for (size_t i = threadIdx.x; i < n16; i += kThreads) dst[i] = src[i];
+}
+
+// One 4-row unit of a [rows][K] down matrix: row pointers wrow, columns
+// [0, I) of x rows xr (TG tokens); writes the row sums times sc[r] to
+// part[(o0 + r - pr0) * pstride + col[t]].
+template <int WD, int AD, bool XL, int TG>
+__device__ __forceinline__ void down_unit(const char *const (&wrow)[kRowBlock], int I,
+                                          const typename XSrc<XL>::ptr (&xr)[TG], const float (&sc)[kRowBlock],
+                                          float *prow, int pstride, const int (&col)[TG], int nt) {
+  float acc[kRowBlock][TG];
+#pragma unroll
+  for (int r = 0; r < kRowBlock; ++r)
+#pragma unroll
+    for (int t = 0; t < TG; ++t) acc[r][t] = 0.f;
+  rows_dot<WD, AD, XL, kRowBlock, seg_down<WD, TG>(), TG>(wrow, 0, I, xr, acc);
+#pragma unroll
+  for (int r = 0; r < kRowBlock; ++r)
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const float v = wave_sum63(acc[r][t]) * sc[r];
+      if (t < nt && lane_id() == 63) prow[r * pstride + col[t]] = v;
+    }
+}
+
+// shared-expert units of rows [pr0, pr1): (row block, column block hf)
+template <int AD, int SD, bool XL>
+__device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, int w0) {
+  const int I = p->I, Is = p->Is, B = p->B;
+  const int nsh = Is / I, P = B * p->k, pstride = P + B * nsh;
+  const int nrb = (pr1 - pr0) / kRowBlock;
+  float *part = L.at<float>(p->o_part);
+  const float one[kRowBlock] = {1.f, 1.f, 1.f, 1.f};
+  for (int un = (wave_id() + kWaves - w0 % kWaves) % kWaves; un < nrb * nsh; un += kWaves) {
+    const int rb = un / nsh, hf = un % nsh;
+    const int o0 = pr0 + rb * kRowBlock;
+    const char *wrow[kRowBlock];
+#pragma unroll
+    for (int r = 0; r < kRowBlock; ++r)
+      wrow[r] = (const char *)lp->sd + ((size_t)(o0 + r) * Is + (size_t)hf * I) * dsz<SD>();
+    for_token_groups(B, [&]<int TG>(int t0, int nt) {
+      typename XSrc<XL>::ptr xr[TG];
+      int col[TG];
 #pragma unroll
       for (int t = 0; t < TG; ++t) {
-        slot[t] = pl[t0 + (t < nt ? t : 0)];
-        xr[t] = (const char *)p->hbuf + (size_t)slot[t] * I * xsize<AD>();
+        const int tt = t0 + (t < nt ? t : 0);
+        if constexpr (XL) xr[t] = L.raw(p->o_hs) + ((size_t)tt * Is + (size_t)hf * I) * dsz<AD>();
+        else xr[t] = (const char *)p->hsbuf + ((size_t)tt * Is + (size_t)hf * I) * dsz<AD>();
+        col[t] = P + (t0 + t) * nsh + hf;
       }
-      for (int r = 0; r < nr; ++r) {
-        const int o = o0 + r;
-        float acc[TG];
-#pragma unroll
-        for (int t = 0; t < TG; ++t) acc[t] = 0.f;
-        const void *wrow = (const char *)lp->ed + (e * wexp + (size_t)o * I) * (ED == DT_F32 ? 4 : ED == DT_BF16 ? 2 : 1);
-        row_dot<ED, AD, (ED == DT_FP8 ? 1 : 2), TG>(wrow, 0, I, xr, acc);
-        float sc = 1.f;
-        if constexpr (ED == DT_FP8) sc = __uint_as_float((uint32_t)lp->eds[(size_t)e * (H / 128) + o / 128] << 16);
-#pragma unroll
-        for (int t = 0; t < TG; ++t)
-          if (t < nt) {
-            const float v = wave_sum(acc[t]) * sc;
-            if (lane == 0) sm.part[(o - pr0) * pstride + slot[t]] = v;
-          }
-      }
-    });
-  } else {
-    const int hf = s - nU;
-    for_token_groups(B, [&]<int TG>(int t0, int nt) {
-      const char *xr[TG];
-#pragma unroll
-      for (int t = 0; t < TG; ++t)
-        xr[t] = (const char *)p->hsbuf + ((size_t)(t0 + (t < nt ? t : 0)) * Is + (size_t)hf * I) * xsize<AD>();
-      for (int r = 0; r < nr; ++r) {
-        const int o = o0 + r;
-        float acc[TG];
-#pragma unroll
-        for (int t = 0; t < TG; ++t) acc[t] = 0.f;
-        const void *wrow = (const char *)lp->sd + ((size_t)o * Is + (size_t)hf * I) * (SD == DT_F32 ? 4 : 2);
-        row_dot<SD, AD, 2, TG>(wrow, 0, I, xr, acc);
-#pragma unroll
-        for (int t = 0; t < TG; ++t)
-          if (t < nt) {
-            const float v = wave_sum(acc[t]);
-            if (lane == 0) sm.part[(o - pr0) * pstride + P + (t0 + t) * nsh + hf] = v;
-          }
-      }
+      down_unit<SD, AD, XL, TG>(wrow, I, xr, one, part + (size_t)(o0 - pr0) * pstride, pstride, col, nt);
     });
   }
 }
 
-// P2: this workgroup's output rows: all units, then the fixed-order combine
-// y = x + shared + sum_i w_i d_i (rank order i).
-template <int AD, int ED, int SD>
-__device__ __forceinline__ void down_phase(KParams p, KLayer lp, Smem &sm) {
-  const int H = p->H, k = p->k, B = p->B, tid = threadIdx.x, wv = wave_id();
-  const int nsh = p->Is > 0 ? p->Is / p->I : 0;
-  const int r0 = blockIdx.x * p->rows_per_wg;
-  const int r1 = min(H, r0 + p->rows_per_wg);
-  const int P = B * k;
-  const int pstride = P + B * nsh;
-  const int nslot = sm.nU + nsh;
-  for (int pr0 = r0; pr0 < r1; pr0 += p->pass_rows) {
-    const int pr1 = min(r1, pr0 + p->pass_rows);
-    const int nrb = (pr1 - pr0 + kRowBlock - 1) / kRowBlock;
-    const int nunit = nrb * nslot;
-    for (int un = wv; un < nunit; un += kWaves) {
-      const int rb = un / nslot, s = un % nslot;
-      const int o0 = pr0 + rb * kRowBlock;
-      down_unit<AD, ED, SD>(p, lp, sm, s, o0, min(kRowBlock, pr1 - o0), pr0, pstride);
+// routed-expert units of rows [pr0, pr1): (row block, expert slot)
+template <int AD, int ED, bool XL>
+__device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, int w0) {
+  const int H = p->H, I = p->I, B = p->B;
+  const int nsh = p->Is / I, P = B * p->k, pstride = P + B * nsh;
+  const int nU = L.head().nU;
+  const int nrb = (pr1 - pr0) / kRowBlock;
+  const int *cnt = L.at<int>(p->o_cnt), *start = L.at<int>(p->o_start), *ulist = L.at<int>(p->o_ulist);
+  const int *plist = L.at<int>(p->o_plist);
+  float *part = L.at<float>(p->o_part);
+  for (int un = (wave_id() + kWaves - w0 % kWaves) % kWaves; un < nrb * nU; un += kWaves) {
+    const int rb = un / nU, s = un % nU;
+    const int o0 = pr0 + rb * kRowBlock;
+    const int e = ulist[s];
+    const int n = cnt[e];
+    const int *pl = plist + start[e];
+    const char *wrow[kRowBlock];
+    float sc[kRowBlock];
+#pragma unroll
+    for (int r = 0; r < kRowBlock; ++r) {
+      wrow[r] = (const char *)lp->ed + ((size_t)e * H + o0 + r) * I * dsz<ED>();
+      sc[r] = 1.f;
+      if constexpr (ED == DT_FP8) sc[r] = __uint_as_float((uint32_t)lp->eds[(size_t)e * (H / 128) + (o0 + r) / 128] << 16);
     }
-    __syncthreads();
-    const int cells = (pr1 - pr0) * B;
-    for (int c = tid; c < cells; c += kThreads) {
-      const int ro = c / B, t = c % B;
-      const int o = pr0 + ro;
-      const float *pp = &sm.part[ro * pstride];
-      float sh = 0.f;
-      for (int hf = 0; hf < nsh; ++hf) sh += pp[P + t * nsh + hf];
-      float rt = 0.f;
-      for (int i = 0; i < k; ++i) rt = fmaf(sm.sel_w[t * k + i], pp[t * k + i], rt);
-      const float v = load_act<AD>(lp->x, (size_t)t * H + o) + sh + rt;
-      store_act<AD>(lp->y, (size_t)t * H + o, v);
-    }
-    __syncthreads();
+    for_token_groups(n, [&]<int TG>(int t0, int nt) {
+      typename XSrc<XL>::ptr xr[TG];
+      int col[TG];
+#pragma unroll
+      for (int t = 0; t < TG; ++t) {
+        col[t] = pl[t0 + (t < nt ? t : 0)];
+        if constexpr (XL) xr[t] = L.raw(p->o_h) + (size_t)col[t] * I * dsz<AD>();
+        else xr[t] = (const char *)p->hbuf + (size_t)col[t] * I * dsz<AD>();
+      }
+      down_unit<ED, AD, XL, TG>(wrow, I, xr, sc, part + (size_t)(o0 - pr0) * pstride, pstride, col, nt);
+    });
   }
+}
+
+// y = x + shared + sum_i w_i d_i (rank order i) for rows [pr0, pr1)
+template <int AD>
+__device__ __forceinline__ void combine(KParams p, KLayer lp, const Lds &L, int pr0, int pr1) {
+  const int H = p->H, k = p->k, B = p->B;
+  const int nsh = p->Is / p->I, P = B * k, pstride = P + B * nsh;
+  const float *part = L.at<float>(p->o_part);
+  const float *sel_w = L.at<float>(p->o_sel_w);
+  const int cells = (pr1 - pr0) * B;
+  for (int c = threadIdx.x; c < cells; c += kThreads) {
+    const int ro = c / B, t = c % B;
+    const int o = pr0 + ro;
+    const float *pp = part + (size_t)ro * pstride;
+    float sh = 0.f;
+    for (int hf = 0; hf < nsh; ++hf) sh += pp[P + t * nsh + hf];
+    float rt = 0.f;
+    for (int i = 0; i < k; ++i) rt = fmaf(sel_w[t * k + i], pp[t * k + i], rt);
+    const float v = load_act<AD>(lp->x, (size_t)t * H + o) + sh + rt;
+    store_act<AD>(lp->y, (size_t)t * H + o, v);
+  }
+}
+
+// Bring the lines of [p, p + bytes) into the caches: one 4-byte load per
+// 128-byte line, folded into a value that is never used.
+__device__ __forceinline__ unsigned touch_lines(const char *p, size_t bytes) {
+  unsigned acc = 0;
+  for (size_t off = (size_t)lane_id() * 128; off < bytes; off += 64 * 128) acc ^= *(const unsigned *)(p + off);
+  return acc;
+}
+
+// The weights this wave reads first in the next layer's P0 (its router and
+// shared gate/up slices), loaded while the layer barrier is pending.
+template <int RD, int SD>
+__device__ __forceinline__ unsigned prefetch_p0(KParams p, KLayer nl, int W, int NW) {
+  const int H = p->H, NSR = p->NSR, NSS = p->NSS, E = p->E, Is = p->Is;
+  const int nrt = E * NSR;
+  unsigned acc = 0;
+  for (int tau = W; tau < nrt + Is * NSS; tau += NW) {
+    if (tau < nrt) {
+      const int e = tau / NSR, s = tau % NSR;
+      const size_t ks = (size_t)(H / NSR) * dsz<RD>();
+      acc ^= touch_lines((const char *)nl->rw + (size_t)e * H * dsz<RD>() + s * ks, ks);
+    } else {
+      const int j = (tau - nrt) / NSS, s = (tau - nrt) % NSS;
+      const size_t ks = (size_t)(H / NSS) * dsz<SD>();
+      const size_t rowb = (size_t)H * dsz<SD>();
+      acc ^= touch_lines((const char *)nl->sgu + (size_t)j * rowb + s * ks, ks);
+      acc ^= touch_lines((const char *)nl->sgu + (size_t)(Is + j) * rowb + s * ks, ks);
+    }
+  }
+  return acc;
 }
 
 // ---------------------------------------------------------------------------
 // the kernel
 
-template <int AD, int RD, int ED, int SD>
+template <int AD, int RD, int ED, int SD, bool SMALL>
 __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
   // read the parameters in place in the kernarg segment (scalar loads; no private copy)
   (void)params;
   KParams p = (KParams)__builtin_amdgcn_kernarg_segment_ptr();
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+  const Lds L{smem_raw};
+  SmemHead &sh = L.head();
   const int tid = threadIdx.x, wv = wave_id();
   const int NW = p->G * kWaves;
   const int W = blockIdx.x * kWaves + wv;  // global wave id
 
-  for (int i = tid; i < kMaxBarriers; i += kThreads) sm.bar_cnt[i] = sm.bar_claim[i] = sm.bar_flag[i] = 0;
+  for (int i = tid; i < kMaxBarriers; i += kThreads) sh.bar_cnt[i] = sh.bar_claim[i] = sh.bar_flag[i] = 0;
+  if (tid == 0) sh.sink = 0;
   __syncthreads();
 
-  int nb = 0;  // global barrier number
+  unsigned sink = 0;
   for (int l = 0; l < p->L; ++l) {
     KLayer lp = &p->lp[l];
-    const int b0 = 4 * l;
+    const int b0 = kBarPerLayer * l;
 
-    produce_xhat<AD>(p, lp, sm);
-    bar_arrive(p, sm, b0);
-    bar_wait(p, sm, b0, nb++);
+    // x-hat
+    if constexpr (SMALL) {
+      stage_xhat<AD>(p, lp, L);
+    } else {
+      produce_xhat<AD>(p, lp, L);
+      bar_arrive(p, sh, b0 + BAR_XHAT);
+      bar_wait(p, sh, b0 + BAR_XHAT);
+    }
 
-    router_phase<RD>(p, lp, W, NW);
-    bar_arrive(p, sm, b0 + 1);
-    if (!p->route_only) shared_phase<AD, SD>(p, lp, W, NW);
-    bar_wait(p, sm, b0 + 1, nb++);
+    // P0: router slices, then shared gate/up
+    const int nrt = p->E * p->NSR;
+    int tau = W;
+    for (; tau < nrt; tau += NW) router_task<RD, SMALL>(p, lp, L, tau / p->NSR, tau % p->NSR);
+    bar_arrive(p, sh, b0 + BAR_ROUTER);
+    if (!p->route_only) {
+      for (; tau < nrt + p->Is * p->NSS; tau += NW)
+        shared_gu_task<AD, SD, SMALL>(p, lp, L, (tau - nrt) / p->NSS, (tau - nrt) % p->NSS);
+      bar_arrive(p, sh, b0 + BAR_SHARED);
+    }
+    bar_wait(p, sh, b0 + BAR_ROUTER);
 
     if (p->route_only) {
       if (blockIdx.x == 0)
-        for (int t = wv; t < p->B; t += kWaves) topk_token(p, lp, sm, t, true);
+        for (int t = wv; t < p->B; t += kWaves) topk_token(p, lp, L, t, true);
       break;
     }
-    for (int t = wv; t < p->B; t += kWaves) topk_token(p, lp, sm, t, blockIdx.x == 0);
-    __syncthreads();
-    build_tables(p, sm);
-    expert_phase<AD, ED>(p, lp, sm, W, NW);
-    bar_arrive(p, sm, b0 + 2);
-    bar_wait(p, sm, b0 + 2, nb++);
 
-    down_phase<AD, ED, SD>(p, lp, sm);
+    // P1: routing, gather tables, expert gate/up
+    for (int t = wv; t < p->B; t += kWaves) topk_token(p, lp, L, t, blockIdx.x == 0);
+    __syncthreads();
+    build_tables(p, L);
+    const int ntask = sh.nU * p->I;
+    for (int q = W; q < ntask; q += NW) expert_gu_task<AD, ED, SMALL>(p, lp, L, q / p->I, q % p->I);
+    bar_arrive(p, sh, b0 + BAR_H);
+
+    // P2: this workgroup's output rows
+    const int r0 = blockIdx.x * p->rows_per_wg;
+    const int r1 = min(p->H, r0 + p->rows_per_wg);
+    const bool one_pass = p->pass_rows >= p->rows_per_wg;
+    const int nsh = p->Is / p->I;
+    bar_wait(p, sh, b0 + BAR_SHARED);
+    if constexpr (SMALL) {
+      __syncthreads();  // x-hat in LDS is dead; its space now holds shared h and the partials
+      finish_shared_h<AD>(p, L);
+      __syncthreads();
+    }
+    if (one_pass && r0 < r1) shared_down_units<AD, SD, SMALL>(p, lp, L, r0, r1, 0);
+    bar_wait(p, sh, b0 + BAR_H);
+    if constexpr (SMALL) {
+      stage_h(p, L, dsz<AD>());
+      __syncthreads();
+    }
+    for (int pr0 = r0; pr0 < r1; pr0 += p->pass_rows) {
+      const int pr1 = min(r1, pr0 + p->pass_rows);
+      const int nrb = (pr1 - pr0) / kRowBlock;
+      if (!one_pass) shared_down_units<AD, SD, SMALL>(p, lp, L, pr0, pr1, 0);
+      expert_down_units<AD, ED, SMALL>(p, lp, L, pr0, pr1, one_pass ? 0 : nrb * nsh);
+      __syncthreads();
+      combine<AD>(p, lp, L, pr0, pr1);
+      __syncthreads();
+    }
+
     if (l + 1 < p->L) {
-      bar_arrive(p, sm, b0 + 3);
-      bar_wait(p, sm, b0 + 3, nb++);
+      bar_arrive(p, sh, b0 + BAR_LAYER);
+      sink ^= prefetch_p0<RD, SD>(p, &p->lp[l + 1], W, NW);
+      bar_wait(p, sh, b0 + BAR_LAYER);
     }
   }
+  if (sink == 0x9E3779B9u) sh.sink = sink;  // keeps the prefetch loads; practically never taken
 
   // last workgroup out resets the counters for the next launch on this workspace
   __syncthreads();
   if (tid == 0) {
-    const unsigned old = __hip_atomic_fetch_add(&p->ctrl[kCtrlDone], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned old =
+        __hip_atomic_fetch_add(ctrl_word(p, CTRL_DONE), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (unsigned)p->G - 1u) {
-      __hip_atomic_store(&p->ctrl[kCtrlBar], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p->ctrl[kCtrlDone], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      for (int b = 0; b < kBarPerLayer * p->L; ++b)
+        __hip_atomic_store(ctrl_word(p, CTRL_BAR + b), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctrl_word(p, CTRL_DONE), 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -763,15 +1035,12 @@ DevInfo g_dev[64];
 
 moe_status device_info(DevInfo &out) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-    return fail(MOE_ERR_DEVICE, "hipGetDevice failed");
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(MOE_ERR_DEVICE, "hipGetDevice failed");
   if (g_dev[dev].cus == 0) {
     hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
-      return fail(MOE_ERR_DEVICE, "hipGetDeviceProperties failed");
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(MOE_ERR_DEVICE, "hipGetDeviceProperties failed");
     int lds = 0;
-    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-      lds = 65536;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) lds = 65536;
     g_dev[dev].max_lds = lds;
     g_dev[dev].cus = prop.multiProcessorCount;
   }
@@ -796,8 +1065,7 @@ moe_status check_desc(const moe_layer_desc *d) {
     return fail(MOE_ERR_UNSUPPORTED, "shared_inter=%d: need 0 or a multiple of expert_inter, at most 8192",
                 d->shared_inter);
   if (d->top_k > kMaxK || d->top_k > d->num_experts || d->num_experts > kMaxE)
-    return fail(MOE_ERR_UNSUPPORTED, "top_k=%d num_experts=%d: need 1<=k<=32, k<=E<=1024", d->top_k,
-                d->num_experts);
+    return fail(MOE_ERR_UNSUPPORTED, "top_k=%d num_experts=%d: need 1<=k<=32, k<=E<=1024", d->top_k, d->num_experts);
   const bool f32set = d->act == MOE_F32 && d->router == MOE_F32 && d->expert == MOE_F32 && d->shared == MOE_F32;
   const bool bfset = d->act == MOE_BF16 && (d->router == MOE_F32 || d->router == MOE_BF16) &&
                      (d->expert == MOE_BF16 || d->expert == MOE_FP8_E4M3) && d->shared == MOE_BF16;
@@ -807,26 +1075,34 @@ moe_status check_desc(const moe_layer_desc *d) {
   return MOE_OK;
 }
 
-int router_splits(const moe_layer_desc *d) {
-  const int chunk = 64 * (d->router == MOE_F32 ? 4 : 8);
-  return ((d->hidden / 2) % chunk == 0) ? 2 : 1;
+// K-slices of a row of `hidden` elements of dtype dt: the most (of `most`,
+// halving) that keep whole 64-lane chunks per slice and about 4 KB or more.
+int k_slices(int hidden, moe_dtype dt, int most) {
+  const int chunk = 64 * (16 / dsize(dt));
+  for (int ns = most; ns > 1; ns /= 2)
+    if ((hidden / ns) % chunk == 0 && (size_t)hidden * dsize(dt) / ns >= 4096) return ns;
+  return 1;
 }
 
+bool small_regime(int B) { return B <= kSmallB; }
+
 struct WsLayout {
-  size_t xhat, xa, rpart, hbuf, hsbuf, xbuf0, xbuf1, total;
+  size_t xhat, xa, rpart, hspart, hbuf, hsbuf, xbuf0, xbuf1, total;
 };
 
 size_t up256(size_t v) { return (v + 255u) & ~(size_t)255u; }
 
 WsLayout ws_layout(const moe_layer_desc *d, int B, int L) {
   WsLayout w{};
-  size_t off = kCtrlBytes;
+  size_t off = up256(kCtrlBytes);
   const size_t act = (size_t)dsize(d->act);
+  const size_t is = (size_t)(d->shared_inter > 0 ? d->shared_inter : 1);
   w.xhat = off; off += up256((size_t)B * d->hidden * 4);
   w.xa = off; off += up256((size_t)B * d->hidden * act);
-  w.rpart = off; off += up256((size_t)2 * B * d->num_experts * 4);
+  w.rpart = off; off += up256((size_t)4 * B * d->num_experts * 4);
+  w.hspart = off; off += up256((size_t)2 * B * 2 * is * 4);
   w.hbuf = off; off += up256((size_t)B * d->top_k * d->expert_inter * act);
-  w.hsbuf = off; off += up256((size_t)B * (d->shared_inter > 0 ? d->shared_inter : 1) * act);
+  w.hsbuf = off; off += up256((size_t)B * is * act);
   w.xbuf0 = off; off += (L > 1) ? up256((size_t)B * d->hidden * act) : 0;
   w.xbuf1 = off; off += (L > 2) ? up256((size_t)B * d->hidden * act) : 0;
   w.total = off;
@@ -835,13 +1111,18 @@ WsLayout ws_layout(const moe_layer_desc *d, int B, int L) {
 
 typedef void (*kernel_fn)(Params);
 
-kernel_fn pick_kernel(const moe_layer_desc *d) {
-  if (d->act == MOE_F32) return moe_kernel<DT_F32, DT_F32, DT_F32, DT_F32>;
+template <bool S>
+kernel_fn pick_kernel_t(const moe_layer_desc *d) {
+  if (d->act == MOE_F32) return moe_kernel<DT_F32, DT_F32, DT_F32, DT_F32, S>;
   if (d->expert == MOE_BF16)
-    return d->router == MOE_F32 ? moe_kernel<DT_BF16, DT_F32, DT_BF16, DT_BF16>
-                                : moe_kernel<DT_BF16, DT_BF16, DT_BF16, DT_BF16>;
-  return d->router == MOE_F32 ? moe_kernel<DT_BF16, DT_F32, DT_FP8, DT_BF16>
-                              : moe_kernel<DT_BF16, DT_BF16, DT_FP8, DT_BF16>;
+    return d->router == MOE_F32 ? moe_kernel<DT_BF16, DT_F32, DT_BF16, DT_BF16, S>
+                                : moe_kernel<DT_BF16, DT_BF16, DT_BF16, DT_BF16, S>;
+  return d->router == MOE_F32 ? moe_kernel<DT_BF16, DT_F32, DT_FP8, DT_BF16, S>
+                              : moe_kernel<DT_BF16, DT_BF16, DT_FP8, DT_BF16, S>;
+}
+
+kernel_fn pick_kernel(const moe_layer_desc *d, bool small) {
+  return small ? pick_kernel_t<true>(d) : pick_kernel_t<false>(d);
 }
 
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
@@ -865,9 +1146,10 @@ moe_status check_weights(const moe_layer_desc *d, const moe_layer_weights *w) {
   return MOE_OK;
 }
 
+size_t align16(size_t v) { return (v + 15u) & ~(size_t)15u; }
+
 moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int L, const void *x, void *y, int B,
-                  int32_t *idx, float *wts, float *logits, void *ws, size_t ws_bytes, void *stream,
-                  bool route_only) {
+                  int32_t *idx, float *wts, float *logits, void *ws, size_t ws_bytes, void *stream, bool route_only) {
   moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
   if (B < 1 || B > kMaxB) return fail(MOE_ERR_UNSUPPORTED, "batch %d outside 1..64", B);
@@ -894,21 +1176,55 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   memset(&p, 0, sizeof p);
   p.H = d->hidden; p.E = d->num_experts; p.k = d->top_k; p.I = d->expert_inter; p.Is = d->shared_inter;
   p.B = B; p.L = L; p.route_only = route_only ? 1 : 0; p.eps = d->rms_eps;
-  p.NS = router_splits(d);
   p.G = di.cus;
   if (p.G < 1) return fail(MOE_ERR_DEVICE, "device reports no compute units");
+  const bool small = small_regime(B);
+  p.NSR = k_slices(d->hidden, d->router, 4);
+  p.NSS = small && d->shared_inter > 0 ? k_slices(d->hidden, d->shared, 2) : 1;
   int rpw = (p.H + p.G - 1) / p.G;
   rpw = (rpw + kRowBlock - 1) / kRowBlock * kRowBlock;
   p.rows_per_wg = rpw;
+
+  // LDS carve-up
+  const int E = d->num_experts, P = B * d->top_k, H = d->hidden;
   const int nsh = d->shared_inter > 0 ? d->shared_inter / d->expert_inter : 0;
-  const size_t fixed = (offsetof(Smem, part) + 15) & ~(size_t)15;
-  const size_t per_row = (size_t)(B * d->top_k + B * nsh) * sizeof(float);
+  const size_t act = (size_t)dsize(d->act);
+  size_t o = align16(sizeof(SmemHead));
+  p.o_sel_idx = (int)o; o = align16(o + (size_t)P * 4);
+  p.o_sel_w = (int)o; o = align16(o + (size_t)P * 4);
+  p.o_cnt = (int)o; o = align16(o + (size_t)E * 4);
+  p.o_start = (int)o; o = align16(o + (size_t)E * 4);
+  p.o_tmask = (int)o; o = align16(o + (size_t)E * 8);
+  p.o_ulist = (int)o; o = align16(o + (size_t)E * 4);
+  p.o_plist = (int)o; o = align16(o + (size_t)P * 4);
+  const size_t region = o;
+  size_t need_a = 0, p2_fixed = 0;
+  if (small) {
+    p.o_xf = (int)region;
+    size_t a = align16(region + (size_t)B * H * 4);
+    p.o_xa = (int)a;
+    need_a = (d->act == MOE_F32) ? a : align16(a + (size_t)B * H * act);
+    p.o_hs = (int)region;
+    size_t b = align16(region + (size_t)B * (d->shared_inter > 0 ? d->shared_inter : 1) * act);
+    p.o_h = (int)b;
+    b = align16(b + (size_t)P * d->expert_inter * act);
+    p2_fixed = b;
+  } else {
+    p2_fixed = region;
+  }
+  p.o_part = (int)p2_fixed;
+  const size_t per_row = (size_t)(P + B * nsh) * sizeof(float);
   const size_t lds_cap = (size_t)(di.max_lds > 0 ? di.max_lds : 65536);
-  size_t budget = lds_cap > fixed + 4096 ? lds_cap - fixed : 4096;
-  int pr = (int)(budget / per_row);
+  if (need_a > lds_cap || p2_fixed + (size_t)kRowBlock * per_row > lds_cap)
+    return fail(MOE_ERR_UNSUPPORTED, "shape needs more LDS than the device's %zu bytes", lds_cap);
+  int pr = (int)((lds_cap - p2_fixed) / per_row);
   pr = pr / kRowBlock * kRowBlock;
-  if (pr < kRowBlock) return fail(MOE_ERR_UNSUPPORTED, "LDS too small for batch %d", B);
   p.pass_rows = pr < rpw ? pr : rpw;
+  if (small && p.pass_rows < rpw)
+    return fail(MOE_ERR_UNSUPPORTED, "small-batch layout needs one LDS pass over %d rows", rpw);
+  size_t lds = p2_fixed + (size_t)p.pass_rows * per_row;
+  if (need_a > lds) lds = need_a;
+
   p.timeout_ticks = 200000000LL;  // 2 s at 100 MHz
   // test hook: a tiny limit makes every barrier wait give up at once (no hang, no fault)
   if (const char *ev = getenv("MOE_DEBUG_BARRIER_TIMEOUT_TICKS")) p.timeout_ticks = atoll(ev);
@@ -917,6 +1233,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   p.xhat = (float *)(wsb + wl.xhat);
   p.xa = (d->act == MOE_F32) ? (void *)p.xhat : (void *)(wsb + wl.xa);
   p.rpart = (float *)(wsb + wl.rpart);
+  p.hspart = (float *)(wsb + wl.hspart);
   p.hbuf = wsb + wl.hbuf;
   p.hsbuf = wsb + wl.hsbuf;
   p.xbuf[0] = wsb + wl.xbuf0;
@@ -934,8 +1251,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     lp.w_out = wts ? wts + (size_t)l * B * d->top_k : nullptr;
     lp.logits_out = logits;
   }
-  const size_t lds = fixed + (size_t)p.pass_rows * per_row;
-  kernel_fn fn = pick_kernel(d);
+  kernel_fn fn = pick_kernel(d, small);
   if (hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return fail(MOE_ERR_DEVICE, "hipFuncSetAttribute(%zu bytes of LDS) failed", lds);
   // the grid is persistent: one resident workgroup per CU is required
@@ -979,13 +1295,12 @@ moe_status moe_check_workspace(void *ws, size_t ws_bytes, void *stream) {
   if (!ws || ws_bytes < kCtrlBytes) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace is NULL or too small");
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return fail(MOE_ERR_DEVICE, "stream sync failed");
   unsigned err = 0;
-  if (hipMemcpy(&err, (unsigned char *)ws + kCtrlErr * sizeof(unsigned), sizeof err, hipMemcpyDeviceToHost) !=
-      hipSuccess)
+  unsigned char *word = (unsigned char *)ws + (size_t)CTRL_ERR * kCtrlStride * sizeof(unsigned);
+  if (hipMemcpy(&err, word, sizeof err, hipMemcpyDeviceToHost) != hipSuccess)
     return fail(MOE_ERR_DEVICE, "reading the error word failed");
   if (err) {
     const unsigned zero = 0;
-    if (hipMemcpy((unsigned char *)ws + kCtrlErr * sizeof(unsigned), &zero, sizeof zero, hipMemcpyHostToDevice) !=
-        hipSuccess)
+    if (hipMemcpy(word, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess)
       return fail(MOE_ERR_DEVICE, "clearing the error word failed");
     return fail(MOE_ERR_TIMEOUT, "a launch on this workspace stopped at its barrier watchdog");
   }
