@@ -110,16 +110,20 @@ struct Params {
   unsigned *ctrl;         // control words, kCtrlStride apart
   float *xhat;            // [B][H] fp32 (general regime)
   void *xa;               // [B][H] act (general regime; == xhat for fp32 activations)
-  float *rpart;           // [NSR][B][E]
+  float *rpart;           // [B][E][4]: slice s of expert e's logit at [t][e][s] (s < NSR)
   float *hspart;          // [NSS][B][2 Is] (small regime)
   void *hbuf;             // [B*k][I] act
   void *hsbuf;            // [B][Is] act (general regime)
   void *xbuf[2];          // [B][H] act, stack intermediates
   // LDS carve-up, byte offsets from the start of dynamic LDS
-  int o_sel_idx, o_sel_w, o_cnt, o_start, o_tmask, o_ulist, o_plist;
-  int o_xf, o_xa;         // small regime, P0-P1: x-hat fp32 / act [B][H]
-  int o_hs, o_h;          // small regime, P2: shared h [B][Is], expert h [B*k][I] (act)
-  int o_part;             // P2 partial sums [pass_rows][pstride] fp32
+  int o_sel_idx, o_sel_w;           // routing of each token [B*k]
+  int o_ulist, o_ucnt, o_ustart;    // gather tables per union slot [min(E, B*k)]
+  int o_plist;                      // (token, rank) pairs grouped by expert [B*k]
+  int o_cnt, o_start, o_tmask;      // per-expert scratch of the workgroup-wide table build [E]
+  int o_xf, o_xa;                   // small regime: x-hat fp32 / act [B][H]
+  int o_hs;                         // small regime: shared h [B][Is] (act)
+  int o_h;                          // small regime: expert h [B*k][I] (act), over x-hat once P1 is done
+  int o_part;                       // P2 partial sums [pass_rows][pstride] fp32
   LayerPtrs lp[kMaxL];
 };
 
@@ -128,9 +132,14 @@ struct SmemHead {
   int bar_cnt[kMaxBarriers];    // waves of this workgroup that arrived
   int bar_claim[kMaxBarriers];  // one wave polls the global counter
   int bar_flag[kMaxBarriers];   // raised once the barrier is passed
-  float red[kWaves];
+  float red[kWaves * kSmallB];
   int scan_tmp[2 * kWaves];
   int nU;
+  int route_claim, route_ready;    // small regime: the first free wave does the routing
+  int shared_claim, shared_ready;  // small regime: ... and the shared expert's h
+  int unit_ctr[2];                 // small regime: P2 units handed out to waves
+  unsigned cand_key[kWaves][2 * 64];  // top-k candidates of each wave (ordered logit bits), then the ranked k
+  int cand_idx[kWaves][2 * 64];
   unsigned sink;
 };
 
@@ -140,6 +149,7 @@ typedef const KARG Params *KParams;
 typedef const KARG LayerPtrs *KLayer;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) unsigned char lds_t;
 
 // ---------------------------------------------------------------------------
@@ -183,6 +193,12 @@ template <int D> __device__ __forceinline__ void store_act(void *p, size_t i, fl
 template <int D> __device__ __forceinline__ void store_act_lds(lds_t *p, size_t i, float v) {
   if constexpr (D == DT_F32) ((__attribute__((address_space(3))) float *)p)[i] = v;
   else ((__attribute__((address_space(3))) uint16_t *)p)[i] = f32_to_bf16(v);
+}
+
+// value of v once stored in dtype D
+template <int D> __device__ __forceinline__ float round_act(float v) {
+  if constexpr (D == DT_F32) return v;
+  else return __uint_as_float((uint32_t)f32_to_bf16(v) << 16);
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
@@ -380,14 +396,22 @@ __device__ __forceinline__ void rows_dot(const char *const (&wrow)[NR], int k0, 
   }
 }
 
-// chunks per step of a gate/up pair (2 rows), sized to the register budget
-template <int WD, int TG> constexpr int seg_gu() {
-  return WD == DT_FP8 ? (TG <= 2 ? 7 : 3) : WD == DT_BF16 ? 7 : 4;
-}
-// chunks per step of a 4-row down unit
-template <int WD, int TG> constexpr int seg_down() { return WD == DT_FP8 ? 1 : WD == DT_BF16 ? 2 : 2; }
+// 16-byte weight loads per lane in flight per step. HBM read bandwidth on
+// MI355X peaks (about 7.1-7.3 TB/s) with only ~28-32 KB in flight per CU and
+// falls with more, while every extra in-flight byte lengthens the queue that
+// the latency-critical loads (barrier polls, router partials) wait in; with
+// 16 waves per CU, two 1 KB wave loads each is the measured optimum.
+#ifndef MOE_LOADS_PER_STEP
+#define MOE_LOADS_PER_STEP 2
+#endif
+constexpr int kLoadsPerStep = MOE_LOADS_PER_STEP;
+// chunks per step of a gate/up pair (2 rows)
+template <int WD, int TG> constexpr int seg_gu() { return kLoadsPerStep >= 4 ? kLoadsPerStep / 2 : 1; }
+// rows of a 4-row down unit handled per pass, and chunks per step
+constexpr int kDownRows = kLoadsPerStep >= 4 ? 4 : kLoadsPerStep >= 2 ? 2 : 1;
+template <int WD, int TG> constexpr int seg_down() { return kLoadsPerStep / kDownRows > 0 ? kLoadsPerStep / kDownRows : 1; }
 // chunks per step of a router row slice
-template <int WD, int TG> constexpr int seg_router() { return TG <= 2 ? 7 : 4; }
+template <int WD, int TG> constexpr int seg_router() { return kLoadsPerStep; }
 
 // Run f.template operator()<TG>(t0, nt) over groups of up to kTokGroup of n
 // tokens, with the smallest specialisation that holds each group.
@@ -407,6 +431,28 @@ __device__ __forceinline__ void for_token_groups(int n, F &&f) {
 __device__ __forceinline__ long long rt_now() { return (long long)__builtin_amdgcn_s_memrealtime(); }
 
 __device__ __forceinline__ unsigned *ctrl_word(KParams p, int w) { return p->ctrl + (size_t)w * kCtrlStride; }
+
+// Small regime: values other workgroups read after a barrier are written
+// with device-coherent stores (write-through past this XCD's L2), so the
+// barrier does not need an L2 write-back, which costs several microseconds
+// per workgroup while the memory system is streaming.
+__device__ __forceinline__ void publish(float *q, float v) {
+  __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A wave is done with the work barrier b waits for, and every value it wrote
+// for other workgroups went out through publish(): waiting for its stores to
+// complete (they are then visible device-wide) replaces the L2 write-back.
+// Readers still acquire at agent scope (L1/L2 invalidate) before reading.
+__device__ void bar_arrive_published(KParams p, SmemHead &sh, int b) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if (lane_id() == 0) {
+    const int old = __hip_atomic_fetch_add(&sh.bar_cnt[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (old == kWaves - 1)
+      __hip_atomic_fetch_add(ctrl_word(p, CTRL_BAR + b), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 
 // A wave is done with the work barrier b waits for.
 __device__ void bar_arrive(KParams p, SmemHead &sh, int b) {
@@ -463,57 +509,103 @@ struct Lds {
 // ---------------------------------------------------------------------------
 // x-hat
 
+// Activation chunk c (16 bytes) of a row; chunks past the row's end read
+// chunk 0 (always in bounds) and are masked by the caller.
+template <int AD> constexpr int act_chunks_max() { return AD == DT_F32 ? 4 : 2; }  // (H <= 16384) / 1024 threads
+
+template <int AD>
+__device__ __forceinline__ void act_chunk_vals(const u32x4 &v, float (&f)[8]) {
+  if constexpr (AD == DT_F32) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y); f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  } else {
+    f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+    f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+  }
+}
+
+// RMSNorm of NT tokens (rows x_t of `x`, t = tok[i]) by the whole workgroup:
+// every load is issued before the first use (one round trip); out(t, h, v)
+// receives x-hat. Chunk c of a row is handled by thread c mod 1024.
+template <int AD, int NT, class Out>
+__device__ __forceinline__ void rmsnorm_rows(KParams p, KLayer lp, SmemHead &sh, const int (&tok)[NT], Out &&out) {
+  constexpr int EPC = 16 / dsz<AD>(), NC = act_chunks_max<AD>();
+  const int H = p->H, tid = threadIdx.x, nch = H / EPC;
+  u32x4 xv[NT][NC], gv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = tid + c * kThreads;
+    const int cc = ch < nch ? ch : 0;
+    gv[c] = *(const u32x4 *)((const char *)lp->gamma + (size_t)cc * 16);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) xv[i][c] = *(const u32x4 *)((const char *)lp->x + ((size_t)tok[i] * nch + cc) * 16);
+  }
+  float ss[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    ss[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (tid + c * kThreads < nch) {
+        float f[8];
+        act_chunk_vals<AD>(xv[i][c], f);
+#pragma unroll
+        for (int q = 0; q < EPC; ++q) ss[i] = fmaf(f[q], f[q], ss[i]);
+      }
+    }
+    ss[i] = readlane_f(wave_sum63(ss[i]), 63);
+    if (lane_id() == 0) sh.red[i * kWaves + wave_id()] = ss[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    float tot = 0.f;
+    for (int w2 = 0; w2 < kWaves; ++w2) tot += sh.red[i * kWaves + w2];
+    const float r = 1.0f / sqrtf(tot / (float)H + p->eps);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int ch = tid + c * kThreads;
+      if (ch < nch) {
+        float f[8], g[8];
+        act_chunk_vals<AD>(xv[i][c], f);
+        act_chunk_vals<AD>(gv[c], g);
+#pragma unroll
+        for (int q = 0; q < EPC; ++q) out(i, ch * EPC + q, f[q] * r * g[q]);
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // Small regime: this workgroup normalises every token into its own LDS:
 // xf [B][H] fp32 (router input) and xa [B][H] act (FFN input).
 template <int AD>
 __device__ __attribute__((noinline)) void stage_xhat(KParams p, KLayer lp, const Lds &L) {
-  const int H = p->H, tid = threadIdx.x;
-  SmemHead &sh = L.head();
+  const int H = p->H;
   float *xf = L.at<float>(p->o_xf);
-  for (int t = 0; t < p->B; ++t) {
-    float ss = 0.f;
-    for (int h = tid; h < H; h += kThreads) {
-      const float v = load_act<AD>(lp->x, (size_t)t * H + h);
-      ss = fmaf(v, v, ss);
-    }
-    ss = readlane_f(wave_sum63(ss), 63);
-    if (lane_id() == 0) sh.red[wave_id()] = ss;
-    __syncthreads();
-    float tot = 0.f;
-    for (int w2 = 0; w2 < kWaves; ++w2) tot += sh.red[w2];
-    const float r = 1.0f / sqrtf(tot / (float)H + p->eps);
-    for (int h = tid; h < H; h += kThreads) {
-      const float xh = load_act<AD>(lp->x, (size_t)t * H + h) * r * load_act<AD>(lp->gamma, h);
-      xf[(size_t)t * H + h] = xh;
-      if constexpr (AD != DT_F32) store_act_lds<AD>(L.raw(p->o_xa), (size_t)t * H + h, xh);
-    }
-    __syncthreads();
+  lds_t *xa = L.raw(p->o_xa);
+  auto put = [&](int t, int h, float v) {
+    xf[(size_t)t * H + h] = v;
+    if constexpr (AD != DT_F32) store_act_lds<AD>(xa, (size_t)t * H + h, v);
+  };
+  if (p->B == 1) {
+    const int tok[1] = {0};
+    rmsnorm_rows<AD, 1>(p, lp, L.head(), tok, put);
+  } else {
+    const int tok[2] = {0, 1};
+    rmsnorm_rows<AD, 2>(p, lp, L.head(), tok, put);
   }
 }
 
 // General regime: workgroup t normalises token t into global memory.
 template <int AD>
 __device__ __attribute__((noinline)) void produce_xhat(KParams p, KLayer lp, const Lds &L) {
-  const int H = p->H, tid = threadIdx.x;
-  SmemHead &sh = L.head();
+  const int H = p->H;
   for (int t = blockIdx.x; t < p->B; t += p->G) {
-    float ss = 0.f;
-    for (int h = tid; h < H; h += kThreads) {
-      const float v = load_act<AD>(lp->x, (size_t)t * H + h);
-      ss = fmaf(v, v, ss);
-    }
-    ss = readlane_f(wave_sum63(ss), 63);
-    if (lane_id() == 0) sh.red[wave_id()] = ss;
-    __syncthreads();
-    float tot = 0.f;
-    for (int w2 = 0; w2 < kWaves; ++w2) tot += sh.red[w2];
-    const float r = 1.0f / sqrtf(tot / (float)H + p->eps);
-    for (int h = tid; h < H; h += kThreads) {
-      const float xh = load_act<AD>(lp->x, (size_t)t * H + h) * r * load_act<AD>(lp->gamma, h);
-      p->xhat[(size_t)t * H + h] = xh;
-      if constexpr (AD != DT_F32) store_act<AD>(p->xa, (size_t)t * H + h, xh);
-    }
-    __syncthreads();
+    const int tok[1] = {t};
+    rmsnorm_rows<AD, 1>(p, lp, L.head(), tok, [&](int, int h, float v) {
+      p->xhat[(size_t)t * H + h] = v;
+      if constexpr (AD != DT_F32) store_act<AD>(p->xa, (size_t)t * H + h, v);
+    });
   }
 }
 
@@ -550,7 +642,11 @@ __device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, 
 #pragma unroll
     for (int t = 0; t < TG; ++t) {
       const float v = wave_sum63(acc[0][t]);
-      if (t < nt && lane_id() == 63) p->rpart[((size_t)s * B + t0 + t) * E + e] = v;
+      if (t < nt && lane_id() == 63) {
+        float *q = p->rpart + ((size_t)(t0 + t) * E + e) * 4 + s;
+        if constexpr (XL) publish(q, v);
+        else *q = v;
+      }
     }
   });
 }
@@ -578,8 +674,8 @@ __device__ __forceinline__ void shared_gu_task(KParams p, KLayer lp, const Lds &
       if (t < nt && lane_id() == 63) {
         if (p->NSS > 1 || XL) {
           float *hp = p->hspart + ((size_t)s * B + t0 + t) * 2 * Is;
-          hp[j] = g;
-          hp[Is + j] = u;
+          publish(hp + j, g);
+          publish(hp + Is + j, u);
         } else {
           store_act<AD>(p->hsbuf, (size_t)(t0 + t) * Is + j, silu_mul(g, u));
         }
@@ -591,30 +687,67 @@ __device__ __forceinline__ void shared_gu_task(KParams p, KLayer lp, const Lds &
 // ---------------------------------------------------------------------------
 // top-k of one token (one wave): softmax over all E logits restricted to the
 // k largest (ties to the lower index), renormalised.
+//
+// Lane l holds the logits of experts l, l+64, ... . The k-th largest of the 64
+// lane maxima, T, is found by a bitwise search with wave ballots; at least k
+// lanes reach T, so every one of the k largest logits is >= T and only the
+// logits >= T (usually a few dozen) are candidates. The candidates are
+// compacted into LDS and each is ranked against all others by (logit desc,
+// index asc); ranks below k are the selection, in order. When more than 64
+// logits tie at the threshold, a 64-round-free fallback runs k rounds of
+// wave argmax instead.
 
-__device__ __attribute__((noinline)) void topk_token(KParams p, KLayer lp, const Lds &L, int t, bool write_out) {
-  const int lane = lane_id();
-  const int E = p->E, k = p->k, B = p->B, NSR = p->NSR;
+// float -> unsigned with the same order (-0 and +0 are made equal first)
+__device__ __forceinline__ unsigned ord_f32(float v) {
+  const unsigned u = __float_as_uint(v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unord_f32(unsigned o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+constexpr int kMaxCand = 64;
+
+// Logits of token t for the experts of this lane (e = lane + 64 j), from the
+// router partials: one 16-byte load per expert holds its K-slice partials,
+// all loads issued before the first use. Slots past E read expert E-1.
+__device__ __forceinline__ void load_logits(KParams p, KLayer lp, int t, float (&v)[kMaxE / 64]) {
+  const int lane = lane_id(), E = p->E, NSR = p->NSR;
   constexpr int PER = kMaxE / 64;
-  const float qnan = __builtin_nanf("");
+  const u32x4 *base = (const u32x4 *)(p->rpart + (size_t)t * E * 4);
+  u32x4 q[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) q[j] = base[min(lane + 64 * j, E - 1)];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    float s = __uint_as_float(q[j].x);
+    if (NSR > 1) s += __uint_as_float(q[j].y);
+    if (NSR > 2) s += __uint_as_float(q[j].z);
+    if (NSR > 3) s += __uint_as_float(q[j].w);
+    v[j] = s;
+  }
+  if (const float *rb = lp->rb) {
+    float b[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) b[j] = rb[min(lane + 64 * j, E - 1)];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[j] += b[j];
+  }
+}
+
+// Rare path (more than 64 logits tie at the threshold): k rounds of wave
+// argmax over all logits. Returns the selection in lanes < k.
+__device__ __attribute__((noinline)) void topk_rounds(KParams p, KLayer lp, int t, float &myv, int &myidx) {
+  const int lane = lane_id(), E = p->E, k = p->k;
+  constexpr int PER = kMaxE / 64;
   float v[PER];
+  load_logits(p, lp, t, v);
+  const float qnan = __builtin_nanf("");
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int e = lane + 64 * j;
-    float l = qnan;  // not an expert: never selected (NaN compares false)
-    if (e < E) {
-      float s = 0.f;
-      for (int q = 0; q < NSR; ++q) s += p->rpart[((size_t)q * B + t) * E + e];
-      if (lp->rb) s += lp->rb[e];
-      l = (s == s) ? s : -INFINITY;  // a NaN logit ranks last but stays selectable
-      if (write_out && lp->logits_out) lp->logits_out[(size_t)t * E + e] = l;
-    }
-    v[j] = l;
+    v[j] = e < E ? ((v[j] == v[j]) ? v[j] : -INFINITY) : qnan;  // NaN never wins
   }
-  int *sel_idx = L.at<int>(p->o_sel_idx);
-  float *sel_w = L.at<float>(p->o_sel_w);
-  float lmax = 0.f, z = 0.f, selv = 0.f;
-  int seli = 0;
   for (int i = 0; i < k; ++i) {
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
@@ -627,18 +760,93 @@ __device__ __attribute__((noinline)) void topk_token(KParams p, KLayer lp, const
 #pragma unroll
     for (int j = 0; j < PER; ++j)
       if (lane + 64 * j == bi) v[j] = qnan;  // taken
-    if (i == 0) lmax = bv;
-    const float ex = expf(bv - lmax);
-    z += ex;
-    if (lane == i) { selv = ex; seli = bi; }
+    if (lane == i) { myv = bv; myidx = bi; }
   }
-  if (lane < k) {
-    const float w = selv / z;
-    sel_idx[t * k + lane] = seli;
-    sel_w[t * k + lane] = w;
+}
+
+__device__ __attribute__((noinline)) void topk_token(KParams p, KLayer lp, const Lds &L, int t, bool write_out) {
+  const int lane = lane_id();
+  const int E = p->E, k = p->k;
+  constexpr int PER = kMaxE / 64;
+  float v[PER];
+  load_logits(p, lp, t, v);
+  unsigned o[PER];
+  unsigned omax = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = lane + 64 * j;
+    // a NaN logit ranks last but stays selectable; a slot past E ranks below every expert
+    if (e < E) v[j] = (v[j] == v[j]) ? v[j] : -INFINITY;
+    if (write_out && lp->logits_out && e < E) lp->logits_out[(size_t)t * E + e] = v[j];
+    o[j] = e < E ? ord_f32(v[j]) : 0u;
+    omax = max(omax, o[j]);
+  }
+  // T = k-th largest lane maximum (largest T with at least k lanes >= T)
+  unsigned thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const unsigned c = thr | (1u << bit);
+    if (__popcll(__ballot(omax >= c)) >= k) thr = c;
+  }
+  int nc = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) nc += (lane + 64 * j < E && o[j] >= thr) ? 1 : 0;
+  // exclusive prefix of the candidate counts over the lanes
+  int incl = nc;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int up = __shfl_up(incl, d);
+    if (lane >= d) incl += up;
+  }
+  const int total = __shfl(incl, 63);
+  int *sel_idx = L.at<int>(p->o_sel_idx);
+  float *sel_w = L.at<float>(p->o_sel_w);
+  int myidx = 0;
+  float myv = -INFINITY;
+  if (total <= kMaxCand) {
+    unsigned *ck = L.head().cand_key[wave_id()];
+    int *ci = L.head().cand_idx[wave_id()];
+    int pos = incl - nc;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E && o[j] >= thr) { ck[pos] = o[j]; ci[pos] = e; ++pos; }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    if (lane < total) {
+      const unsigned mk = ck[lane];
+      const int me = ci[lane];
+      int rank = 0;
+      for (int c = 0; c < total; ++c) {
+        const unsigned ok = ck[c];
+        const int oe = ci[c];
+        rank += (ok > mk || (ok == mk && oe < me)) ? 1 : 0;
+      }
+      if (rank < k) {
+        ck[kMaxCand + rank] = mk;
+        ci[kMaxCand + rank] = me;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    if (lane < k) {
+      myv = unord_f32(ck[kMaxCand + lane]);
+      myidx = ci[kMaxCand + lane];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  } else {
+    topk_rounds(p, lp, t, myv, myidx);
+  }
+  // renormalised softmax over the selection (the denominator over all E cancels)
+  const bool mine = lane < k;
+  const float lmax = readlane_f(myv, 0);
+  const float ex = mine ? expf(myv - lmax) : 0.f;
+  const float z = readlane_f(wave_sum63(ex), 63);
+  if (mine) {
+    const float wgt = ex / z;
+    sel_idx[t * k + lane] = myidx;
+    sel_w[t * k + lane] = wgt;
     if (write_out) {
-      if (lp->idx_out) lp->idx_out[(size_t)t * k + lane] = seli;
-      if (lp->w_out) lp->w_out[(size_t)t * k + lane] = w;
+      if (lp->idx_out) lp->idx_out[(size_t)t * k + lane] = myidx;
+      if (lp->w_out) lp->w_out[(size_t)t * k + lane] = wgt;
     }
   }
 }
@@ -650,6 +858,7 @@ __device__ __attribute__((noinline)) void build_tables(KParams p, const Lds &L) 
   const int E = p->E, P = p->B * p->k;
   SmemHead &sh = L.head();
   int *cnt = L.at<int>(p->o_cnt), *start = L.at<int>(p->o_start), *ulist = L.at<int>(p->o_ulist);
+  int *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   int *plist = L.at<int>(p->o_plist);
   const int *sel_idx = L.at<int>(p->o_sel_idx);
   unsigned long long *tmask = L.at<unsigned long long>(p->o_tmask);
@@ -690,7 +899,44 @@ __device__ __attribute__((noinline)) void build_tables(KParams p, const Lds &L) 
     const unsigned long long below = (t == 0) ? 0ull : (tmask[e] & ((1ull << t) - 1ull));
     plist[start[e] + __popcll(below)] = q;
   }
+  for (int u = tid; u < sh.nU; u += kThreads) {
+    ucnt[u] = cnt[ulist[u]];
+    ustart[u] = start[ulist[u]];
+  }
   __syncthreads();
+}
+
+// The same tables built by one wave when B*k <= 64: the (expert, pair) keys
+// are sorted across the lanes (bitonic), then each run of equal experts is a
+// union slot. Pairs of one expert keep ascending order, hence ascending tokens.
+__device__ __attribute__((noinline)) void build_tables_wave(KParams p, const Lds &L) {
+  const int lane = lane_id(), P = p->B * p->k;
+  const int *sel_idx = L.at<int>(p->o_sel_idx);
+  int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
+  int *plist = L.at<int>(p->o_plist);
+  unsigned key = lane < P ? ((unsigned)sel_idx[lane] << 6) | (unsigned)lane : 0xFFFFFFFFu;
+#pragma unroll
+  for (int kk = 2; kk <= 64; kk <<= 1)
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      const unsigned o = (unsigned)__shfl_xor((int)key, j);
+      const bool asc = (lane & kk) == 0, low = (lane & j) == 0;
+      key = (asc == low) ? min(key, o) : max(key, o);
+    }
+  const bool valid = lane < P;
+  const unsigned prev = (unsigned)__shfl_up((int)key, 1);
+  const bool first = valid && (lane == 0 || (prev >> 6) != (key >> 6));
+  const unsigned long long firsts = __ballot(first);
+  if (valid) plist[lane] = (int)(key & 63u);
+  if (first) {
+    const int rank = __popcll(firsts & ((1ull << lane) - 1ull));
+    const unsigned long long rest = lane < 63 ? firsts >> (lane + 1) : 0ull;
+    const int nxt = rest ? lane + __ffsll((long long)rest) : P;
+    ulist[rank] = (int)(key >> 6);
+    ustart[rank] = lane;
+    ucnt[rank] = nxt - lane;
+  }
+  if (lane == 0) L.head().nU = __popcll(firsts);
 }
 
 // ---------------------------------------------------------------------------
@@ -699,11 +945,11 @@ __device__ __attribute__((noinline)) void build_tables(KParams p, const Lds &L) 
 template <int AD, int ED, bool XL>
 __device__ __forceinline__ void expert_gu_task(KParams p, KLayer lp, const Lds &L, int u, int j) {
   const int H = p->H, I = p->I, k = p->k;
-  const int *cnt = L.at<int>(p->o_cnt), *start = L.at<int>(p->o_start), *ulist = L.at<int>(p->o_ulist);
+  const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   const int *plist = L.at<int>(p->o_plist);
   const int e = ulist[u];
-  const int n = cnt[e];
-  const int *pl = plist + start[e];
+  const int n = ucnt[u];
+  const int *pl = plist + ustart[u];
   const size_t rowb = (size_t)H * dsz<ED>();
   const char *gu = (const char *)lp->egu + (size_t)e * 2 * I * rowb;
   const char *const wrow[2] = {gu + (size_t)j * rowb, gu + (size_t)(I + j) * rowb};
@@ -730,7 +976,12 @@ __device__ __forceinline__ void expert_gu_task(KParams p, KLayer lp, const Lds &
     for (int t = 0; t < TG; ++t) {
       const float g = wave_sum63(acc[0][t]) * gs;
       const float uu = wave_sum63(acc[1][t]) * us;
-      if (t < nt && lane_id() == 63) store_act<AD>(p->hbuf, (size_t)slot[t] * I + j, silu_mul(g, uu));
+      if (t < nt && lane_id() == 63) {
+        const float h = silu_mul(g, uu);
+        // small regime: fp32 copy of the act-rounded h, published; otherwise h in the act dtype
+        if constexpr (XL) publish((float *)p->hbuf + (size_t)slot[t] * I + j, round_act<AD>(h));
+        else store_act<AD>(p->hbuf, (size_t)slot[t] * I + j, h);
+      }
     }
   });
 }
@@ -738,29 +989,80 @@ __device__ __forceinline__ void expert_gu_task(KParams p, KLayer lp, const Lds &
 // ---------------------------------------------------------------------------
 // P2: down projections of this workgroup's rows
 
-// shared h for every token from the slice partials, into LDS (small regime)
+// Small regime, one wave: the shared expert's h for every token from the
+// slice partials, into LDS. Lane l covers 4 consecutive columns per step; all
+// partial loads of a step are issued before the first use.
 template <int AD>
-__device__ __attribute__((noinline)) void finish_shared_h(KParams p, const Lds &L) {
-  const int Is = p->Is, B = p->B, NSS = p->NSS;
+__device__ __attribute__((noinline)) void finish_shared_h_wave(KParams p, const Lds &L) {
+  const int Is = p->Is, B = p->B, NSS = p->NSS, lane = lane_id();
   lds_t *hs = L.raw(p->o_hs);
-  for (int c = threadIdx.x; c < B * Is; c += kThreads) {
-    const int t = c / Is, j = c % Is;
-    float g = 0.f, u = 0.f;
-    for (int s = 0; s < NSS; ++s) {
-      const float *hp = p->hspart + ((size_t)s * B + t) * 2 * Is;
-      g += hp[j];
-      u += hp[Is + j];
+  constexpr int U = 2;  // 16-byte groups per lane per step
+  for (int t = 0; t < B; ++t) {
+    for (int j0 = 0; j0 < Is; j0 += 64 * 4 * U) {
+      u32x4 g[U][2], u[U][2];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int j = min(j0 + (q * 64 + lane) * 4, Is - 4);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const float *hp = p->hspart + ((size_t)min(s2, NSS - 1) * B + t) * 2 * Is;
+          g[q][s2] = *(const u32x4 *)(hp + j);
+          u[q][s2] = *(const u32x4 *)(hp + Is + j);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int j = j0 + (q * 64 + lane) * 4;
+        if (j < Is) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            float gg = __uint_as_float(g[q][0][c]), uu = __uint_as_float(u[q][0][c]);
+            if (NSS > 1) { gg += __uint_as_float(g[q][1][c]); uu += __uint_as_float(u[q][1][c]); }
+            store_act_lds<AD>(hs, (size_t)t * Is + j + c, silu_mul(gg, uu));
+          }
+        }
+      }
     }
-    store_act_lds<AD>(hs, (size_t)t * Is + j, silu_mul(g, u));
   }
 }
 
-// expert h of every selected (token, expert) pair into LDS (small regime)
-__device__ __attribute__((noinline)) void stage_h(KParams p, const Lds &L, int act_bytes) {
-  const size_t n16 = (size_t)p->B * p->k * p->I * act_bytes / 16;
+// Small regime: the expert h of every selected (token, expert) pair, from the
+// published fp32 copy into LDS in the act dtype (values are already rounded).
+// Every load is issued before the first use.
+template <int AD>
+__device__ __attribute__((noinline)) void stage_h(KParams p, const Lds &L) {
+  const int n4 = p->B * p->k * p->I / 4;  // groups of 4 values
+  constexpr int U = 8;                     // covers B*k*I <= 32768 values in one round
   const u32x4 *src = (const u32x4 *)p->hbuf;
-  __attribute__((address_space(3))) u32x4 *dst = (__attribute__((address_space(3))) u32x4 *)L.raw(p->o_h);
-  for (size_t i = threadIdx.x; i < n16; i += kThreads) dst[i] = src[i];
+  u32x4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = threadIdx.x + u * kThreads;
+    v[u] = src[i < n4 ? i : 0];
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = threadIdx.x + u * kThreads;
+    if (i < n4) {
+      if constexpr (AD == DT_F32) {
+        *(__attribute__((address_space(3))) u32x4 *)(L.raw(p->o_h) + (size_t)i * 16) = v[u];
+      } else {
+        // the values are bf16-exact: their top halves are the bf16 patterns
+        const uint32_t lo = (v[u].x >> 16) | (v[u].y & 0xFFFF0000u);
+        const uint32_t hi = (v[u].z >> 16) | (v[u].w & 0xFFFF0000u);
+        *(__attribute__((address_space(3))) u32x2 *)(L.raw(p->o_h) + (size_t)i * 8) = u32x2{lo, hi};
+      }
+    }
+  }
+  for (int i = threadIdx.x + U * kThreads; i < n4; i += kThreads) {  // larger shapes: rest, one by one
+    const u32x4 w = src[i];
+    if constexpr (AD == DT_F32) {
+      *(__attribute__((address_space(3))) u32x4 *)(L.raw(p->o_h) + (size_t)i * 16) = w;
+    } else {
+      *(__attribute__((address_space(3))) u32x2 *)(L.raw(p->o_h) + (size_t)i * 8) =
+          u32x2{(w.x >> 16) | (w.y & 0xFFFF0000u), (w.z >> 16) | (w.w & 0xFFFF0000u)};
+    }
+  }
 }
 
 // One 4-row unit of a [rows][K] down matrix: row pointers wrow, columns
@@ -770,67 +1072,92 @@ template <int WD, int AD, bool XL, int TG>
 __device__ __forceinline__ void down_unit(const char *const (&wrow)[kRowBlock], int I,
                                           const typename XSrc<XL>::ptr (&xr)[TG], const float (&sc)[kRowBlock],
                                           float *prow, int pstride, const int (&col)[TG], int nt) {
-  float acc[kRowBlock][TG];
 #pragma unroll
-  for (int r = 0; r < kRowBlock; ++r)
+  for (int r0 = 0; r0 < kRowBlock; r0 += kDownRows) {
+    const char *wr[kDownRows];
+    float acc[kDownRows][TG];
 #pragma unroll
-    for (int t = 0; t < TG; ++t) acc[r][t] = 0.f;
-  rows_dot<WD, AD, XL, kRowBlock, seg_down<WD, TG>(), TG>(wrow, 0, I, xr, acc);
+    for (int r = 0; r < kDownRows; ++r) {
+      wr[r] = wrow[r0 + r];
 #pragma unroll
-  for (int r = 0; r < kRowBlock; ++r)
-#pragma unroll
-    for (int t = 0; t < TG; ++t) {
-      const float v = wave_sum63(acc[r][t]) * sc[r];
-      if (t < nt && lane_id() == 63) prow[r * pstride + col[t]] = v;
+      for (int t = 0; t < TG; ++t) acc[r][t] = 0.f;
     }
+    rows_dot<WD, AD, XL, kDownRows, seg_down<WD, TG>(), TG>(wr, 0, I, xr, acc);
+#pragma unroll
+    for (int r = 0; r < kDownRows; ++r)
+#pragma unroll
+      for (int t = 0; t < TG; ++t) {
+        const float v = wave_sum63(acc[r][t]) * sc[r0 + r];
+        if (t < nt && lane_id() == 63) prow[(r0 + r) * pstride + col[t]] = v;
+      }
+  }
 }
 
-// shared-expert units of rows [pr0, pr1): (row block, column block hf)
-template <int AD, int SD, bool XL>
+// Next P2 unit of this wave: handed out through an LDS counter (DYN, small
+// regime) or dealt round-robin from wave w0.
+template <bool DYN>
+__device__ __forceinline__ int next_unit(SmemHead &sh, int which, int &cur, int w0) {
+  if constexpr (DYN) {
+    int u = 0;
+    if (lane_id() == 0) u = __hip_atomic_fetch_add(&sh.unit_ctr[which], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(u);
+  } else {
+    cur = (cur < 0) ? (wave_id() + kWaves - w0 % kWaves) % kWaves : cur + kWaves;
+    return cur;
+  }
+}
+
+// shared-expert units of rows [pr0, pr1): (row block, column block hf); the
+// shared h comes from LDS (small regime) or global memory
+template <int AD, int SD, bool SMALL>
 __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, int w0) {
   const int I = p->I, Is = p->Is, B = p->B;
   const int nsh = Is / I, P = B * p->k, pstride = P + B * nsh;
   const int nrb = (pr1 - pr0) / kRowBlock;
   float *part = L.at<float>(p->o_part);
   const float one[kRowBlock] = {1.f, 1.f, 1.f, 1.f};
-  for (int un = (wave_id() + kWaves - w0 % kWaves) % kWaves; un < nrb * nsh; un += kWaves) {
-    const int rb = un / nsh, hf = un % nsh;
+  int cur = -1;
+  for (int un = next_unit<SMALL>(L.head(), 0, cur, w0); un < nrb * nsh; un = next_unit<SMALL>(L.head(), 0, cur, w0)) {
+    const int hf = un / nrb, rb = un % nrb;
     const int o0 = pr0 + rb * kRowBlock;
     const char *wrow[kRowBlock];
 #pragma unroll
     for (int r = 0; r < kRowBlock; ++r)
       wrow[r] = (const char *)lp->sd + ((size_t)(o0 + r) * Is + (size_t)hf * I) * dsz<SD>();
     for_token_groups(B, [&]<int TG>(int t0, int nt) {
-      typename XSrc<XL>::ptr xr[TG];
+      typename XSrc<SMALL>::ptr xr[TG];
       int col[TG];
 #pragma unroll
       for (int t = 0; t < TG; ++t) {
         const int tt = t0 + (t < nt ? t : 0);
-        if constexpr (XL) xr[t] = L.raw(p->o_hs) + ((size_t)tt * Is + (size_t)hf * I) * dsz<AD>();
+        if constexpr (SMALL) xr[t] = L.raw(p->o_hs) + ((size_t)tt * Is + (size_t)hf * I) * dsz<AD>();
         else xr[t] = (const char *)p->hsbuf + ((size_t)tt * Is + (size_t)hf * I) * dsz<AD>();
         col[t] = P + (t0 + t) * nsh + hf;
       }
-      down_unit<SD, AD, XL, TG>(wrow, I, xr, one, part + (size_t)(o0 - pr0) * pstride, pstride, col, nt);
+      down_unit<SD, AD, SMALL, TG>(wrow, I, xr, one, part + (size_t)(o0 - pr0) * pstride, pstride, col, nt);
     });
   }
 }
 
-// routed-expert units of rows [pr0, pr1): (row block, expert slot)
-template <int AD, int ED, bool XL>
+// routed-expert units of rows [pr0, pr1): (expert slot, row block), expert-major
+// so a wave's consecutive units read consecutive rows; h from LDS (small
+// regime) or global memory
+template <int AD, int ED, bool SMALL>
 __device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, int w0) {
   const int H = p->H, I = p->I, B = p->B;
   const int nsh = p->Is / I, P = B * p->k, pstride = P + B * nsh;
   const int nU = L.head().nU;
   const int nrb = (pr1 - pr0) / kRowBlock;
-  const int *cnt = L.at<int>(p->o_cnt), *start = L.at<int>(p->o_start), *ulist = L.at<int>(p->o_ulist);
+  const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   const int *plist = L.at<int>(p->o_plist);
   float *part = L.at<float>(p->o_part);
-  for (int un = (wave_id() + kWaves - w0 % kWaves) % kWaves; un < nrb * nU; un += kWaves) {
-    const int rb = un / nU, s = un % nU;
+  int cur = -1;
+  for (int un = next_unit<SMALL>(L.head(), 1, cur, w0); un < nrb * nU; un = next_unit<SMALL>(L.head(), 1, cur, w0)) {
+    const int s = un / nrb, rb = un % nrb;
     const int o0 = pr0 + rb * kRowBlock;
     const int e = ulist[s];
-    const int n = cnt[e];
-    const int *pl = plist + start[e];
+    const int n = ucnt[s];
+    const int *pl = plist + ustart[s];
     const char *wrow[kRowBlock];
     float sc[kRowBlock];
 #pragma unroll
@@ -840,15 +1167,15 @@ __device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Ld
       if constexpr (ED == DT_FP8) sc[r] = __uint_as_float((uint32_t)lp->eds[(size_t)e * (H / 128) + (o0 + r) / 128] << 16);
     }
     for_token_groups(n, [&]<int TG>(int t0, int nt) {
-      typename XSrc<XL>::ptr xr[TG];
+      typename XSrc<SMALL>::ptr xr[TG];
       int col[TG];
 #pragma unroll
       for (int t = 0; t < TG; ++t) {
         col[t] = pl[t0 + (t < nt ? t : 0)];
-        if constexpr (XL) xr[t] = L.raw(p->o_h) + (size_t)col[t] * I * dsz<AD>();
+        if constexpr (SMALL) xr[t] = L.raw(p->o_h) + (size_t)col[t] * I * dsz<AD>();
         else xr[t] = (const char *)p->hbuf + (size_t)col[t] * I * dsz<AD>();
       }
-      down_unit<ED, AD, XL, TG>(wrow, I, xr, sc, part + (size_t)(o0 - pr0) * pstride, pstride, col, nt);
+      down_unit<ED, AD, SMALL, TG>(wrow, I, xr, sc, part + (size_t)(o0 - pr0) * pstride, pstride, col, nt);
     });
   }
 }
@@ -908,6 +1235,52 @@ __device__ __forceinline__ unsigned prefetch_p0(KParams p, KLayer nl, int W, int
 // ---------------------------------------------------------------------------
 // the kernel
 
+// Small regime: the first wave of the workgroup to get here (it has no P0
+// work left) waits for the router barrier, routes every token and builds the
+// gather tables; the other waves keep streaming their P0 rows meanwhile and
+// pick the tables up from LDS when they are done.
+template <bool FIRST_WAVE_ROUTES>
+__device__ __forceinline__ void route_small(KParams p, KLayer lp, const Lds &L, int b_router) {
+  SmemHead &sh = L.head();
+  int claimed = 0;
+  if (lane_id() == 0)
+    claimed = __hip_atomic_exchange(&sh.route_claim, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
+  claimed = __builtin_amdgcn_readfirstlane(claimed);
+  if (claimed) {
+    bar_wait(p, sh, b_router);
+    for (int t = 0; t < p->B; ++t) topk_token(p, lp, L, t, blockIdx.x == 0);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    build_tables_wave(p, L);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane_id() == 0) __hip_atomic_store(&sh.route_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else if (lane_id() == 0) {
+    while (__hip_atomic_load(&sh.route_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+      __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Small regime: the first wave done with P1 waits for the shared barrier and
+// finishes the shared expert's h in LDS; the others wait for it.
+template <int AD>
+__device__ __forceinline__ void shared_h_small(KParams p, const Lds &L, int b_shared) {
+  SmemHead &sh = L.head();
+  int claimed = 0;
+  if (lane_id() == 0)
+    claimed = __hip_atomic_exchange(&sh.shared_claim, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
+  claimed = __builtin_amdgcn_readfirstlane(claimed);
+  if (claimed) {
+    bar_wait(p, sh, b_shared);
+    finish_shared_h_wave<AD>(p, L);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane_id() == 0) __hip_atomic_store(&sh.shared_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else if (lane_id() == 0) {
+    while (__hip_atomic_load(&sh.shared_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+      __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 template <int AD, int RD, int ED, int SD, bool SMALL>
 __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
   // read the parameters in place in the kernarg segment (scalar loads; no private copy)
@@ -922,12 +1295,16 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
 
   for (int i = tid; i < kMaxBarriers; i += kThreads) sh.bar_cnt[i] = sh.bar_claim[i] = sh.bar_flag[i] = 0;
   if (tid == 0) sh.sink = 0;
-  __syncthreads();
 
   unsigned sink = 0;
   for (int l = 0; l < p->L; ++l) {
     KLayer lp = &p->lp[l];
     const int b0 = kBarPerLayer * l;
+    if (tid == 0) {
+      sh.route_claim = sh.route_ready = sh.shared_claim = sh.shared_ready = 0;
+      sh.unit_ctr[0] = sh.unit_ctr[1] = 0;
+    }
+    __syncthreads();
 
     // x-hat
     if constexpr (SMALL) {
@@ -942,53 +1319,62 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
     const int nrt = p->E * p->NSR;
     int tau = W;
     for (; tau < nrt; tau += NW) router_task<RD, SMALL>(p, lp, L, tau / p->NSR, tau % p->NSR);
-    bar_arrive(p, sh, b0 + BAR_ROUTER);
-    if (!p->route_only) {
-      for (; tau < nrt + p->Is * p->NSS; tau += NW)
-        shared_gu_task<AD, SD, SMALL>(p, lp, L, (tau - nrt) / p->NSS, (tau - nrt) % p->NSS);
-      bar_arrive(p, sh, b0 + BAR_SHARED);
-    }
-    bar_wait(p, sh, b0 + BAR_ROUTER);
-
+    if constexpr (SMALL) bar_arrive_published(p, sh, b0 + BAR_ROUTER);
+    else bar_arrive(p, sh, b0 + BAR_ROUTER);
     if (p->route_only) {
+      bar_wait(p, sh, b0 + BAR_ROUTER);
       if (blockIdx.x == 0)
         for (int t = wv; t < p->B; t += kWaves) topk_token(p, lp, L, t, true);
       break;
     }
+    for (; tau < nrt + p->Is * p->NSS; tau += NW)
+      shared_gu_task<AD, SD, SMALL>(p, lp, L, (tau - nrt) / p->NSS, (tau - nrt) % p->NSS);
+    if constexpr (SMALL) bar_arrive_published(p, sh, b0 + BAR_SHARED);
+    else bar_arrive(p, sh, b0 + BAR_SHARED);
 
     // P1: routing, gather tables, expert gate/up
-    for (int t = wv; t < p->B; t += kWaves) topk_token(p, lp, L, t, blockIdx.x == 0);
-    __syncthreads();
-    build_tables(p, L);
+    if constexpr (SMALL) {
+      route_small<true>(p, lp, L, b0 + BAR_ROUTER);
+    } else {
+      bar_wait(p, sh, b0 + BAR_ROUTER);
+      for (int t = wv; t < p->B; t += kWaves) topk_token(p, lp, L, t, blockIdx.x == 0);
+      __syncthreads();
+      build_tables(p, L);
+    }
     const int ntask = sh.nU * p->I;
     for (int q = W; q < ntask; q += NW) expert_gu_task<AD, ED, SMALL>(p, lp, L, q / p->I, q % p->I);
-    bar_arrive(p, sh, b0 + BAR_H);
+    if constexpr (SMALL) bar_arrive_published(p, sh, b0 + BAR_H);
+    else bar_arrive(p, sh, b0 + BAR_H);
 
-    // P2: this workgroup's output rows
+    // P2: this workgroup's output rows; the shared expert's rows first (their
+    // input is complete since P0), which fills the wait for the expert barrier
     const int r0 = blockIdx.x * p->rows_per_wg;
     const int r1 = min(p->H, r0 + p->rows_per_wg);
-    const bool one_pass = p->pass_rows >= p->rows_per_wg;
-    const int nsh = p->Is / p->I;
-    bar_wait(p, sh, b0 + BAR_SHARED);
     if constexpr (SMALL) {
-      __syncthreads();  // x-hat in LDS is dead; its space now holds shared h and the partials
-      finish_shared_h<AD>(p, L);
+      shared_h_small<AD>(p, L, b0 + BAR_SHARED);
+      if (r0 < r1) shared_down_units<AD, SD, true>(p, lp, L, r0, r1, 0);
+      bar_wait(p, sh, b0 + BAR_H);
+      stage_h<AD>(p, L);
       __syncthreads();
-    }
-    if (one_pass && r0 < r1) shared_down_units<AD, SD, SMALL>(p, lp, L, r0, r1, 0);
-    bar_wait(p, sh, b0 + BAR_H);
-    if constexpr (SMALL) {
-      stage_h(p, L, dsz<AD>());
+      if (r0 < r1) expert_down_units<AD, ED, true>(p, lp, L, r0, r1, 0);
       __syncthreads();
-    }
-    for (int pr0 = r0; pr0 < r1; pr0 += p->pass_rows) {
-      const int pr1 = min(r1, pr0 + p->pass_rows);
-      const int nrb = (pr1 - pr0) / kRowBlock;
-      if (!one_pass) shared_down_units<AD, SD, SMALL>(p, lp, L, pr0, pr1, 0);
-      expert_down_units<AD, ED, SMALL>(p, lp, L, pr0, pr1, one_pass ? 0 : nrb * nsh);
+      if (r0 < r1) combine<AD>(p, lp, L, r0, r1);
       __syncthreads();
-      combine<AD>(p, lp, L, pr0, pr1);
-      __syncthreads();
+    } else {
+      const bool one_pass = p->pass_rows >= p->rows_per_wg;
+      const int nsh = p->Is / p->I;
+      bar_wait(p, sh, b0 + BAR_SHARED);
+      if (one_pass && r0 < r1) shared_down_units<AD, SD, false>(p, lp, L, r0, r1, 0);
+      bar_wait(p, sh, b0 + BAR_H);
+      for (int pr0 = r0; pr0 < r1; pr0 += p->pass_rows) {
+        const int pr1 = min(r1, pr0 + p->pass_rows);
+        const int nrb = (pr1 - pr0) / kRowBlock;
+        if (!one_pass) shared_down_units<AD, SD, false>(p, lp, L, pr0, pr1, 0);
+        expert_down_units<AD, ED, false>(p, lp, L, pr0, pr1, one_pass ? 0 : nrb * nsh);
+        __syncthreads();
+        combine<AD>(p, lp, L, pr0, pr1);
+        __syncthreads();
+      }
     }
 
     if (l + 1 < p->L) {
@@ -1099,9 +1485,9 @@ WsLayout ws_layout(const moe_layer_desc *d, int B, int L) {
   const size_t is = (size_t)(d->shared_inter > 0 ? d->shared_inter : 1);
   w.xhat = off; off += up256((size_t)B * d->hidden * 4);
   w.xa = off; off += up256((size_t)B * d->hidden * act);
-  w.rpart = off; off += up256((size_t)4 * B * d->num_experts * 4);
+  w.rpart = off; off += up256((size_t)B * d->num_experts * 4 * 4);
   w.hspart = off; off += up256((size_t)2 * B * 2 * is * 4);
-  w.hbuf = off; off += up256((size_t)B * d->top_k * d->expert_inter * act);
+  w.hbuf = off; off += up256((size_t)B * d->top_k * d->expert_inter * 4);  // fp32 in the small regime
   w.hsbuf = off; off += up256((size_t)B * is * act);
   w.xbuf0 = off; off += (L > 1) ? up256((size_t)B * d->hidden * act) : 0;
   w.xbuf1 = off; off += (L > 2) ? up256((size_t)B * d->hidden * act) : 0;
@@ -1188,42 +1574,44 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   // LDS carve-up
   const int E = d->num_experts, P = B * d->top_k, H = d->hidden;
   const int nsh = d->shared_inter > 0 ? d->shared_inter / d->expert_inter : 0;
+  const int nslot = P < E ? P : E;
   const size_t act = (size_t)dsize(d->act);
   size_t o = align16(sizeof(SmemHead));
   p.o_sel_idx = (int)o; o = align16(o + (size_t)P * 4);
   p.o_sel_w = (int)o; o = align16(o + (size_t)P * 4);
-  p.o_cnt = (int)o; o = align16(o + (size_t)E * 4);
-  p.o_start = (int)o; o = align16(o + (size_t)E * 4);
-  p.o_tmask = (int)o; o = align16(o + (size_t)E * 8);
-  p.o_ulist = (int)o; o = align16(o + (size_t)E * 4);
+  p.o_ulist = (int)o; o = align16(o + (size_t)nslot * 4);
+  p.o_ucnt = (int)o; o = align16(o + (size_t)nslot * 4);
+  p.o_ustart = (int)o; o = align16(o + (size_t)nslot * 4);
   p.o_plist = (int)o; o = align16(o + (size_t)P * 4);
-  const size_t region = o;
-  size_t need_a = 0, p2_fixed = 0;
   if (small) {
-    p.o_xf = (int)region;
-    size_t a = align16(region + (size_t)B * H * 4);
-    p.o_xa = (int)a;
-    need_a = (d->act == MOE_F32) ? a : align16(a + (size_t)B * H * act);
-    p.o_hs = (int)region;
-    size_t b = align16(region + (size_t)B * (d->shared_inter > 0 ? d->shared_inter : 1) * act);
-    p.o_h = (int)b;
-    b = align16(b + (size_t)P * d->expert_inter * act);
-    p2_fixed = b;
+    if (P > 64) return fail(MOE_ERR_UNSUPPORTED, "small-batch routing needs batch*top_k <= 64");
+    p.o_xf = (int)o; o = align16(o + (size_t)B * H * 4);
+    p.o_xa = (int)o; o = align16(o + (d->act == MOE_F32 ? 0 : (size_t)B * H * act));
+    p.o_hs = (int)o; o = align16(o + (size_t)B * (d->shared_inter > 0 ? d->shared_inter : 1) * act);
+    // expert h lands over x-hat once every P1 task is done (after the expert
+    // barrier), or after the other regions when it is the larger of the two
+    const size_t hbytes = (size_t)P * d->expert_inter * act;
+    if ((size_t)p.o_xf + hbytes <= (size_t)p.o_hs) {
+      p.o_h = p.o_xf;
+    } else {
+      p.o_h = (int)o; o = align16(o + hbytes);
+    }
   } else {
-    p2_fixed = region;
+    p.o_cnt = (int)o; o = align16(o + (size_t)E * 4);
+    p.o_start = (int)o; o = align16(o + (size_t)E * 4);
+    p.o_tmask = (int)o; o = align16(o + (size_t)E * 8);
   }
-  p.o_part = (int)p2_fixed;
+  p.o_part = (int)o;
   const size_t per_row = (size_t)(P + B * nsh) * sizeof(float);
   const size_t lds_cap = (size_t)(di.max_lds > 0 ? di.max_lds : 65536);
-  if (need_a > lds_cap || p2_fixed + (size_t)kRowBlock * per_row > lds_cap)
+  if (o + (size_t)kRowBlock * per_row > lds_cap)
     return fail(MOE_ERR_UNSUPPORTED, "shape needs more LDS than the device's %zu bytes", lds_cap);
-  int pr = (int)((lds_cap - p2_fixed) / per_row);
+  int pr = (int)((lds_cap - o) / per_row);
   pr = pr / kRowBlock * kRowBlock;
   p.pass_rows = pr < rpw ? pr : rpw;
   if (small && p.pass_rows < rpw)
     return fail(MOE_ERR_UNSUPPORTED, "small-batch layout needs one LDS pass over %d rows", rpw);
-  size_t lds = p2_fixed + (size_t)p.pass_rows * per_row;
-  if (need_a > lds) lds = need_a;
+  const size_t lds = o + (size_t)p.pass_rows * per_row;
 
   p.timeout_ticks = 200000000LL;  // 2 s at 100 MHz
   // test hook: a tiny limit makes every barrier wait give up at once (no hang, no fault)
