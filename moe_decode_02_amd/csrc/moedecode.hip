@@ -73,8 +73,13 @@ constexpr int kMaxL = 8;
 constexpr int kTokGroup = 4;    // tokens whose partial sums a lane holds at once
 constexpr int kRowBlock = 4;    // down-projection rows per unit
 constexpr int kSmallB = 2;      // B <= kSmallB: x-hat and h staged in each workgroup's LDS
+constexpr int kMaxRounds = 32;  // rounds of P0 slices over the grid's waves
 
-enum : int { BAR_XHAT = 0, BAR_ROUTER = 1, BAR_SHARED = 2, BAR_H = 3, BAR_LAYER = 4, kBarPerLayer = 5 };
+// expert barriers of the small regime: P1's rounds fall into up to kP1Groups
+// groups, each with a barrier, so the down projections of the experts done in
+// early groups run while later groups are still being computed
+constexpr int kP1Groups = 4;
+enum : int { BAR_XHAT = 0, BAR_ROUTER = 1, BAR_SHARED = 2, BAR_LAYER = 3, BAR_H = 4, kBarPerLayer = 4 + kP1Groups };
 constexpr int kMaxBarriers = kBarPerLayer * kMaxL;
 constexpr int kCtrlStride = 16;  // words: each control word on its own 64-byte line
 enum : int { CTRL_DONE = 0, CTRL_ERR = 1, CTRL_BAR = 2 };
@@ -100,8 +105,12 @@ struct LayerPtrs {
 struct Params {
   int H, E, k, I, Is, B, L;
   int route_only;
+  int use_mfma;           // general regime: experts with >= kMfmaMin tokens go through MFMA tiles
   int NSR;                // router K-slices
   int NSS;                // shared gate/up K-slices (small regime), else 1
+  int s0;                 // first P0 task index of the shared slices (a multiple of the wave count of a workgroup)
+  int slw;                // floats per wave and round in the LDS slice slots (B, or 2B with shared slices)
+  int p0r, p0w;           // P0 rounds; waves per workgroup that take a task in the last round
   int G;                  // workgroups
   int rows_per_wg;        // P2 output rows per workgroup (multiple of kRowBlock)
   int pass_rows;          // P2 rows per LDS pass
@@ -110,19 +119,21 @@ struct Params {
   unsigned *ctrl;         // control words, kCtrlStride apart
   float *xhat;            // [B][H] fp32 (general regime)
   void *xa;               // [B][H] act (general regime; == xhat for fp32 activations)
-  float *rpart;           // [B][E][4]: slice s of expert e's logit at [t][e][s] (s < NSR)
-  float *hspart;          // [NSS][B][2 Is] (small regime)
+  float *rfin;            // [B][E]: the logits (slices summed in order by the last slice's wave)
+  float *hsh32;           // [B][Is]: the shared h, act-rounded, as fp32 (small regime)
   void *hbuf;             // [B*k][I] act
-  void *hsbuf;            // [B][Is] act (general regime)
+  void *hsbuf;             // [B][Is] act (general regime)
+  float *partbuf;          // [H][pstride] P2 partial sums (general regime)
   void *xbuf[2];          // [B][H] act, stack intermediates
   // LDS carve-up, byte offsets from the start of dynamic LDS
   int o_sel_idx, o_sel_w;           // routing of each token [B*k]
   int o_ulist, o_ucnt, o_ustart;    // gather tables per union slot [min(E, B*k)]
   int o_plist;                      // (token, rank) pairs grouped by expert [B*k]
   int o_cnt, o_start, o_tmask;      // per-expert scratch of the workgroup-wide table build [E]
+  int o_mslot, o_gslot;             // general regime: union slots on MFMA tiles / on GEMV [min(E, B*k)]
   int o_xf, o_xa;                   // small regime: x-hat fp32 / act [B][H]
   int o_hs;                         // small regime: shared h [B][Is] (act)
-  int o_h;                          // small regime: expert h [B*k][I] (act), over x-hat once P1 is done
+  int o_slc;                        // slice sums of P0 tasks [round][wave][slw]
   int o_part;                       // P2 partial sums [pass_rows][pstride] fp32
   LayerPtrs lp[kMaxL];
 };
@@ -137,7 +148,11 @@ struct SmemHead {
   int nU;
   int route_claim, route_ready;    // small regime: the first free wave does the routing
   int shared_claim, shared_ready;  // small regime: ... and the shared expert's h
-  int unit_ctr[2];                 // small regime: P2 units handed out to waves
+  int unit_ctr[2 + kP1Groups];     // P2 units handed out to waves (shared, experts / expert group)
+  int task_ctr[3];                 // router / shared / expert gate-up tasks handed out
+  int rcnt[kMaxRounds][kWaves];    // slices of a router row / shared pair done, per round and slice group
+  int scnt[kMaxRounds][kWaves];
+  int nM, nG;                      // general regime: union slots on MFMA tiles, on GEMV
   unsigned cand_key[kWaves][2 * 64];  // top-k candidates of each wave (ordered logit bits), then the ranked k
   int cand_idx[kWaves][2 * 64];
   unsigned sink;
@@ -440,6 +455,12 @@ __device__ __forceinline__ void publish(float *q, float v) {
   __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// element i of an act-dtype array, published
+template <int D> __device__ __forceinline__ void publish_act(void *p, size_t i, float v) {
+  if constexpr (D == DT_F32) __hip_atomic_store((float *)p + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else __hip_atomic_store((uint16_t *)p + i, f32_to_bf16(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // A wave is done with the work barrier b waits for, and every value it wrote
 // for other workgroups went out through publish(): waiting for its stores to
 // complete (they are then visible device-wide) replaces the L2 write-back.
@@ -499,12 +520,32 @@ __device__ void bar_wait(KParams p, SmemHead &sh, int b) {
 // ---------------------------------------------------------------------------
 // LDS views
 
+// The kernel's dynamic LDS. Every region is addressed from this symbol, never
+// from a pointer held in memory, so the compiler sees LDS accesses (ds_*
+// instructions) in every function, inlined or not, and no function reloads a
+// base pointer from scratch memory.
+extern __shared__ __align__(16) unsigned char smem_raw[];
+
 struct Lds {
-  unsigned char *base;
-  __device__ SmemHead &head() const { return *reinterpret_cast<SmemHead *>(base); }
-  template <class T> __device__ T *at(int off) const { return reinterpret_cast<T *>(base + off); }
-  __device__ lds_t *raw(int off) const { return (lds_t *)(base + off); }
+  __device__ SmemHead &head() const { return *reinterpret_cast<SmemHead *>(smem_raw); }
+  template <class T> __device__ T *at(int off) const { return reinterpret_cast<T *>(smem_raw + off); }
+  __device__ lds_t *raw(int off) const { return (lds_t *)(smem_raw + off); }
 };
+
+// Arguments of a non-inlined function arrive in vector registers even when
+// they are uniform; re-reading them through lane 0 puts them back in scalar
+// registers, so parameter reads are scalar loads and addresses built from
+// them can use a scalar base (no memory round trip of vector loads first).
+template <class T> __device__ __forceinline__ T uni(T v) {
+  if constexpr (sizeof(T) == 8) {
+    const unsigned long long u = (unsigned long long)v;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+    return (T)(((unsigned long long)hi << 32) | lo);
+  } else {
+    return (T)__builtin_amdgcn_readfirstlane((int)v);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // x-hat
@@ -579,7 +620,9 @@ __device__ __forceinline__ void rmsnorm_rows(KParams p, KLayer lp, SmemHead &sh,
 // Small regime: this workgroup normalises every token into its own LDS:
 // xf [B][H] fp32 (router input) and xa [B][H] act (FFN input).
 template <int AD>
-__device__ __attribute__((noinline)) void stage_xhat(KParams p, KLayer lp, const Lds &L) {
+__device__ __attribute__((noinline)) void stage_xhat(KParams p_arg, KLayer lp_arg, const Lds &L) {
+  const KParams p = uni(p_arg);
+  const KLayer lp = uni(lp_arg);
   const int H = p->H;
   float *xf = L.at<float>(p->o_xf);
   lds_t *xa = L.raw(p->o_xa);
@@ -598,7 +641,9 @@ __device__ __attribute__((noinline)) void stage_xhat(KParams p, KLayer lp, const
 
 // General regime: workgroup t normalises token t into global memory.
 template <int AD>
-__device__ __attribute__((noinline)) void produce_xhat(KParams p, KLayer lp, const Lds &L) {
+__device__ __attribute__((noinline)) void produce_xhat(KParams p_arg, KLayer lp_arg, const Lds &L) {
+  const KParams p = uni(p_arg);
+  const KLayer lp = uni(lp_arg);
   const int H = p->H;
   for (int t = blockIdx.x; t < p->B; t += p->G) {
     const int tok[1] = {t};
@@ -625,11 +670,33 @@ __device__ __forceinline__ typename XSrc<XL>::ptr xhat_row(KParams p, const Lds 
 // ---------------------------------------------------------------------------
 // P0: router slices and shared gate/up rows
 
-// task (row e, slice s) -> rpart[s][t][e] for all tokens
+// The K-slices of one router row (or shared gate/up pair) are P0 tasks of
+// consecutive indices that waves of one workgroup handle in the same round
+// (the slice count divides the workgroup's wave count and the first index is a
+// multiple of it, so slice s is the group's wave s). Each wave leaves its
+// slice sums in its LDS slot of the round; the wave that finishes the last
+// slice of the group sums the slots in slice order (a fixed order: identical
+// rows give identical logits) and writes the result for other workgroups.
+__device__ __forceinline__ float *slice_slot(KParams p, const Lds &L, int round, int wave) {
+  return L.at<float>(p->o_slc) + ((size_t)round * kWaves + wave) * p->slw;
+}
+
+__device__ __forceinline__ bool last_slice(int (&cnt)[kMaxRounds][kWaves], int round, int NS) {
+  if (NS == 1) return true;
+  int old = 0;
+  if (lane_id() == 0)
+    old = __hip_atomic_fetch_add(&cnt[round][wave_id() / NS], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_amdgcn_readfirstlane(old) == NS - 1;
+}
+
+// router task tau = (row e, slice s) of round `round`: slice sums of all
+// tokens to this wave's LDS slot; the last slice's wave writes the logit rfin[t][e]
+// (published in the small regime)
 template <int RD, bool XL>
-__device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, int e, int s) {
-  const int H = p->H, E = p->E, B = p->B;
-  const int Ks = H / p->NSR;
+__device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, int tau, int round) {
+  const int H = p->H, E = p->E, B = p->B, NSR = p->NSR;
+  const int e = tau / NSR, s = tau % NSR;
+  const int Ks = H / NSR;
   const char *const wrow[1] = {(const char *)lp->rw + (size_t)e * H * dsz<RD>()};
   for_token_groups(B, [&]<int TG>(int t0, int nt) {
     typename XSrc<XL>::ptr xr[TG];
@@ -643,20 +710,35 @@ __device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, 
     for (int t = 0; t < TG; ++t) {
       const float v = wave_sum63(acc[0][t]);
       if (t < nt && lane_id() == 63) {
-        float *q = p->rpart + ((size_t)(t0 + t) * E + e) * 4 + s;
-        if constexpr (XL) publish(q, v);
-        else *q = v;
+        if (NSR == 1) {
+          if constexpr (XL) publish(p->rfin + (size_t)(t0 + t) * E + e, v);
+          else p->rfin[(size_t)(t0 + t) * E + e] = v;
+        } else {
+          slice_slot(p, L, round, wave_id())[t0 + t] = v;
+        }
       }
     }
   });
+  if (NSR > 1 && last_slice(L.head().rcnt, round, NSR)) {
+    const int w0 = wave_id() - s;
+    for (int t = lane_id(); t < B; t += 64) {
+      float sum = slice_slot(p, L, round, w0)[t];
+      for (int s2 = 1; s2 < NSR; ++s2) sum += slice_slot(p, L, round, w0 + s2)[t];
+      if constexpr (XL) publish(p->rfin + (size_t)t * E + e, sum);
+      else p->rfin[(size_t)t * E + e] = sum;
+    }
+  }
 }
 
-// shared gate/up task (pair j, slice s). Small regime: partial g and u sums to
-// hspart[s][t][j] and hspart[s][t][Is + j]. General regime (one slice): h.
+// shared gate/up task tau = (pair j, slice s) of round `round`. One slice
+// (general regime): h of every token straight to hsbuf (act dtype). Several
+// slices (small regime): slice sums to the LDS slot, and the last slice's wave
+// publishes h, act-rounded, as fp32 to hsh32.
 template <int AD, int SD, bool XL>
-__device__ __forceinline__ void shared_gu_task(KParams p, KLayer lp, const Lds &L, int j, int s) {
-  const int H = p->H, B = p->B, Is = p->Is;
-  const int Ks = H / p->NSS;
+__device__ __forceinline__ void shared_gu_task(KParams p, KLayer lp, const Lds &L, int tau, int round) {
+  const int H = p->H, B = p->B, Is = p->Is, NSS = p->NSS;
+  const int j = tau / NSS, s = tau % NSS;
+  const int Ks = H / NSS;
   const size_t rowb = (size_t)H * dsz<SD>();
   const char *const wrow[2] = {(const char *)lp->sgu + (size_t)j * rowb, (const char *)lp->sgu + (size_t)(Is + j) * rowb};
   for_token_groups(B, [&]<int TG>(int t0, int nt) {
@@ -672,16 +754,33 @@ __device__ __forceinline__ void shared_gu_task(KParams p, KLayer lp, const Lds &
       const float g = wave_sum63(acc[0][t]);
       const float u = wave_sum63(acc[1][t]);
       if (t < nt && lane_id() == 63) {
-        if (p->NSS > 1 || XL) {
-          float *hp = p->hspart + ((size_t)s * B + t0 + t) * 2 * Is;
-          publish(hp + j, g);
-          publish(hp + Is + j, u);
+        if constexpr (XL) {
+          if (NSS == 1) {
+            publish(p->hsh32 + (size_t)(t0 + t) * Is + j, round_act<AD>(silu_mul(g, u)));
+          } else {
+            float *q = slice_slot(p, L, round, wave_id()) + 2 * (t0 + t);
+            q[0] = g;
+            q[1] = u;
+          }
         } else {
           store_act<AD>(p->hsbuf, (size_t)(t0 + t) * Is + j, silu_mul(g, u));
         }
       }
     }
   });
+  if constexpr (XL) {
+    if (NSS > 1 && last_slice(L.head().scnt, round, NSS)) {
+      const int w0 = wave_id() - s;
+      for (int t = lane_id(); t < B; t += 64) {
+        float g = slice_slot(p, L, round, w0)[2 * t], u = slice_slot(p, L, round, w0)[2 * t + 1];
+        for (int s2 = 1; s2 < NSS; ++s2) {
+          g += slice_slot(p, L, round, w0 + s2)[2 * t];
+          u += slice_slot(p, L, round, w0 + s2)[2 * t + 1];
+        }
+        publish(p->hsh32 + (size_t)t * Is + j, round_act<AD>(silu_mul(g, u)));
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -708,28 +807,23 @@ __device__ __forceinline__ float unord_f32(unsigned o) {
 
 constexpr int kMaxCand = 64;
 
-// Logits of token t for the experts of this lane (e = lane + 64 j), from the
-// router partials: one 16-byte load per expert holds its K-slice partials,
-// all loads issued before the first use. Slots past E read expert E-1.
+// Logits of token t for the experts of this lane (e = lane + 64 j), all
+// loads issued before the first use. Slots past E read expert E-1.
+// (32-bit byte offsets from a uniform base: one register per address)
+__device__ __forceinline__ float ld_off(const float *base, unsigned i) {
+  return *(const float *)((const char *)base + i * 4u);
+}
+
 __device__ __forceinline__ void load_logits(KParams p, KLayer lp, int t, float (&v)[kMaxE / 64]) {
-  const int lane = lane_id(), E = p->E, NSR = p->NSR;
+  const int lane = lane_id(), E = p->E;
   constexpr int PER = kMaxE / 64;
-  const u32x4 *base = (const u32x4 *)(p->rpart + (size_t)t * E * 4);
-  u32x4 q[PER];
+  const float *base = p->rfin + (size_t)t * E;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) q[j] = base[min(lane + 64 * j, E - 1)];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    float s = __uint_as_float(q[j].x);
-    if (NSR > 1) s += __uint_as_float(q[j].y);
-    if (NSR > 2) s += __uint_as_float(q[j].z);
-    if (NSR > 3) s += __uint_as_float(q[j].w);
-    v[j] = s;
-  }
+  for (int j = 0; j < PER; ++j) v[j] = ld_off(base, (unsigned)min(lane + 64 * j, E - 1));
   if (const float *rb = lp->rb) {
     float b[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) b[j] = rb[min(lane + 64 * j, E - 1)];
+    for (int j = 0; j < PER; ++j) b[j] = ld_off(rb, (unsigned)min(lane + 64 * j, E - 1));
 #pragma unroll
     for (int j = 0; j < PER; ++j) v[j] += b[j];
   }
@@ -737,7 +831,10 @@ __device__ __forceinline__ void load_logits(KParams p, KLayer lp, int t, float (
 
 // Rare path (more than 64 logits tie at the threshold): k rounds of wave
 // argmax over all logits. Returns the selection in lanes < k.
-__device__ __attribute__((noinline)) void topk_rounds(KParams p, KLayer lp, int t, float &myv, int &myidx) {
+__device__ __attribute__((noinline)) void topk_rounds(KParams p_arg, KLayer lp_arg, int t_arg, float &myv, int &myidx) {
+  const KParams p = uni(p_arg);
+  const KLayer lp = uni(lp_arg);
+  const int t = uni(t_arg);
   const int lane = lane_id(), E = p->E, k = p->k;
   constexpr int PER = kMaxE / 64;
   float v[PER];
@@ -764,7 +861,11 @@ __device__ __attribute__((noinline)) void topk_rounds(KParams p, KLayer lp, int 
   }
 }
 
-__device__ __attribute__((noinline)) void topk_token(KParams p, KLayer lp, const Lds &L, int t, bool write_out) {
+__device__ __attribute__((noinline)) void topk_token(KParams p_arg, KLayer lp_arg, const Lds &L, int t_arg, bool write_out_arg) {
+  const KParams p = uni(p_arg);
+  const KLayer lp = uni(lp_arg);
+  const int t = uni(t_arg);
+  const bool write_out = uni(write_out_arg);
   const int lane = lane_id();
   const int E = p->E, k = p->k;
   constexpr int PER = kMaxE / 64;
@@ -853,7 +954,8 @@ __device__ __attribute__((noinline)) void topk_token(KParams p, KLayer lp, const
 
 // gather tables: union U of selected experts (ascending), each expert's pairs
 // (t*k+i) in ascending token order.
-__device__ __attribute__((noinline)) void build_tables(KParams p, const Lds &L) {
+__device__ __attribute__((noinline)) void build_tables(KParams p_arg, const Lds &L) {
+  const KParams p = uni(p_arg);
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   const int E = p->E, P = p->B * p->k;
   SmemHead &sh = L.head();
@@ -909,7 +1011,8 @@ __device__ __attribute__((noinline)) void build_tables(KParams p, const Lds &L) 
 // The same tables built by one wave when B*k <= 64: the (expert, pair) keys
 // are sorted across the lanes (bitonic), then each run of equal experts is a
 // union slot. Pairs of one expert keep ascending order, hence ascending tokens.
-__device__ __attribute__((noinline)) void build_tables_wave(KParams p, const Lds &L) {
+__device__ __attribute__((noinline)) void build_tables_wave(KParams p_arg, const Lds &L) {
+  const KParams p = uni(p_arg);
   const int lane = lane_id(), P = p->B * p->k;
   const int *sel_idx = L.at<int>(p->o_sel_idx);
   int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
@@ -978,8 +1081,8 @@ __device__ __forceinline__ void expert_gu_task(KParams p, KLayer lp, const Lds &
       const float uu = wave_sum63(acc[1][t]) * us;
       if (t < nt && lane_id() == 63) {
         const float h = silu_mul(g, uu);
-        // small regime: fp32 copy of the act-rounded h, published; otherwise h in the act dtype
-        if constexpr (XL) publish((float *)p->hbuf + (size_t)slot[t] * I + j, round_act<AD>(h));
+        // h in the act dtype (published in the small regime)
+        if constexpr (XL) publish_act<AD>(p->hbuf, (size_t)slot[t] * I + j, h);
         else store_act<AD>(p->hbuf, (size_t)slot[t] * I + j, h);
       }
     }
@@ -989,78 +1092,33 @@ __device__ __forceinline__ void expert_gu_task(KParams p, KLayer lp, const Lds &
 // ---------------------------------------------------------------------------
 // P2: down projections of this workgroup's rows
 
-// Small regime, one wave: the shared expert's h for every token from the
-// slice partials, into LDS. Lane l covers 4 consecutive columns per step; all
-// partial loads of a step are issued before the first use.
+// Small regime, one wave: the shared expert's h of every token (published
+// fp32, already act-rounded) into LDS in the act dtype. Every load of a step
+// is issued before the first use.
 template <int AD>
-__device__ __attribute__((noinline)) void finish_shared_h_wave(KParams p, const Lds &L) {
-  const int Is = p->Is, B = p->B, NSS = p->NSS, lane = lane_id();
+__device__ __forceinline__ void stage_shared_h_wave(KParams p, const Lds &L) {
+  const int n4 = p->B * p->Is / 4, lane = lane_id();
+  const u32x4 *src = (const u32x4 *)p->hsh32;
   lds_t *hs = L.raw(p->o_hs);
-  constexpr int U = 2;  // 16-byte groups per lane per step
-  for (int t = 0; t < B; ++t) {
-    for (int j0 = 0; j0 < Is; j0 += 64 * 4 * U) {
-      u32x4 g[U][2], u[U][2];
+  constexpr int U = 8;
+  for (int i0 = 0; i0 < n4; i0 += 64 * U) {
+    u32x4 v[U];
 #pragma unroll
-      for (int q = 0; q < U; ++q) {
-        const int j = min(j0 + (q * 64 + lane) * 4, Is - 4);
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * 64 + lane;
+      v[u] = src[i < n4 ? i : 0];
+    }
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const float *hp = p->hspart + ((size_t)min(s2, NSS - 1) * B + t) * 2 * Is;
-          g[q][s2] = *(const u32x4 *)(hp + j);
-          u[q][s2] = *(const u32x4 *)(hp + Is + j);
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * 64 + lane;
+      if (i < n4) {
+        if constexpr (AD == DT_F32) {
+          *(__attribute__((address_space(3))) u32x4 *)(hs + (size_t)i * 16) = v[u];
+        } else {
+          *(__attribute__((address_space(3))) u32x2 *)(hs + (size_t)i * 8) =
+              u32x2{(v[u].x >> 16) | (v[u].y & 0xFFFF0000u), (v[u].z >> 16) | (v[u].w & 0xFFFF0000u)};
         }
       }
-#pragma unroll
-      for (int q = 0; q < U; ++q) {
-        const int j = j0 + (q * 64 + lane) * 4;
-        if (j < Is) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            float gg = __uint_as_float(g[q][0][c]), uu = __uint_as_float(u[q][0][c]);
-            if (NSS > 1) { gg += __uint_as_float(g[q][1][c]); uu += __uint_as_float(u[q][1][c]); }
-            store_act_lds<AD>(hs, (size_t)t * Is + j + c, silu_mul(gg, uu));
-          }
-        }
-      }
-    }
-  }
-}
-
-// Small regime: the expert h of every selected (token, expert) pair, from the
-// published fp32 copy into LDS in the act dtype (values are already rounded).
-// Every load is issued before the first use.
-template <int AD>
-__device__ __attribute__((noinline)) void stage_h(KParams p, const Lds &L) {
-  const int n4 = p->B * p->k * p->I / 4;  // groups of 4 values
-  constexpr int U = 8;                     // covers B*k*I <= 32768 values in one round
-  const u32x4 *src = (const u32x4 *)p->hbuf;
-  u32x4 v[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int i = threadIdx.x + u * kThreads;
-    v[u] = src[i < n4 ? i : 0];
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int i = threadIdx.x + u * kThreads;
-    if (i < n4) {
-      if constexpr (AD == DT_F32) {
-        *(__attribute__((address_space(3))) u32x4 *)(L.raw(p->o_h) + (size_t)i * 16) = v[u];
-      } else {
-        // the values are bf16-exact: their top halves are the bf16 patterns
-        const uint32_t lo = (v[u].x >> 16) | (v[u].y & 0xFFFF0000u);
-        const uint32_t hi = (v[u].z >> 16) | (v[u].w & 0xFFFF0000u);
-        *(__attribute__((address_space(3))) u32x2 *)(L.raw(p->o_h) + (size_t)i * 8) = u32x2{lo, hi};
-      }
-    }
-  }
-  for (int i = threadIdx.x + U * kThreads; i < n4; i += kThreads) {  // larger shapes: rest, one by one
-    const u32x4 w = src[i];
-    if constexpr (AD == DT_F32) {
-      *(__attribute__((address_space(3))) u32x4 *)(L.raw(p->o_h) + (size_t)i * 16) = w;
-    } else {
-      *(__attribute__((address_space(3))) u32x2 *)(L.raw(p->o_h) + (size_t)i * 8) =
-          u32x2{(w.x >> 16) | (w.y & 0xFFFF0000u), (w.z >> 16) | (w.w & 0xFFFF0000u)};
     }
   }
 }
@@ -1093,6 +1151,13 @@ __device__ __forceinline__ void down_unit(const char *const (&wrow)[kRowBlock], 
   }
 }
 
+// partial sums of P2: LDS rows of the pass (small regime) or global rows
+template <bool SMALL>
+__device__ __forceinline__ float *part_base(KParams p, const Lds &L) {
+  if constexpr (SMALL) return L.at<float>(p->o_part);
+  else return p->partbuf;
+}
+
 // Next P2 unit of this wave: handed out through an LDS counter (DYN, small
 // regime) or dealt round-robin from wave w0.
 template <bool DYN>
@@ -1114,10 +1179,11 @@ __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Ld
   const int I = p->I, Is = p->Is, B = p->B;
   const int nsh = Is / I, P = B * p->k, pstride = P + B * nsh;
   const int nrb = (pr1 - pr0) / kRowBlock;
-  float *part = L.at<float>(p->o_part);
+  float *part = part_base<SMALL>(p, L);
+  const int prb = SMALL ? pr0 : 0;
   const float one[kRowBlock] = {1.f, 1.f, 1.f, 1.f};
   int cur = -1;
-  for (int un = next_unit<SMALL>(L.head(), 0, cur, w0); un < nrb * nsh; un = next_unit<SMALL>(L.head(), 0, cur, w0)) {
+  for (int un = next_unit<true>(L.head(), 0, cur, w0); un < nrb * nsh; un = next_unit<true>(L.head(), 0, cur, w0)) {
     const int hf = un / nrb, rb = un % nrb;
     const int o0 = pr0 + rb * kRowBlock;
     const char *wrow[kRowBlock];
@@ -1134,64 +1200,292 @@ __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Ld
         else xr[t] = (const char *)p->hsbuf + ((size_t)tt * Is + (size_t)hf * I) * dsz<AD>();
         col[t] = P + (t0 + t) * nsh + hf;
       }
-      down_unit<SD, AD, SMALL, TG>(wrow, I, xr, one, part + (size_t)(o0 - pr0) * pstride, pstride, col, nt);
+      down_unit<SD, AD, SMALL, TG>(wrow, I, xr, one, part + (size_t)(o0 - prb) * pstride, pstride, col, nt);
     });
   }
 }
 
-// routed-expert units of rows [pr0, pr1): (expert slot, row block), expert-major
-// so a wave's consecutive units read consecutive rows; h from LDS (small
-// regime) or global memory
+// ---------------------------------------------------------------------------
+// MFMA tiles for the experts that many tokens of a batch select (general
+// regime). v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+i] and
+// B[8(l/16)+i][l%16] (i < 8) and receives D[4(l/16)+i][l%16] (i < 4). A is 16
+// weight rows, B is 16 tokens of the activation; the weights are read once
+// for all the expert's tokens. fp8 weights: a lane loads 16 codes of its row,
+// converts them exactly to bf16 (gfx950's OCP e4m3 conversion) and feeds two
+// MFMAs; B takes the matching activation columns, so the K order is the same
+// permutation on both sides.
+
+#ifndef MOE_MFMA_MIN
+#define MOE_MFMA_MIN 16
+#endif
+constexpr int kMfmaMin = MOE_MFMA_MIN;  // tokens of one expert from which its rows go through MFMA tiles
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// 8 e4m3 codes (two words) -> 8 bf16 (exact: e4m3 values are bf16 values)
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+  r.y = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+  r.z = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
+  r.w = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
+  return r;
+}
+
+// acc[row tile r][token tile nt] += W rows (wa[r]) x activation rows (xb[nt]) over K
+// columns. Lane l: weight row l%16 of each tile, token column l%16, K group l/16.
+template <int WD, int NR, int NT>
+__device__ __forceinline__ void mfma_rows(const char *const (&wa)[NR], int K, const char *const (&xb)[NT],
+                                          f32x4 (&acc)[NR][NT]) {
+  const int kq = lane_id() >> 4;
+  if constexpr (WD == DT_FP8) {
+    for (int k0 = 0; k0 < K; k0 += 64) {
+      const int c = k0 + kq * 16;
+      u32x4 w[NR], x0[NT], x1[NT];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) w[r] = ldw(wa[r] + c);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        x0[t] = *(const u32x4 *)(xb[t] + (size_t)c * 2);
+        x1[t] = *(const u32x4 *)(xb[t] + (size_t)(c + 8) * 2);
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const u32x4 lo = fp8x8_to_bf16(w[r].x, w[r].y), hi = fp8x8_to_bf16(w[r].z, w[r].w);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          acc[r][t] = mfma16(lo, x0[t], acc[r][t]);
+          acc[r][t] = mfma16(hi, x1[t], acc[r][t]);
+        }
+      }
+    }
+  } else {
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      const int c = k0 + kq * 8;
+      u32x4 w[NR], x[NT];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) w[r] = ldw(wa[r] + (size_t)c * 2);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) x[t] = *(const u32x4 *)(xb[t] + (size_t)c * 2);
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[r][t] = mfma16(w[r], x[t], acc[r][t]);
+    }
+  }
+}
+
+// Run f.template operator()<NT>() with NT = ceil(n / 16) token tiles (1..4).
+template <class F>
+__device__ __forceinline__ void with_token_tiles(int n, F &&f) {
+  const int nt = (n + 15) / 16;
+  if (nt <= 1) f.template operator()<1>();
+  else if (nt == 2) f.template operator()<2>();
+  else if (nt == 3) f.template operator()<3>();
+  else f.template operator()<4>();
+}
+
+// P1 MFMA task: rows [16 jb, 16 jb + 16) of union slot u's gate and up
+// matrices for all of the expert's tokens; h = SiLU(g) * u to hbuf.
+template <int AD, int ED>
+__device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L, int u, int jb) {
+  const int H = p->H, I = p->I, k = p->k, lane = lane_id();
+  const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
+  const int *pl = L.at<int>(p->o_plist) + ustart[u];
+  const int e = ulist[u], n = ucnt[u];
+  const int r = lane & 15, kq = lane >> 4;
+  const size_t rowb = (size_t)H * dsz<ED>();
+  const char *gu = (const char *)lp->egu + (size_t)e * 2 * I * rowb;
+  const char *const wa[2] = {gu + (size_t)(16 * jb + r) * rowb, gu + (size_t)(I + 16 * jb + r) * rowb};
+  float gs = 1.f, us = 1.f;
+  if constexpr (ED == DT_FP8) {
+    const uint16_t *sc = lp->egus + (size_t)e * (2 * I / 128);
+    gs = __uint_as_float((uint32_t)sc[(16 * jb) / 128] << 16);
+    us = __uint_as_float((uint32_t)sc[(I + 16 * jb) / 128] << 16);
+  }
+  with_token_tiles(n, [&]<int NT>() {
+    const char *xb[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int c = min(16 * t + r, n - 1);  // columns past n repeat a valid token; discarded
+      xb[t] = (const char *)p->xa + (size_t)(pl[c] / k) * H * 2;
+    }
+    f32x4 acc[2][NT];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mfma_rows<ED, 2, NT>(wa, H, xb, acc);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int c = 16 * t + r;
+      if (c < n) {
+        const int slot = pl[c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          store_act<AD>(p->hbuf, (size_t)slot * I + 16 * jb + 4 * kq + i, silu_mul(acc[0][t][i] * gs, acc[1][t][i] * us));
+      }
+    }
+  });
+}
+
+// P2 MFMA tile: rows [o0, o0 + 16) of union slot s's down matrix for all of
+// the expert's tokens; rows >= lo go to the partial sums (rows below lo were
+// written by the previous tile of the same workgroup).
+template <int AD, int ED>
+__device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &L, int s, int o0, int lo, float *part,
+                                               int pstride) {
+  const int H = p->H, I = p->I, lane = lane_id();
+  const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
+  const int *pl = L.at<int>(p->o_plist) + ustart[s];
+  const int e = ulist[s], n = ucnt[s];
+  const int r = lane & 15, kq = lane >> 4;
+  const char *const wa[1] = {(const char *)lp->ed + ((size_t)e * H + o0 + r) * I * dsz<ED>()};
+  with_token_tiles(n, [&]<int NT>() {
+    const char *xb[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xb[t] = (const char *)p->hbuf + (size_t)pl[min(16 * t + r, n - 1)] * I * 2;
+    f32x4 acc[1][NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mfma_rows<ED, 1, NT>(wa, I, xb, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = o0 + 4 * kq + i;
+      float sc = 1.f;
+      if constexpr (ED == DT_FP8) sc = __uint_as_float((uint32_t)lp->eds[(size_t)e * (H / 128) + o / 128] << 16);
+      if (o >= lo) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int c = 16 * t + r;
+          if (c < n) part[(size_t)o * pstride + pl[c]] = acc[0][t][i] * sc;
+        }
+      }
+    }
+  });
+}
+
+// Union slots split by token count: MFMA tiles (n >= kMfmaMin) and GEMV.
+__device__ __attribute__((noinline)) void classify_slots(KParams p_arg, const Lds &L) {
+  const KParams p = uni(p_arg);
+  SmemHead &sh = L.head();
+  if (wave_id() == 0) {
+    const int lane = lane_id(), nU = sh.nU;
+    const int *ucnt = L.at<int>(p->o_ucnt);
+    int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
+    int nm = 0, ng = 0;
+    for (int u0 = 0; u0 < nU; u0 += 64) {
+      const int u = u0 + lane;
+      const bool valid = u < nU;
+      const bool m = valid && p->use_mfma && ucnt[u] >= kMfmaMin;
+      const unsigned long long bm = __ballot(m), bg = __ballot(valid && !m);
+      const unsigned long long below = (1ull << lane) - 1ull;
+      if (m) mslot[nm + __popcll(bm & below)] = u;
+      if (valid && !m) gslot[ng + __popcll(bg & below)] = u;
+      nm += __popcll(bm);
+      ng += __popcll(bg);
+    }
+    if (lane == 0) { sh.nM = nm; sh.nG = ng; }
+  }
+  __syncthreads();
+}
+
+// One routed expert's 4-row GEMV unit (slot s, rows [o0, o0+4)).
 template <int AD, int ED, bool SMALL>
-__device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, int w0) {
-  const int H = p->H, I = p->I, B = p->B;
-  const int nsh = p->Is / I, P = B * p->k, pstride = P + B * nsh;
-  const int nU = L.head().nU;
-  const int nrb = (pr1 - pr0) / kRowBlock;
+__device__ __forceinline__ void expert_down_gemv(KParams p, KLayer lp, const Lds &L, int s, int o0, float *prow,
+                                                 int pstride) {
+  const int H = p->H, I = p->I;
   const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   const int *plist = L.at<int>(p->o_plist);
-  float *part = L.at<float>(p->o_part);
-  int cur = -1;
-  for (int un = next_unit<SMALL>(L.head(), 1, cur, w0); un < nrb * nU; un = next_unit<SMALL>(L.head(), 1, cur, w0)) {
-    const int s = un / nrb, rb = un % nrb;
-    const int o0 = pr0 + rb * kRowBlock;
-    const int e = ulist[s];
-    const int n = ucnt[s];
-    const int *pl = plist + ustart[s];
-    const char *wrow[kRowBlock];
-    float sc[kRowBlock];
+  const int e = ulist[s];
+  const int n = ucnt[s];
+  const int *pl = plist + ustart[s];
+  const char *wrow[kRowBlock];
+  float sc[kRowBlock];
 #pragma unroll
-    for (int r = 0; r < kRowBlock; ++r) {
-      wrow[r] = (const char *)lp->ed + ((size_t)e * H + o0 + r) * I * dsz<ED>();
-      sc[r] = 1.f;
-      if constexpr (ED == DT_FP8) sc[r] = __uint_as_float((uint32_t)lp->eds[(size_t)e * (H / 128) + (o0 + r) / 128] << 16);
+  for (int r = 0; r < kRowBlock; ++r) {
+    wrow[r] = (const char *)lp->ed + ((size_t)e * H + o0 + r) * I * dsz<ED>();
+    sc[r] = 1.f;
+    if constexpr (ED == DT_FP8) sc[r] = __uint_as_float((uint32_t)lp->eds[(size_t)e * (H / 128) + (o0 + r) / 128] << 16);
+  }
+  for_token_groups(n, [&]<int TG>(int t0, int nt) {
+    typename XSrc<false>::ptr xr[TG];
+    int col[TG];
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      col[t] = pl[t0 + (t < nt ? t : 0)];
+      xr[t] = (const char *)p->hbuf + (size_t)col[t] * I * dsz<AD>();
     }
-    for_token_groups(n, [&]<int TG>(int t0, int nt) {
-      typename XSrc<SMALL>::ptr xr[TG];
-      int col[TG];
-#pragma unroll
-      for (int t = 0; t < TG; ++t) {
-        col[t] = pl[t0 + (t < nt ? t : 0)];
-        if constexpr (SMALL) xr[t] = L.raw(p->o_h) + (size_t)col[t] * I * dsz<AD>();
-        else xr[t] = (const char *)p->hbuf + (size_t)col[t] * I * dsz<AD>();
+    down_unit<ED, AD, false, TG>(wrow, I, xr, sc, prow, pstride, col, nt);
+  });
+}
+
+// routed-expert units of rows [pr0, pr1), handed out through an LDS counter.
+// Small regime: (expert slot, row block), expert-major so a wave's
+// consecutive units read consecutive rows; h from LDS. General regime: the
+// MFMA tiles of the experts with many tokens first, then the GEMV units of the
+// others; h from global memory.
+// routed-expert units of rows [pr0, pr1): (union slot, 4-row block), slot-major
+// so a wave's consecutive units read consecutive rows. Small regime: the slots
+// [ua, ub) of one expert group, handed out through unit counter uc.
+template <int AD, int ED, bool SMALL>
+__device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, int w0,
+                                                  int ua = 0, int ub = 0, int uc = 1) {
+  const int I = p->I, B = p->B;
+  const int nsh = p->Is / I, P = B * p->k, pstride = P + B * nsh;
+  const int nrb = (pr1 - pr0) / kRowBlock;
+  float *part = part_base<SMALL>(p, L);
+  const int prb = SMALL ? pr0 : 0;
+  int cur = -1;
+  const int ntile = (pr1 - pr0) >= 16 ? (pr1 - pr0 + 15) / 16 : 0;
+  if (SMALL || L.head().nM == 0 || ntile == 0) {
+    // every slot on GEMV (also the MFMA slots of a workgroup with fewer than 16 rows)
+    if (!SMALL) { ua = 0; ub = L.head().nU; uc = 1; }
+    const int nu = ub - ua;
+    for (int un = next_unit<true>(L.head(), uc, cur, w0); un < nrb * nu; un = next_unit<true>(L.head(), uc, cur, w0)) {
+      const int s = ua + un / nrb, o0 = pr0 + (un % nrb) * kRowBlock;
+      expert_down_gemv<AD, ED, SMALL>(p, lp, L, s, o0, part + (size_t)(o0 - prb) * pstride, pstride);
+    }
+  } else {
+    const int nM = L.head().nM, nG = L.head().nG;
+    const int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
+    const int nmu = nM * ntile;
+    for (int un = next_unit<true>(L.head(), 1, cur, w0); un < nmu + nG * nrb; un = next_unit<true>(L.head(), 1, cur, w0)) {
+      if (un < nmu) {
+        const int ti = un % ntile;
+        const int o0 = min(pr0 + 16 * ti, pr1 - 16);  // the last tile ends at pr1
+        const int lo = pr0 + 16 * ti;                 // rows below lo belong to the previous tile
+        mfma_down_tile<AD, ED>(p, lp, L, mslot[un / ntile], o0, lo, part, pstride);
+      } else {
+        const int g = un - nmu;
+        const int s = gslot[g / nrb], o0 = pr0 + (g % nrb) * kRowBlock;
+        expert_down_gemv<AD, ED, false>(p, lp, L, s, o0, part + (size_t)(o0 - prb) * pstride, pstride);
       }
-      down_unit<ED, AD, SMALL, TG>(wrow, I, xr, sc, part + (size_t)(o0 - pr0) * pstride, pstride, col, nt);
-    });
+    }
   }
 }
 
 // y = x + shared + sum_i w_i d_i (rank order i) for rows [pr0, pr1)
-template <int AD>
+template <int AD, bool SMALL>
 __device__ __forceinline__ void combine(KParams p, KLayer lp, const Lds &L, int pr0, int pr1) {
   const int H = p->H, k = p->k, B = p->B;
   const int nsh = p->Is / p->I, P = B * k, pstride = P + B * nsh;
-  const float *part = L.at<float>(p->o_part);
+  const float *part = part_base<SMALL>(p, L);
+  const int prb = SMALL ? pr0 : 0;
   const float *sel_w = L.at<float>(p->o_sel_w);
   const int cells = (pr1 - pr0) * B;
   for (int c = threadIdx.x; c < cells; c += kThreads) {
     const int ro = c / B, t = c % B;
     const int o = pr0 + ro;
-    const float *pp = part + (size_t)ro * pstride;
+    const float *pp = part + (size_t)(o - prb) * pstride;
     float sh = 0.f;
     for (int hf = 0; hf < nsh; ++hf) sh += pp[P + t * nsh + hf];
     float rt = 0.f;
@@ -1209,20 +1503,33 @@ __device__ __forceinline__ unsigned touch_lines(const char *p, size_t bytes) {
   return acc;
 }
 
+// P0 task of wave wv of workgroup g in round r, or -1. Every round but the
+// last gives each workgroup kWaves consecutive task indices; the last gives
+// each p0w (fewer when the tasks left do not need all waves), so the spare
+// waves of every workgroup are free early and one of them routes the batch.
+// The slices of a row stay within one workgroup and round: p0w and the
+// shared tasks' first index are multiples of the slice counts.
+__device__ __forceinline__ int p0_task(KParams p, int r, int g, int wv) {
+  const int w = (r == p->p0r - 1) ? p->p0w : kWaves;
+  return wv < w ? r * p->G * kWaves + g * w + wv : -1;
+}
+
 // The weights this wave reads first in the next layer's P0 (its router and
 // shared gate/up slices), loaded while the layer barrier is pending.
 template <int RD, int SD>
-__device__ __forceinline__ unsigned prefetch_p0(KParams p, KLayer nl, int W, int NW) {
+__device__ __forceinline__ unsigned prefetch_p0(KParams p, KLayer nl) {
   const int H = p->H, NSR = p->NSR, NSS = p->NSS, E = p->E, Is = p->Is;
   const int nrt = E * NSR;
   unsigned acc = 0;
-  for (int tau = W; tau < nrt + Is * NSS; tau += NW) {
+  for (int r = 0; r < p->p0r; ++r) {
+    const int tau = p0_task(p, r, blockIdx.x, wave_id());
+    if (tau < 0 || tau >= p->s0 + Is * NSS) continue;
     if (tau < nrt) {
       const int e = tau / NSR, s = tau % NSR;
       const size_t ks = (size_t)(H / NSR) * dsz<RD>();
       acc ^= touch_lines((const char *)nl->rw + (size_t)e * H * dsz<RD>() + s * ks, ks);
-    } else {
-      const int j = (tau - nrt) / NSS, s = (tau - nrt) % NSS;
+    } else if (tau >= p->s0) {
+      const int j = (tau - p->s0) / NSS, s = (tau - p->s0) % NSS;
       const size_t ks = (size_t)(H / NSS) * dsz<SD>();
       const size_t rowb = (size_t)H * dsz<SD>();
       acc ^= touch_lines((const char *)nl->sgu + (size_t)j * rowb + s * ks, ks);
@@ -1235,50 +1542,134 @@ __device__ __forceinline__ unsigned prefetch_p0(KParams p, KLayer nl, int W, int
 // ---------------------------------------------------------------------------
 // the kernel
 
-// Small regime: the first wave of the workgroup to get here (it has no P0
-// work left) waits for the router barrier, routes every token and builds the
-// gather tables; the other waves keep streaming their P0 rows meanwhile and
-// pick the tables up from LDS when they are done.
-template <bool FIRST_WAVE_ROUTES>
-__device__ __forceinline__ void route_small(KParams p, KLayer lp, const Lds &L, int b_router) {
+// Next task of this workgroup's share [a, z) (handed out through an LDS
+// counter, so waves that start late or run slow take fewer), or -1.
+__device__ __forceinline__ int take(SmemHead &sh, int which, int a, int z) {
+  int q = 0;
+  if (lane_id() == 0) q = __hip_atomic_fetch_add(&sh.task_ctr[which], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  q = __builtin_amdgcn_readfirstlane(q) + a;
+  return q < z ? q : -1;
+}
+
+// workgroup g's contiguous share of n tasks
+__device__ __forceinline__ int share_lo(int n, int g, int G) { return (int)((long long)n * g / G); }
+
+__device__ __forceinline__ void raise_flag(int &f) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if (lane_id() == 0) __hip_atomic_store(&f, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void wait_flag(int &f) {
+  if (lane_id() == 0)
+    while (__hip_atomic_load(&f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// P0 of this wave: its router slices, arrival at the router barrier, its
+// shared gate/up slices, arrival at the shared barrier. PUB: the small
+// regime's published stores and arrivals.
+template <int AD, int RD, int SD, bool PUB>
+__device__ __forceinline__ void p0_tasks(KParams p, KLayer lp, const Lds &L, int b0) {
   SmemHead &sh = L.head();
+  const int nrt = p->E * p->NSR, s0 = p->s0, end = s0 + p->Is * p->NSS;
+  bool routed = false;  // arrived at the router barrier
+  for (int r = 0; r < p->p0r; ++r) {
+    const int tau = p0_task(p, r, blockIdx.x, wave_id());
+    if (tau < 0 || tau >= end) break;
+    if (tau >= nrt && !routed) {
+      if constexpr (PUB) bar_arrive_published(p, sh, b0 + BAR_ROUTER);
+      else bar_arrive(p, sh, b0 + BAR_ROUTER);
+      routed = true;
+    }
+    if (tau < nrt) router_task<RD, PUB>(p, lp, L, tau, r);
+    else if (tau >= s0) shared_gu_task<AD, SD, PUB>(p, lp, L, tau - s0, r);
+  }
+  if constexpr (PUB) {
+    if (!routed) bar_arrive_published(p, sh, b0 + BAR_ROUTER);
+    bar_arrive_published(p, sh, b0 + BAR_SHARED);
+  } else {
+    if (!routed) bar_arrive(p, sh, b0 + BAR_ROUTER);
+    bar_arrive(p, sh, b0 + BAR_SHARED);
+  }
+}
+
+// One layer at B <= 2. P0: router slices, then shared gate/up slices, dealt
+// round-robin over all waves of the grid (every slice is ~7 KB, so the waves
+// finish together). The first wave of each workgroup to run out of P0 work
+// routes the batch and builds the gather tables (by then the memory system has
+// drained, so its few dependent loads are fast), the others wait for the
+// tables. P1 and P2 overlap: a wave done with P1 runs the shared expert's
+// down rows and then the routed experts' down rows of every expert group
+// whose barrier has passed, while slower waves finish the later groups. The
+// first wave done with P1 stages the shared expert's h.
+template <int AD, int RD, int ED, int SD>
+__device__ __forceinline__ void layer_small(KParams p, KLayer lp, const Lds &L, int b0, int W, int NW) {
+  SmemHead &sh = L.head();
+  const int G = p->G, g = blockIdx.x;
+  stage_xhat<AD>(p, lp, L);
+
+  // P0
+  p0_tasks<AD, RD, SD, true>(p, lp, L, b0);
+
+  // routing, by the first wave out of P0 work
   int claimed = 0;
   if (lane_id() == 0)
     claimed = __hip_atomic_exchange(&sh.route_claim, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
   claimed = __builtin_amdgcn_readfirstlane(claimed);
   if (claimed) {
-    bar_wait(p, sh, b_router);
+    bar_wait(p, sh, b0 + BAR_ROUTER);
     for (int t = 0; t < p->B; ++t) topk_token(p, lp, L, t, blockIdx.x == 0);
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
     build_tables_wave(p, L);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    if (lane_id() == 0) __hip_atomic_store(&sh.route_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  } else if (lane_id() == 0) {
-    while (__hip_atomic_load(&sh.route_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-      __builtin_amdgcn_s_sleep(1);
+    raise_flag(sh.route_ready);
+  } else {
+    wait_flag(sh.route_ready);
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
-// Small regime: the first wave done with P1 waits for the shared barrier and
-// finishes the shared expert's h in LDS; the others wait for it.
-template <int AD>
-__device__ __forceinline__ void shared_h_small(KParams p, const Lds &L, int b_shared) {
-  SmemHead &sh = L.head();
-  int claimed = 0;
-  if (lane_id() == 0)
-    claimed = __hip_atomic_exchange(&sh.shared_claim, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
-  claimed = __builtin_amdgcn_readfirstlane(claimed);
-  if (claimed) {
-    bar_wait(p, sh, b_shared);
-    finish_shared_h_wave<AD>(p, L);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    if (lane_id() == 0) __hip_atomic_store(&sh.shared_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  } else if (lane_id() == 0) {
-    while (__hip_atomic_load(&sh.shared_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-      __builtin_amdgcn_s_sleep(1);
+  // P1: the expert gate/up rows (union slot, pair) in slot order, round-robin
+  // over the grid's waves; the rounds fall into nG groups, each closed by its
+  // barrier, so a slot is complete once the group of its last round is
+  const int I = p->I, N = sh.nU * I;
+  const int R1 = (N + NW - 1) / NW, nG = min(kP1Groups, R1);
+  for (int gi = 0; gi < nG; ++gi) {
+    for (int r = share_lo(R1, gi, nG); r < share_lo(R1, gi + 1, nG); ++r) {
+      const int q = W + r * NW;
+      if (q < N) expert_gu_task<AD, ED, true>(p, lp, L, q / I, q % I);
+    }
+    bar_arrive_published(p, sh, b0 + BAR_H + gi);
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+  // P2: the shared expert's rows first (input ready since P0), which fills the
+  // wait for the expert barrier, then the routed experts' rows and the combine
+  int sclaim = 0;
+  if (lane_id() == 0)
+    sclaim = __hip_atomic_exchange(&sh.shared_claim, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
+  sclaim = __builtin_amdgcn_readfirstlane(sclaim);
+  if (sclaim) {
+    bar_wait(p, sh, b0 + BAR_SHARED);
+    stage_shared_h_wave<AD>(p, L);
+    raise_flag(sh.shared_ready);
+  } else {
+    wait_flag(sh.shared_ready);
+  }
+  const int r0 = g * p->rows_per_wg;
+  const int r1 = min(p->H, r0 + p->rows_per_wg);
+  if (r0 < r1) shared_down_units<AD, SD, true>(p, lp, L, r0, r1, 0);
+  // the routed experts' rows, group by group: slots [ua, ub) end in group gi
+  int ua = 0;
+  for (int gi = 0; gi < nG; ++gi) {
+    const int rend = share_lo(R1, gi + 1, nG);
+    int ub = ua;
+    while (ub < sh.nU && ((ub + 1) * I - 1) / NW < rend) ++ub;
+    if (ub > ua) {
+      bar_wait(p, sh, b0 + BAR_H + gi);
+      if (r0 < r1) expert_down_units<AD, ED, true>(p, lp, L, r0, r1, 0, ua, ub, 2 + gi);
+    }
+    ua = ub;
+  }
+  __syncthreads();
+  if (r0 < r1) combine<AD, true>(p, lp, L, r0, r1);
+  __syncthreads();
 }
 
 template <int AD, int RD, int ED, int SD, bool SMALL>
@@ -1286,8 +1677,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
   // read the parameters in place in the kernarg segment (scalar loads; no private copy)
   (void)params;
   KParams p = (KParams)__builtin_amdgcn_kernarg_segment_ptr();
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  const Lds L{smem_raw};
+  const Lds L{};
   SmemHead &sh = L.head();
   const int tid = threadIdx.x, wv = wave_id();
   const int NW = p->G * kWaves;
@@ -1300,86 +1690,81 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
   for (int l = 0; l < p->L; ++l) {
     KLayer lp = &p->lp[l];
     const int b0 = kBarPerLayer * l;
+    for (int i = tid; i < kMaxRounds * kWaves; i += kThreads) (&sh.rcnt[0][0])[i] = (&sh.scnt[0][0])[i] = 0;
     if (tid == 0) {
       sh.route_claim = sh.route_ready = sh.shared_claim = sh.shared_ready = 0;
-      sh.unit_ctr[0] = sh.unit_ctr[1] = 0;
+      for (int i = 0; i < 2 + kP1Groups; ++i) sh.unit_ctr[i] = 0;
+      sh.task_ctr[0] = sh.task_ctr[1] = sh.task_ctr[2] = 0;
     }
     __syncthreads();
 
-    // x-hat
-    if constexpr (SMALL) {
-      stage_xhat<AD>(p, lp, L);
-    } else {
-      produce_xhat<AD>(p, lp, L);
-      bar_arrive(p, sh, b0 + BAR_XHAT);
-      bar_wait(p, sh, b0 + BAR_XHAT);
-    }
-
-    // P0: router slices, then shared gate/up
-    const int nrt = p->E * p->NSR;
-    int tau = W;
-    for (; tau < nrt; tau += NW) router_task<RD, SMALL>(p, lp, L, tau / p->NSR, tau % p->NSR);
-    if constexpr (SMALL) bar_arrive_published(p, sh, b0 + BAR_ROUTER);
-    else bar_arrive(p, sh, b0 + BAR_ROUTER);
     if (p->route_only) {
+      if constexpr (SMALL) {
+        stage_xhat<AD>(p, lp, L);
+      } else {
+        produce_xhat<AD>(p, lp, L);
+        bar_arrive(p, sh, b0 + BAR_XHAT);
+        bar_wait(p, sh, b0 + BAR_XHAT);
+      }
+      for (int tau = W, r = 0; tau < p->E * p->NSR; tau += NW, ++r) router_task<RD, SMALL>(p, lp, L, tau, r);
+      if constexpr (SMALL) bar_arrive_published(p, sh, b0 + BAR_ROUTER);
+      else bar_arrive(p, sh, b0 + BAR_ROUTER);
       bar_wait(p, sh, b0 + BAR_ROUTER);
       if (blockIdx.x == 0)
         for (int t = wv; t < p->B; t += kWaves) topk_token(p, lp, L, t, true);
       break;
     }
-    for (; tau < nrt + p->Is * p->NSS; tau += NW)
-      shared_gu_task<AD, SD, SMALL>(p, lp, L, (tau - nrt) / p->NSS, (tau - nrt) % p->NSS);
-    if constexpr (SMALL) bar_arrive_published(p, sh, b0 + BAR_SHARED);
-    else bar_arrive(p, sh, b0 + BAR_SHARED);
 
-    // P1: routing, gather tables, expert gate/up
     if constexpr (SMALL) {
-      route_small<true>(p, lp, L, b0 + BAR_ROUTER);
+      layer_small<AD, RD, ED, SD>(p, lp, L, b0, W, NW);
     } else {
+      // x-hat
+      produce_xhat<AD>(p, lp, L);
+      bar_arrive(p, sh, b0 + BAR_XHAT);
+      bar_wait(p, sh, b0 + BAR_XHAT);
+
+      // P0: router slices, then shared gate/up
+      p0_tasks<AD, RD, SD, false>(p, lp, L, b0);
+
+      // P1: routing (one wave per token), gather tables, expert gate/up. Each
+      // workgroup owns a contiguous share of the work in row units (an MFMA
+      // task is 16 rows, a GEMV task 1): the MFMA tasks of its share first,
+      // then its GEMV tasks, handed out to its waves through LDS counters.
       bar_wait(p, sh, b0 + BAR_ROUTER);
       for (int t = wv; t < p->B; t += kWaves) topk_token(p, lp, L, t, blockIdx.x == 0);
       __syncthreads();
       build_tables(p, L);
-    }
-    const int ntask = sh.nU * p->I;
-    for (int q = W; q < ntask; q += NW) expert_gu_task<AD, ED, SMALL>(p, lp, L, q / p->I, q % p->I);
-    if constexpr (SMALL) bar_arrive_published(p, sh, b0 + BAR_H);
-    else bar_arrive(p, sh, b0 + BAR_H);
-
-    // P2: this workgroup's output rows; the shared expert's rows first (their
-    // input is complete since P0), which fills the wait for the expert barrier
-    const int r0 = blockIdx.x * p->rows_per_wg;
-    const int r1 = min(p->H, r0 + p->rows_per_wg);
-    if constexpr (SMALL) {
-      shared_h_small<AD>(p, L, b0 + BAR_SHARED);
-      if (r0 < r1) shared_down_units<AD, SD, true>(p, lp, L, r0, r1, 0);
-      bar_wait(p, sh, b0 + BAR_H);
-      stage_h<AD>(p, L);
-      __syncthreads();
-      if (r0 < r1) expert_down_units<AD, ED, true>(p, lp, L, r0, r1, 0);
-      __syncthreads();
-      if (r0 < r1) combine<AD>(p, lp, L, r0, r1);
-      __syncthreads();
-    } else {
-      const bool one_pass = p->pass_rows >= p->rows_per_wg;
-      const int nsh = p->Is / p->I;
-      bar_wait(p, sh, b0 + BAR_SHARED);
-      if (one_pass && r0 < r1) shared_down_units<AD, SD, false>(p, lp, L, r0, r1, 0);
-      bar_wait(p, sh, b0 + BAR_H);
-      for (int pr0 = r0; pr0 < r1; pr0 += p->pass_rows) {
-        const int pr1 = min(r1, pr0 + p->pass_rows);
-        const int nrb = (pr1 - pr0) / kRowBlock;
-        if (!one_pass) shared_down_units<AD, SD, false>(p, lp, L, pr0, pr1, 0);
-        expert_down_units<AD, ED, false>(p, lp, L, pr0, pr1, one_pass ? 0 : nrb * nsh);
-        __syncthreads();
-        combine<AD>(p, lp, L, pr0, pr1);
-        __syncthreads();
+      classify_slots(p, L);
+      {
+        const int I = p->I, nb = I / 16, G = p->G, g = blockIdx.x;
+        const int nMU = sh.nM * I, C = (sh.nM + sh.nG) * I;
+        const int ca = share_lo(C, g, G), cz = share_lo(C, g + 1, G);
+        const int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
+        const int ma = (min(ca, nMU) + 15) / 16, mz = (min(cz, nMU) + 15) / 16;
+        for (int q = take(sh, 0, ma, mz); q >= 0; q = take(sh, 0, ma, mz))
+          mfma_gu_task<AD, ED>(p, lp, L, mslot[q / nb], q % nb);
+        const int ga = max(ca, nMU) - nMU, gz = max(cz, nMU) - nMU;
+        for (int q = take(sh, 1, ga, gz); q >= 0; q = take(sh, 1, ga, gz))
+          expert_gu_task<AD, ED, false>(p, lp, L, gslot[q / I], q % I);
       }
+      bar_arrive(p, sh, b0 + BAR_H);
+
+      // P2: this workgroup's output rows, partial sums in global memory; the
+      // shared expert's rows first, which fills the wait for the expert barrier
+      const int r0 = blockIdx.x * p->rows_per_wg;
+      const int r1 = min(p->H, r0 + p->rows_per_wg);
+      bar_wait(p, sh, b0 + BAR_SHARED);
+      if (r0 < r1) shared_down_units<AD, SD, false>(p, lp, L, r0, r1, 0);
+      bar_wait(p, sh, b0 + BAR_H);
+      if (r0 < r1) expert_down_units<AD, ED, false>(p, lp, L, r0, r1, 0);
+      __syncthreads();
+      if (r0 < r1) combine<AD, false>(p, lp, L, r0, r1);
+      __syncthreads();
     }
 
     if (l + 1 < p->L) {
       bar_arrive(p, sh, b0 + BAR_LAYER);
-      sink ^= prefetch_p0<RD, SD>(p, &p->lp[l + 1], W, NW);
+      sink ^= prefetch_p0<RD, SD>(p, &p->lp[l + 1]);
       bar_wait(p, sh, b0 + BAR_LAYER);
     }
   }
@@ -1473,7 +1858,7 @@ int k_slices(int hidden, moe_dtype dt, int most) {
 bool small_regime(int B) { return B <= kSmallB; }
 
 struct WsLayout {
-  size_t xhat, xa, rpart, hspart, hbuf, hsbuf, xbuf0, xbuf1, total;
+  size_t xhat, xa, rfin, hsh32, hbuf, hsbuf, partbuf, xbuf0, xbuf1, total;
 };
 
 size_t up256(size_t v) { return (v + 255u) & ~(size_t)255u; }
@@ -1485,10 +1870,12 @@ WsLayout ws_layout(const moe_layer_desc *d, int B, int L) {
   const size_t is = (size_t)(d->shared_inter > 0 ? d->shared_inter : 1);
   w.xhat = off; off += up256((size_t)B * d->hidden * 4);
   w.xa = off; off += up256((size_t)B * d->hidden * act);
-  w.rpart = off; off += up256((size_t)B * d->num_experts * 4 * 4);
-  w.hspart = off; off += up256((size_t)2 * B * 2 * is * 4);
-  w.hbuf = off; off += up256((size_t)B * d->top_k * d->expert_inter * 4);  // fp32 in the small regime
+  w.rfin = off; off += up256((size_t)B * d->num_experts * 4);
+  w.hsh32 = off; off += up256((size_t)B * is * 4);
+  w.hbuf = off; off += up256((size_t)B * d->top_k * d->expert_inter * act);
   w.hsbuf = off; off += up256((size_t)B * is * act);
+  const size_t pstride = (size_t)B * d->top_k + (size_t)B * (d->shared_inter / d->expert_inter);
+  w.partbuf = off; off += up256((size_t)d->hidden * pstride * 4);
   w.xbuf0 = off; off += (L > 1) ? up256((size_t)B * d->hidden * act) : 0;
   w.xbuf1 = off; off += (L > 2) ? up256((size_t)B * d->hidden * act) : 0;
   w.total = off;
@@ -1567,6 +1954,30 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   const bool small = small_regime(B);
   p.NSR = k_slices(d->hidden, d->router, 4);
   p.NSS = small && d->shared_inter > 0 ? k_slices(d->hidden, d->shared, 2) : 1;
+  // the slices of a row are one workgroup's waves of one round: the shared
+  // tasks start at a multiple of the workgroup's wave count, and the rounds
+  // must fit the per-round slice counters and LDS slots (else every row is
+  // one slice)
+  const int NW = p.G * kWaves;
+  int rounds = 0;
+  auto plan_slices = [&]() {
+    p.s0 = (p.E * p.NSR + kWaves - 1) / kWaves * kWaves;
+    p.slw = p.NSS > 1 ? 2 * B : B;
+    const int ntask = p.s0 + p.Is * p.NSS;
+    p.p0r = (ntask + NW - 1) / NW;
+    // last round: as few waves per workgroup as cover the tasks left, a
+    // multiple of the slice counts of the rows in that round
+    const int left = ntask - (p.p0r - 1) * NW;
+    const int unit = (p.p0r - 1) * NW >= p.E * p.NSR ? p.NSS : (p.NSR > p.NSS ? p.NSR : p.NSS);
+    p.p0w = ((left + p.G - 1) / p.G + unit - 1) / unit * unit;
+    if (p.p0w > kWaves) p.p0w = kWaves;
+    rounds = (p.NSR > 1 || p.NSS > 1) ? p.p0r : 0;
+  };
+  plan_slices();
+  if (rounds > kMaxRounds || (size_t)rounds * kWaves * p.slw * sizeof(float) > 16384) {
+    p.NSR = p.NSS = 1;
+    plan_slices();
+  }
   int rpw = (p.H + p.G - 1) / p.G;
   rpw = (rpw + kRowBlock - 1) / kRowBlock * kRowBlock;
   p.rows_per_wg = rpw;
@@ -1588,30 +1999,24 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     p.o_xf = (int)o; o = align16(o + (size_t)B * H * 4);
     p.o_xa = (int)o; o = align16(o + (d->act == MOE_F32 ? 0 : (size_t)B * H * act));
     p.o_hs = (int)o; o = align16(o + (size_t)B * (d->shared_inter > 0 ? d->shared_inter : 1) * act);
-    // expert h lands over x-hat once every P1 task is done (after the expert
-    // barrier), or after the other regions when it is the larger of the two
-    const size_t hbytes = (size_t)P * d->expert_inter * act;
-    if ((size_t)p.o_xf + hbytes <= (size_t)p.o_hs) {
-      p.o_h = p.o_xf;
-    } else {
-      p.o_h = (int)o; o = align16(o + hbytes);
-    }
   } else {
     p.o_cnt = (int)o; o = align16(o + (size_t)E * 4);
     p.o_start = (int)o; o = align16(o + (size_t)E * 4);
     p.o_tmask = (int)o; o = align16(o + (size_t)E * 8);
+    p.o_mslot = (int)o; o = align16(o + (size_t)nslot * 4);
+    p.o_gslot = (int)o; o = align16(o + (size_t)nslot * 4);
   }
+  p.o_slc = (int)o;
+  o = align16(o + (size_t)rounds * kWaves * p.slw * sizeof(float));
   p.o_part = (int)o;
+  // small regime: the workgroup's P2 partial sums stay in LDS (one pass over
+  // its rows); general regime: they go to the workspace
   const size_t per_row = (size_t)(P + B * nsh) * sizeof(float);
   const size_t lds_cap = (size_t)(di.max_lds > 0 ? di.max_lds : 65536);
-  if (o + (size_t)kRowBlock * per_row > lds_cap)
-    return fail(MOE_ERR_UNSUPPORTED, "shape needs more LDS than the device's %zu bytes", lds_cap);
-  int pr = (int)((lds_cap - o) / per_row);
-  pr = pr / kRowBlock * kRowBlock;
-  p.pass_rows = pr < rpw ? pr : rpw;
-  if (small && p.pass_rows < rpw)
-    return fail(MOE_ERR_UNSUPPORTED, "small-batch layout needs one LDS pass over %d rows", rpw);
-  const size_t lds = o + (size_t)p.pass_rows * per_row;
+  p.pass_rows = rpw;
+  const size_t lds = small ? o + (size_t)rpw * per_row : o;
+  if (lds > lds_cap) return fail(MOE_ERR_UNSUPPORTED, "shape needs more LDS than the device's %zu bytes", lds_cap);
+  p.use_mfma = (!small && d->expert != MOE_F32 && rpw >= 16) ? 1 : 0;
 
   p.timeout_ticks = 200000000LL;  // 2 s at 100 MHz
   // test hook: a tiny limit makes every barrier wait give up at once (no hang, no fault)
@@ -1620,10 +2025,11 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   p.ctrl = (unsigned *)wsb;
   p.xhat = (float *)(wsb + wl.xhat);
   p.xa = (d->act == MOE_F32) ? (void *)p.xhat : (void *)(wsb + wl.xa);
-  p.rpart = (float *)(wsb + wl.rpart);
-  p.hspart = (float *)(wsb + wl.hspart);
+  p.rfin = (float *)(wsb + wl.rfin);
+  p.hsh32 = (float *)(wsb + wl.hsh32);
   p.hbuf = wsb + wl.hbuf;
   p.hsbuf = wsb + wl.hsbuf;
+  p.partbuf = (float *)(wsb + wl.partbuf);
   p.xbuf[0] = wsb + wl.xbuf0;
   p.xbuf[1] = wsb + wl.xbuf1;
   for (int l = 0; l < L; ++l) {

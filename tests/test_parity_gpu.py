@@ -150,6 +150,24 @@ def test_small_bf16_random_gamma_zipf(dev):
         full_parity(w, B, dev, poison=True, random_gamma=True)
 
 
+@pytest.mark.parametrize("expert,router,seed", [(synth.BF16, synth.F32, 41), (synth.FP8, synth.BF16, 43)])
+def test_mfma_tiles_every_token(dev, expert, router, seed):
+    """B=64 over 16 experts (top-4): each expert gets ~16 tokens, so most run
+    through the MFMA tiles (experts with >= 16 tokens) and the rest through
+    the GEMV; H=4096 gives every workgroup >= 16 output rows, so the down
+    projection uses MFMA tiles too. Every token vs the oracle."""
+    w = small_workload(name="mfma", H=4096, E=16, k=4, I=256, Is=256, act=synth.BF16, router=router,
+                       expert=expert, shared=synth.BF16, seed=seed)
+    Lh = host_layer(w, experts=[])
+    x, _ = draw_tokens_with_margin(w, 64, [Lh])
+    idx_r, _, _ = oracle_routes(w, Lh, x)
+    counts = np.bincount(idx_r.ravel(), minlength=w.E)
+    log(f"mfma test: expert token counts {sorted(counts.tolist(), reverse=True)}")
+    assert np.sum(counts >= 16) >= 4  # the MFMA path is exercised
+    err = full_parity(w, 64, dev, poison=True)
+    log(f"mfma tiles ({expert}) max rel err {err:.2e}")
+
+
 def test_k3_b1(dev):
     err = full_parity(synth.WORKLOADS["k3_b1"], 1, dev, poison=True)
     log(f"k3_b1 max rel err {err:.2e}")
