@@ -134,6 +134,21 @@ def stream_probe(torch, md, dev, stream, gib=4, reps=5):
     return best
 
 
+def calibration_copy(torch, md, dev, stream):
+    """One plain copy of a known size (1 GiB), whose FETCH_SIZE / WRITE_SIZE
+    counters calibrate those of the decode kernel in a --pmc profile."""
+    from moe_decode_02_amd.profiling import COPY_BYTES
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(3)
+    grid = torch.cuda.get_device_properties(dev).multi_processor_count * 16
+    rc = md.probe_lib().moe_probe_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, grid, stream.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"moe_probe_copy failed: hip error {rc}")
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -257,6 +272,7 @@ def main() -> int:
         f"single-launch median {np.median(lat):.1f} p95 {np.percentile(lat, 95):.1f} min {lat.min():.1f} us, "
         f"{nbytes / 1e6:.1f} MB/step -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
 
+    calibration_copy(torch, md, dev, stream)
     probe = stream_probe(torch, md, dev, stream)
     log(f"bench: streaming-read probe {probe:.0f} GB/s ({probe / HBM_PEAK_GBS:.1%} of 8 TB/s); "
         f"the step reaches {gbs / probe:.1%} of it")
@@ -265,6 +281,13 @@ def main() -> int:
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, B, args.cpu_seconds)
         log(f"bench: cpu baseline {cpu}")
+
+    # HBM bytes per launch measured by the committed FETCH_SIZE / WRITE_SIZE
+    # profile of this workload, if it was taken on the current kernel source
+    from moe_decode_02_amd.profiling import read_traffic
+    tr = read_traffic(os.path.join(ROOT, "profiles", f"moe_kernel_{w.name}_B{B}_traffic.txt"))
+    hbm_bytes = None if tr is None else tr["read"] + tr["write"]
+    traffic = None if tr is None else hbm_bytes / (ms_step * 1e-3) / 1e9
 
     out = {
         "metric": "MoE decode layer us/step + tok/s (B=1-64); achieved HBM GB/s vs peak",
@@ -285,8 +308,8 @@ def main() -> int:
         "config": {"workload": f"{w.name}: {WORKLOAD_NOTES[w.name]}", "batch": B, "layers": L,
                    "rotated_instances": C, "kernel_launches_per_step": 1},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "algorithmic_bytes_per_launch": nbytes},
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": nbytes, "hbm_bytes_per_launch": hbm_bytes},
         "cpu_baseline": cpu,
         "stream_probe_GBs": probe,
     }
