@@ -72,7 +72,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxL = 8;
 constexpr int kTokGroup = 4;    // tokens whose partial sums a lane holds at once
 constexpr int kRowBlock = 4;    // down-projection rows per unit
-constexpr int kSmallB = 2;      // B <= kSmallB: x-hat and h staged in each workgroup's LDS
+constexpr int kSmallB = 2;      // B <= kSmallB: the small regime (x-hat in every workgroup's LDS)
 constexpr int kMaxRounds = 32;  // rounds of P0 slices over the grid's waves
 
 // expert barriers of the small regime: P1's rounds fall into up to kP1Groups
@@ -84,6 +84,9 @@ constexpr int kMaxBarriers = kBarPerLayer * kMaxL;
 constexpr int kCtrlStride = 16;  // words: each control word on its own 64-byte line
 enum : int { CTRL_DONE = 0, CTRL_ERR = 1, CTRL_BAR = 2 };
 constexpr size_t kCtrlBytes = (size_t)(CTRL_BAR + kMaxBarriers) * kCtrlStride * sizeof(unsigned);
+// small-regime logit buffers (two layer parities), right after the control words
+constexpr size_t kRlogOffset = (kCtrlBytes + 255u) & ~(size_t)255u;
+constexpr size_t kRlogBytes = (size_t)2 * kSmallB * kMaxE * sizeof(float);
 
 struct LayerPtrs {
   const void *x;          // layer input [B][H] (act)
@@ -100,6 +103,7 @@ struct LayerPtrs {
   int32_t *idx_out;       // [B][k] or null
   float *w_out;           // [B][k] or null
   float *logits_out;      // [B][E] or null (route mode)
+  float *lg;              // [B][E] router logits of this layer (see Params::rfin, Params::rlog)
 };
 
 struct Params {
@@ -119,7 +123,9 @@ struct Params {
   unsigned *ctrl;         // control words, kCtrlStride apart
   float *xhat;            // [B][H] fp32 (general regime)
   void *xa;               // [B][H] act (general regime; == xhat for fp32 activations)
-  float *rfin;            // [B][E]: the logits (slices summed in order by the last slice's wave)
+  float *rfin;            // [B][E]: the logits, general regime and route mode
+  float *rlog;            // [2][kSmallB][E]: small-regime logits by layer parity, all-zero bits while
+                          // unwritten (a written logit is never +0: +0 is stored as -0)
   float *hsh32;           // [B][Is]: the shared h, act-rounded, as fp32 (small regime)
   void *hbuf;             // [B*k][I] act
   void *hsbuf;             // [B][Is] act (general regime)
@@ -425,8 +431,14 @@ template <int WD, int TG> constexpr int seg_gu() { return kLoadsPerStep >= 4 ? k
 // rows of a 4-row down unit handled per pass, and chunks per step
 constexpr int kDownRows = kLoadsPerStep >= 4 ? 4 : kLoadsPerStep >= 2 ? 2 : 1;
 template <int WD, int TG> constexpr int seg_down() { return kLoadsPerStep / kDownRows > 0 ? kLoadsPerStep / kDownRows : 1; }
-// chunks per step of a router row slice
-template <int WD, int TG> constexpr int seg_router() { return kLoadsPerStep; }
+// P0 (router and shared gate/up slices): loads per step
+#ifndef MOE_P0_LOADS_PER_STEP
+#define MOE_P0_LOADS_PER_STEP MOE_LOADS_PER_STEP
+#endif
+constexpr int kP0LoadsPerStep = MOE_P0_LOADS_PER_STEP;
+// chunks per step of a router row slice, of a shared gate/up pair's slice
+template <int WD, int TG> constexpr int seg_router() { return kP0LoadsPerStep; }
+template <int WD, int TG> constexpr int seg_p0gu() { return kP0LoadsPerStep >= 4 ? kP0LoadsPerStep / 2 : 1; }
 
 // Run f.template operator()<TG>(t0, nt) over groups of up to kTokGroup of n
 // tokens, with the smallest specialisation that holds each group.
@@ -451,6 +463,10 @@ __device__ __forceinline__ unsigned *ctrl_word(KParams p, int w) { return p->ctr
 // with device-coherent stores (write-through past this XCD's L2), so the
 // barrier does not need an L2 write-back, which costs several microseconds
 // per workgroup while the memory system is streaming.
+// +0 as -0 (equal in every comparison and product), so that all-zero bits
+// can mark a value not yet written
+__device__ __forceinline__ float nonzero_bits(float v) { return __float_as_uint(v) == 0u ? -0.0f : v; }
+
 __device__ __forceinline__ void publish(float *q, float v) {
   __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -698,6 +714,7 @@ __device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, 
   const int e = tau / NSR, s = tau % NSR;
   const int Ks = H / NSR;
   const char *const wrow[1] = {(const char *)lp->rw + (size_t)e * H * dsz<RD>()};
+  const float bias = lp->rb ? lp->rb[e] : 0.f;  // added to the finished fp32 dot product
   for_token_groups(B, [&]<int TG>(int t0, int nt) {
     typename XSrc<XL>::ptr xr[TG];
 #pragma unroll
@@ -711,8 +728,8 @@ __device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, 
       const float v = wave_sum63(acc[0][t]);
       if (t < nt && lane_id() == 63) {
         if (NSR == 1) {
-          if constexpr (XL) publish(p->rfin + (size_t)(t0 + t) * E + e, v);
-          else p->rfin[(size_t)(t0 + t) * E + e] = v;
+          if constexpr (XL) publish(lp->lg + (size_t)(t0 + t) * E + e, nonzero_bits(v + bias));
+          else lp->lg[(size_t)(t0 + t) * E + e] = v + bias;
         } else {
           slice_slot(p, L, round, wave_id())[t0 + t] = v;
         }
@@ -724,8 +741,8 @@ __device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, 
     for (int t = lane_id(); t < B; t += 64) {
       float sum = slice_slot(p, L, round, w0)[t];
       for (int s2 = 1; s2 < NSR; ++s2) sum += slice_slot(p, L, round, w0 + s2)[t];
-      if constexpr (XL) publish(p->rfin + (size_t)t * E + e, sum);
-      else p->rfin[(size_t)t * E + e] = sum;
+      if constexpr (XL) publish(lp->lg + (size_t)t * E + e, nonzero_bits(sum + bias));
+      else lp->lg[(size_t)t * E + e] = sum + bias;
     }
   }
 }
@@ -748,7 +765,7 @@ __device__ __forceinline__ void shared_gu_task(KParams p, KLayer lp, const Lds &
     float acc[2][TG];
 #pragma unroll
     for (int t = 0; t < TG; ++t) acc[0][t] = acc[1][t] = 0.f;
-    rows_dot<SD, AD, XL, 2, seg_gu<SD, TG>(), TG>(wrow, s * Ks, (s + 1) * Ks, xr, acc);
+    rows_dot<SD, AD, XL, 2, seg_p0gu<SD, TG>(), TG>(wrow, s * Ks, (s + 1) * Ks, xr, acc);
 #pragma unroll
     for (int t = 0; t < TG; ++t) {
       const float g = wave_sum63(acc[0][t]);
@@ -796,6 +813,11 @@ __device__ __forceinline__ void shared_gu_task(KParams p, KLayer lp, const Lds &
 // logits tie at the threshold, a 64-round-free fallback runs k rounds of
 // wave argmax instead.
 
+// number of set bits of m in the lanes below this one
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+}
+
 // float -> unsigned with the same order (-0 and +0 are made equal first)
 __device__ __forceinline__ unsigned ord_f32(float v) {
   const unsigned u = __float_as_uint(v + 0.0f);
@@ -814,31 +836,58 @@ __device__ __forceinline__ float ld_off(const float *base, unsigned i) {
   return *(const float *)((const char *)base + i * 4u);
 }
 
+// POLL (small regime): the logits are read device-coherently until none of
+// this token's is still unwritten (all-zero bits); this wait replaces a grid
+// barrier, so the data arrive with the same round trip that observes them.
+template <bool POLL>
 __device__ __forceinline__ void load_logits(KParams p, KLayer lp, int t, float (&v)[kMaxE / 64]) {
   const int lane = lane_id(), E = p->E;
   constexpr int PER = kMaxE / 64;
-  const float *base = p->rfin + (size_t)t * E;
+  static_assert(PER == 16, "the polled load's wait lists 16 values");
+  const float *base = lp->lg + (size_t)t * E;
+  if constexpr (!POLL) {
 #pragma unroll
-  for (int j = 0; j < PER; ++j) v[j] = ld_off(base, (unsigned)min(lane + 64 * j, E - 1));
-  if (const float *rb = lp->rb) {
-    float b[PER];
+    for (int j = 0; j < PER; ++j) v[j] = ld_off(base, (unsigned)min(lane + 64 * j, E - 1));
+  } else {
+    const long long t0 = rt_now();
+    for (;;) {
+      // device-coherent (sc1) loads with a scalar base and 32-bit offsets;
+      // the wait names every result, so nothing reads them before they land
 #pragma unroll
-    for (int j = 0; j < PER; ++j) b[j] = ld_off(rb, (unsigned)min(lane + 64 * j, E - 1));
+      for (int j = 0; j < PER; ++j) {
+        const unsigned off = (unsigned)min(lane + 64 * j, E - 1) * 4u;
+        asm volatile("global_load_dword %0, %1, %2 sc1" : "=v"(v[j]) : "v"(off), "s"(base) : "memory");
+      }
+      asm volatile("s_waitcnt vmcnt(0)"
+                   : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),
+                     "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]),
+                     "+v"(v[15])
+                   :
+                   : "memory");
+      bool missing = false;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) v[j] += b[j];
+      for (int j = 0; j < PER; ++j) missing |= __float_as_uint(v[j]) == 0u;
+      if (__ballot(missing) == 0ull) break;
+      if (rt_now() - t0 > p->timeout_ticks) {
+        if (lane == 0) __hip_atomic_store(ctrl_word(p, CTRL_ERR), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
   }
 }
 
 // Rare path (more than 64 logits tie at the threshold): k rounds of wave
 // argmax over all logits. Returns the selection in lanes < k.
-__device__ __attribute__((noinline)) void topk_rounds(KParams p_arg, KLayer lp_arg, int t_arg, float &myv, int &myidx) {
+template <bool POLL>
+__device__ __forceinline__ void topk_rounds(KParams p_arg, KLayer lp_arg, int t_arg, float &myv, int &myidx) {
   const KParams p = uni(p_arg);
   const KLayer lp = uni(lp_arg);
   const int t = uni(t_arg);
   const int lane = lane_id(), E = p->E, k = p->k;
   constexpr int PER = kMaxE / 64;
   float v[PER];
-  load_logits(p, lp, t, v);
+  load_logits<POLL>(p, lp, t, v);
   const float qnan = __builtin_nanf("");
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
@@ -861,6 +910,7 @@ __device__ __attribute__((noinline)) void topk_rounds(KParams p_arg, KLayer lp_a
   }
 }
 
+template <bool POLL>
 __device__ __attribute__((noinline)) void topk_token(KParams p_arg, KLayer lp_arg, const Lds &L, int t_arg, bool write_out_arg) {
   const KParams p = uni(p_arg);
   const KLayer lp = uni(lp_arg);
@@ -869,36 +919,43 @@ __device__ __attribute__((noinline)) void topk_token(KParams p_arg, KLayer lp_ar
   const int lane = lane_id();
   const int E = p->E, k = p->k;
   constexpr int PER = kMaxE / 64;
-  float v[PER];
-  load_logits(p, lp, t, v);
+  // order keys of the logits: a NaN logit ranks last but stays selectable; a
+  // slot past E gets key 0, below every expert's (so it is never a candidate)
   unsigned o[PER];
+  {
+    float v[PER];
+    load_logits<POLL>(p, lp, t, v);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) o[j] = lane + 64 * j < E ? ord_f32((v[j] == v[j]) ? v[j] : -INFINITY) : 0u;
+  }
+  if (write_out && lp->logits_out) {
+    float *lo = lp->logits_out + (size_t)t * E;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (lane + 64 * j < E) lo[lane + 64 * j] = unord_f32(o[j]);
+  }
   unsigned omax = 0;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int e = lane + 64 * j;
-    // a NaN logit ranks last but stays selectable; a slot past E ranks below every expert
-    if (e < E) v[j] = (v[j] == v[j]) ? v[j] : -INFINITY;
-    if (write_out && lp->logits_out && e < E) lp->logits_out[(size_t)t * E + e] = v[j];
-    o[j] = e < E ? ord_f32(v[j]) : 0u;
-    omax = max(omax, o[j]);
-  }
+  for (int j = 0; j < PER; ++j) omax = max(omax, o[j]);
   // T = k-th largest lane maximum (largest T with at least k lanes >= T)
   unsigned thr = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const unsigned c = thr | (1u << bit);
     if (__popcll(__ballot(omax >= c)) >= k) thr = c;
   }
+  // thr >= the key of -inf > 0: at least k lanes hold an expert
   int nc = 0;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) nc += (lane + 64 * j < E && o[j] >= thr) ? 1 : 0;
-  // exclusive prefix of the candidate counts over the lanes
-  int incl = nc;
+  for (int j = 0; j < PER; ++j) nc += o[j] >= thr ? 1 : 0;
+  // exclusive prefix of the candidate counts over the lanes, from ballots of
+  // their bits (nc <= PER < 32)
+  int pre = 0, total = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int up = __shfl_up(incl, d);
-    if (lane >= d) incl += up;
+  for (int b = 0; b < 5; ++b) {
+    const unsigned long long m = __ballot((nc >> b) & 1);
+    pre += lanes_below(m) << b;
+    total += __popcll(m) << b;
   }
-  const int total = __shfl(incl, 63);
   int *sel_idx = L.at<int>(p->o_sel_idx);
   float *sel_w = L.at<float>(p->o_sel_w);
   int myidx = 0;
@@ -906,22 +963,23 @@ __device__ __attribute__((noinline)) void topk_token(KParams p_arg, KLayer lp_ar
   if (total <= kMaxCand) {
     unsigned *ck = L.head().cand_key[wave_id()];
     int *ci = L.head().cand_idx[wave_id()];
-    int pos = incl - nc;
+    int pos = pre;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && o[j] >= thr) { ck[pos] = o[j]; ci[pos] = e; ++pos; }
-    }
+    for (int j = 0; j < PER; ++j)
+      if (o[j] >= thr) { ck[pos] = o[j]; ci[pos] = lane + 64 * j; ++pos; }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    // one candidate per lane; each is ranked against the others read back
+    // from lane c through the scalar unit (no LDS round trip per candidate)
+    const unsigned mk = lane < total ? ck[lane] : 0u;
+    const int me = lane < total ? ci[lane] : 0x7FFFFFFF;
+    int rank = 0;
+#pragma unroll 4
+    for (int c = 0; c < total; ++c) {
+      const unsigned ok = (unsigned)__builtin_amdgcn_readlane((int)mk, c);
+      const int oe = __builtin_amdgcn_readlane(me, c);
+      rank += (ok > mk || (ok == mk && oe < me)) ? 1 : 0;
+    }
     if (lane < total) {
-      const unsigned mk = ck[lane];
-      const int me = ci[lane];
-      int rank = 0;
-      for (int c = 0; c < total; ++c) {
-        const unsigned ok = ck[c];
-        const int oe = ci[c];
-        rank += (ok > mk || (ok == mk && oe < me)) ? 1 : 0;
-      }
       if (rank < k) {
         ck[kMaxCand + rank] = mk;
         ci[kMaxCand + rank] = me;
@@ -934,7 +992,7 @@ __device__ __attribute__((noinline)) void topk_token(KParams p_arg, KLayer lp_ar
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
   } else {
-    topk_rounds(p, lp, t, myv, myidx);
+    topk_rounds<POLL>(p, lp, t, myv, myidx);
   }
   // renormalised softmax over the selection (the denominator over all E cancels)
   const bool mine = lane < k;
@@ -1009,37 +1067,38 @@ __device__ __attribute__((noinline)) void build_tables(KParams p_arg, const Lds 
 }
 
 // The same tables built by one wave when B*k <= 64: the (expert, pair) keys
-// are sorted across the lanes (bitonic), then each run of equal experts is a
-// union slot. Pairs of one expert keep ascending order, hence ascending tokens.
+// are distinct, so each key's rank (read lane by lane through the scalar
+// unit) is its sorted position; the sorted keys go through LDS, and each run
+// of equal experts is a union slot. Pairs of one expert keep ascending order,
+// hence ascending tokens.
 __device__ __attribute__((noinline)) void build_tables_wave(KParams p_arg, const Lds &L) {
   const KParams p = uni(p_arg);
   const int lane = lane_id(), P = p->B * p->k;
   const int *sel_idx = L.at<int>(p->o_sel_idx);
   int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   int *plist = L.at<int>(p->o_plist);
-  unsigned key = lane < P ? ((unsigned)sel_idx[lane] << 6) | (unsigned)lane : 0xFFFFFFFFu;
-#pragma unroll
-  for (int kk = 2; kk <= 64; kk <<= 1)
-#pragma unroll
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      const unsigned o = (unsigned)__shfl_xor((int)key, j);
-      const bool asc = (lane & kk) == 0, low = (lane & j) == 0;
-      key = (asc == low) ? min(key, o) : max(key, o);
-    }
+  unsigned *sorted = L.head().cand_key[wave_id()];
   const bool valid = lane < P;
-  const unsigned prev = (unsigned)__shfl_up((int)key, 1);
-  const bool first = valid && (lane == 0 || (prev >> 6) != (key >> 6));
+  const unsigned key = valid ? ((unsigned)sel_idx[lane] << 6) | (unsigned)lane : 0xFFFFFFFFu;
+  int rank = 0;
+  for (int c = 0; c < P; ++c) rank += ((unsigned)__builtin_amdgcn_readlane((int)key, c) < key) ? 1 : 0;
+  if (valid) sorted[rank] = key;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  const unsigned k2 = valid ? sorted[lane] : 0xFFFFFFFFu;
+  const unsigned prev = (valid && lane > 0) ? sorted[lane - 1] : 0xFFFFFFFFu;
+  const bool first = valid && (lane == 0 || (prev >> 6) != (k2 >> 6));
   const unsigned long long firsts = __ballot(first);
-  if (valid) plist[lane] = (int)(key & 63u);
+  if (valid) plist[lane] = (int)(k2 & 63u);
   if (first) {
-    const int rank = __popcll(firsts & ((1ull << lane) - 1ull));
+    const int slot = lanes_below(firsts);
     const unsigned long long rest = lane < 63 ? firsts >> (lane + 1) : 0ull;
     const int nxt = rest ? lane + __ffsll((long long)rest) : P;
-    ulist[rank] = (int)(key >> 6);
-    ustart[rank] = lane;
-    ucnt[rank] = nxt - lane;
+    ulist[slot] = (int)(k2 >> 6);
+    ustart[slot] = lane;
+    ucnt[slot] = nxt - lane;
   }
   if (lane == 0) L.head().nU = __popcll(firsts);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
 }
 
 // ---------------------------------------------------------------------------
@@ -1567,7 +1626,8 @@ __device__ __forceinline__ void wait_flag(int &f) {
 
 // P0 of this wave: its router slices, arrival at the router barrier, its
 // shared gate/up slices, arrival at the shared barrier. PUB: the small
-// regime's published stores and arrivals.
+// regime's published stores and arrivals; there the routing waves poll the
+// logits themselves and no router barrier is kept.
 template <int AD, int RD, int SD, bool PUB>
 __device__ __forceinline__ void p0_tasks(KParams p, KLayer lp, const Lds &L, int b0) {
   SmemHead &sh = L.head();
@@ -1577,15 +1637,13 @@ __device__ __forceinline__ void p0_tasks(KParams p, KLayer lp, const Lds &L, int
     const int tau = p0_task(p, r, blockIdx.x, wave_id());
     if (tau < 0 || tau >= end) break;
     if (tau >= nrt && !routed) {
-      if constexpr (PUB) bar_arrive_published(p, sh, b0 + BAR_ROUTER);
-      else bar_arrive(p, sh, b0 + BAR_ROUTER);
+      if constexpr (!PUB) bar_arrive(p, sh, b0 + BAR_ROUTER);
       routed = true;
     }
     if (tau < nrt) router_task<RD, PUB>(p, lp, L, tau, r);
     else if (tau >= s0) shared_gu_task<AD, SD, PUB>(p, lp, L, tau - s0, r);
   }
   if constexpr (PUB) {
-    if (!routed) bar_arrive_published(p, sh, b0 + BAR_ROUTER);
     bar_arrive_published(p, sh, b0 + BAR_SHARED);
   } else {
     if (!routed) bar_arrive(p, sh, b0 + BAR_ROUTER);
@@ -1617,8 +1675,7 @@ __device__ __forceinline__ void layer_small(KParams p, KLayer lp, const Lds &L, 
     claimed = __hip_atomic_exchange(&sh.route_claim, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
   claimed = __builtin_amdgcn_readfirstlane(claimed);
   if (claimed) {
-    bar_wait(p, sh, b0 + BAR_ROUTER);
-    for (int t = 0; t < p->B; ++t) topk_token(p, lp, L, t, blockIdx.x == 0);
+    for (int t = 0; t < p->B; ++t) topk_token<true>(p, lp, L, t, blockIdx.x == 0);
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
     build_tables_wave(p, L);
     raise_flag(sh.route_ready);
@@ -1667,6 +1724,14 @@ __device__ __forceinline__ void layer_small(KParams p, KLayer lp, const Lds &L, 
     }
     ua = ub;
   }
+  // every workgroup is past its routing (all arrived at the last expert
+  // barrier): clear this workgroup's share of the layer's logits for the next
+  // use of the buffer (the stores complete before the layer barrier or the
+  // end of the launch)
+  if (wave_id() == 0) {
+    const int n = p->B * p->E;
+    for (int i = share_lo(n, g, G) + lane_id(); i < share_lo(n, g + 1, G); i += 64) publish(lp->lg + i, 0.f);
+  }
   __syncthreads();
   if (r0 < r1) combine<AD, true>(p, lp, L, r0, r1);
   __syncthreads();
@@ -1711,7 +1776,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       else bar_arrive(p, sh, b0 + BAR_ROUTER);
       bar_wait(p, sh, b0 + BAR_ROUTER);
       if (blockIdx.x == 0)
-        for (int t = wv; t < p->B; t += kWaves) topk_token(p, lp, L, t, true);
+        for (int t = wv; t < p->B; t += kWaves) topk_token<false>(p, lp, L, t, true);
       break;
     }
 
@@ -1731,7 +1796,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       // task is 16 rows, a GEMV task 1): the MFMA tasks of its share first,
       // then its GEMV tasks, handed out to its waves through LDS counters.
       bar_wait(p, sh, b0 + BAR_ROUTER);
-      for (int t = wv; t < p->B; t += kWaves) topk_token(p, lp, L, t, blockIdx.x == 0);
+      for (int t = wv; t < p->B; t += kWaves) topk_token<false>(p, lp, L, t, blockIdx.x == 0);
       __syncthreads();
       build_tables(p, L);
       classify_slots(p, L);
@@ -1858,14 +1923,15 @@ int k_slices(int hidden, moe_dtype dt, int most) {
 bool small_regime(int B) { return B <= kSmallB; }
 
 struct WsLayout {
-  size_t xhat, xa, rfin, hsh32, hbuf, hsbuf, partbuf, xbuf0, xbuf1, total;
+  size_t rlog, xhat, xa, rfin, hsh32, hbuf, hsbuf, partbuf, xbuf0, xbuf1, total;
 };
 
 size_t up256(size_t v) { return (v + 255u) & ~(size_t)255u; }
 
 WsLayout ws_layout(const moe_layer_desc *d, int B, int L) {
   WsLayout w{};
-  size_t off = up256(kCtrlBytes);
+  w.rlog = kRlogOffset;
+  size_t off = up256(kRlogOffset + kRlogBytes);
   const size_t act = (size_t)dsize(d->act);
   const size_t is = (size_t)(d->shared_inter > 0 ? d->shared_inter : 1);
   w.xhat = off; off += up256((size_t)B * d->hidden * 4);
@@ -2026,6 +2092,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   p.xhat = (float *)(wsb + wl.xhat);
   p.xa = (d->act == MOE_F32) ? (void *)p.xhat : (void *)(wsb + wl.xa);
   p.rfin = (float *)(wsb + wl.rfin);
+  p.rlog = (float *)(wsb + wl.rlog);
   p.hsh32 = (float *)(wsb + wl.hsh32);
   p.hbuf = wsb + wl.hbuf;
   p.hsbuf = wsb + wl.hsbuf;
@@ -2044,6 +2111,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     lp.idx_out = idx ? idx + (size_t)l * B * d->top_k : nullptr;
     lp.w_out = wts ? wts + (size_t)l * B * d->top_k : nullptr;
     lp.logits_out = logits;
+    lp.lg = (small && !route_only) ? p.rlog + (size_t)(l & 1) * kSmallB * d->num_experts : p.rfin;
   }
   kernel_fn fn = pick_kernel(d, small);
   if (hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
@@ -2096,6 +2164,10 @@ moe_status moe_check_workspace(void *ws, size_t ws_bytes, void *stream) {
     const unsigned zero = 0;
     if (hipMemcpy(word, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess)
       return fail(MOE_ERR_DEVICE, "clearing the error word failed");
+    // a stopped launch may have left small-batch logits behind: clear them
+    if (ws_bytes >= kRlogOffset + kRlogBytes &&
+        hipMemset((unsigned char *)ws + kRlogOffset, 0, kRlogBytes) != hipSuccess)
+      return fail(MOE_ERR_DEVICE, "clearing the logit buffers failed");
     return fail(MOE_ERR_TIMEOUT, "a launch on this workspace stopped at its barrier watchdog");
   }
   return MOE_OK;
