@@ -39,9 +39,12 @@
  *     [E][H][I]; shared gate/up [2Is][H]; shared down [H][Is].
  *   - All device pointers must be 16-byte aligned.
  *   - The workspace must be zero-filled by the caller once, before the first
- *     call that uses it; the library leaves it reusable (its barrier counters
- *     are generation-based). Calls that share one workspace must not overlap
- *     in time (enqueue them on one stream).
+ *     call that uses it; every call leaves it as it found it (barrier and
+ *     work counters back at zero, the small-batch logit buffers cleared), so
+ *     it is reusable across calls, batch sizes and layer counts. After a
+ *     watchdog stop (MOE_ERR_TIMEOUT from moe_check_workspace, which also
+ *     restores that state) no other repair is needed. Calls that share one
+ *     workspace must not overlap in time (enqueue them on one stream).
  *   - y may be exactly x (in place); any other overlap between inputs and
  *     outputs is an error.
  *   - Routing outputs list each token's k experts by descending logit, ties
@@ -133,8 +136,11 @@ moe_status moe_decode_stack(const moe_layer_desc *desc, const moe_layer_weights 
                             void *ws, size_t ws_bytes, void *stream);
 
 /* Synchronises `stream`, then reads and clears the workspace's error word:
- * MOE_ERR_TIMEOUT if a launch on this workspace stopped at its barrier
- * watchdog, MOE_OK otherwise. A debugging aid, not for the hot path. */
+ * MOE_ERR_TIMEOUT if a launch on this workspace stopped at a watchdog (a grid
+ * barrier or the small-batch logit wait gave up after 2 s), MOE_OK otherwise.
+ * On MOE_ERR_TIMEOUT it also clears the small-batch logit buffers that the
+ * stopped launch may have left written. A debugging aid, not for the hot
+ * path. */
 moe_status moe_check_workspace(void *ws, size_t ws_bytes, void *stream);
 
 /* Static English name of a status. */
