@@ -111,7 +111,7 @@ struct Params {
   int route_only;
   int use_mfma;           // general regime: experts with >= kMfmaMin tokens go through MFMA tiles
   int NSR;                // router K-slices
-  int NSS;                // shared gate/up K-slices (small regime), else 1
+  int NSS;                // shared gate/up K-slices
   int s0;                 // first P0 task index of the shared slices (a multiple of the wave count of a workgroup)
   int slw;                // floats per wave and round in the LDS slice slots (B, or 2B with shared slices)
   int p0r, p0w;           // P0 rounds; waves per workgroup that take a task in the last round
@@ -137,6 +137,7 @@ struct Params {
   int o_plist;                      // (token, rank) pairs grouped by expert [B*k]
   int o_cnt, o_start, o_tmask;      // per-expert scratch of the workgroup-wide table build [E]
   int o_mslot, o_gslot;             // general regime: union slots on MFMA tiles / on GEMV [min(E, B*k)]
+  int o_cpre;                       // general regime: P1 cost before each listed slot [min(E, B*k) + 1]
   int o_xf, o_xa;                   // small regime: x-hat fp32 / act [B][H]
   int o_hs;                         // small regime: shared h [B][Is] (act)
   int o_slc;                        // slice sums of P0 tasks [round][wave][slw]
@@ -491,8 +492,11 @@ __device__ void bar_arrive_published(KParams p, SmemHead &sh, int b) {
   }
 }
 
-// A wave is done with the work barrier b waits for.
+// A wave is done with the work barrier b waits for. Each wave first waits for
+// its own stores to reach the L2 (a workgroup-scope release does not wait for
+// them), so the last wave's L2 write-back covers every wave's stores.
 __device__ void bar_arrive(KParams p, SmemHead &sh, int b) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   if (lane_id() == 0) {
     const int old = __hip_atomic_fetch_add(&sh.bar_cnt[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -747,10 +751,17 @@ __device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, 
   }
 }
 
-// shared gate/up task tau = (pair j, slice s) of round `round`. One slice
-// (general regime): h of every token straight to hsbuf (act dtype). Several
-// slices (small regime): slice sums to the LDS slot, and the last slice's wave
-// publishes h, act-rounded, as fp32 to hsh32.
+// the shared expert's h for (token, pair) index i
+template <int AD, bool XL>
+__device__ __forceinline__ void shared_h_out(KParams p, size_t i, float h) {
+  if constexpr (XL) publish(p->hsh32 + i, round_act<AD>(h));
+  else store_act<AD>(p->hsbuf, i, h);
+}
+
+// shared gate/up task tau = (pair j, slice s) of round `round`. Several
+// slices: slice sums to the LDS slot, and the last slice's wave finishes h.
+// h goes to hsh32 as act-rounded fp32, published (small regime), or to hsbuf
+// in the act dtype (general regime).
 template <int AD, int SD, bool XL>
 __device__ __forceinline__ void shared_gu_task(KParams p, KLayer lp, const Lds &L, int tau, int round) {
   const int H = p->H, B = p->B, Is = p->Is, NSS = p->NSS;
@@ -771,31 +782,25 @@ __device__ __forceinline__ void shared_gu_task(KParams p, KLayer lp, const Lds &
       const float g = wave_sum63(acc[0][t]);
       const float u = wave_sum63(acc[1][t]);
       if (t < nt && lane_id() == 63) {
-        if constexpr (XL) {
-          if (NSS == 1) {
-            publish(p->hsh32 + (size_t)(t0 + t) * Is + j, round_act<AD>(silu_mul(g, u)));
-          } else {
-            float *q = slice_slot(p, L, round, wave_id()) + 2 * (t0 + t);
-            q[0] = g;
-            q[1] = u;
-          }
+        if (NSS == 1) {
+          shared_h_out<AD, XL>(p, (size_t)(t0 + t) * Is + j, silu_mul(g, u));
         } else {
-          store_act<AD>(p->hsbuf, (size_t)(t0 + t) * Is + j, silu_mul(g, u));
+          float *q = slice_slot(p, L, round, wave_id()) + 2 * (t0 + t);
+          q[0] = g;
+          q[1] = u;
         }
       }
     }
   });
-  if constexpr (XL) {
-    if (NSS > 1 && last_slice(L.head().scnt, round, NSS)) {
-      const int w0 = wave_id() - s;
-      for (int t = lane_id(); t < B; t += 64) {
-        float g = slice_slot(p, L, round, w0)[2 * t], u = slice_slot(p, L, round, w0)[2 * t + 1];
-        for (int s2 = 1; s2 < NSS; ++s2) {
-          g += slice_slot(p, L, round, w0 + s2)[2 * t];
-          u += slice_slot(p, L, round, w0 + s2)[2 * t + 1];
-        }
-        publish(p->hsh32 + (size_t)t * Is + j, round_act<AD>(silu_mul(g, u)));
+  if (NSS > 1 && last_slice(L.head().scnt, round, NSS)) {
+    const int w0 = wave_id() - s;
+    for (int t = lane_id(); t < B; t += 64) {
+      float g = slice_slot(p, L, round, w0)[2 * t], u = slice_slot(p, L, round, w0)[2 * t + 1];
+      for (int s2 = 1; s2 < NSS; ++s2) {
+        g += slice_slot(p, L, round, w0 + s2)[2 * t];
+        u += slice_slot(p, L, round, w0 + s2)[2 * t + 1];
       }
+      shared_h_out<AD, XL>(p, (size_t)t * Is + j, silu_mul(g, u));
     }
   }
 }
@@ -1275,7 +1280,7 @@ __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Ld
 // permutation on both sides.
 
 #ifndef MOE_MFMA_MIN
-#define MOE_MFMA_MIN 16
+#define MOE_MFMA_MIN 3
 #endif
 constexpr int kMfmaMin = MOE_MFMA_MIN;  // tokens of one expert from which its rows go through MFMA tiles
 
@@ -1299,45 +1304,86 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-// acc[row tile r][token tile nt] += W rows (wa[r]) x activation rows (xb[nt]) over K
-// columns. Lane l: weight row l%16 of each tile, token column l%16, K group l/16.
-template <int WD, int NR, int NT>
-__device__ __forceinline__ void mfma_rows(const char *const (&wa)[NR], int K, const char *const (&xb)[NT],
-                                          f32x4 (&acc)[NR][NT]) {
-  const int kq = lane_id() >> 4;
-  if constexpr (WD == DT_FP8) {
-    for (int k0 = 0; k0 < K; k0 += 64) {
-      const int c = k0 + kq * 16;
-      u32x4 w[NR], x0[NT], x1[NT];
+// 16-byte loads at a uniform base plus a per-lane 32-bit byte offset, issued
+// as written (the compiler neither splits nor delays them); the results must
+// not be read before mfma_wait().
+__device__ __forceinline__ u32x4 ld16_nt(const char *base, unsigned off) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, %2 nt" : "=v"(v) : "v"(off), "s"(base) : "memory");
+  return v;
+}
+__device__ __forceinline__ u32x4 ld16(const char *base, unsigned off) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(v) : "v"(off), "s"(base) : "memory");
+  return v;
+}
+// waits for every load in flight; each value is then passed through an
+// empty asm so no use of it can be scheduled above the wait
+template <int A, int B2>
+__device__ __forceinline__ void mfma_wait(u32x4 (&a)[A][B2]) {
 #pragma unroll
-      for (int r = 0; r < NR; ++r) w[r] = ldw(wa[r] + c);
+  for (int i = 0; i < A; ++i)
+#pragma unroll
+    for (int j = 0; j < B2; ++j) asm volatile("" : "+v"(a[i][j]));
+}
+
+// acc[row tile r][token tile t] += W rows x activation rows over K columns.
+// Lane l: weight row l%16 of each tile, token column l%16, K group l/16.
+// Addresses are a uniform base plus a per-lane 32-bit byte offset (woff[r]:
+// the lane's row of tile r, xoff[t]: the lane's token row of tile t). Each
+// iteration covers 64 columns and issues every load of the iteration (4 KB
+// of weights per wave for a gate/up pair at bf16) before one wait (bf16: two
+// K groups of 8 per lane; fp8: 16 codes per lane feeding two MFMAs, with the
+// activation columns in the same order).
+template <int WD, int NR, int NT>
+__device__ __forceinline__ void mfma_rows(const char *wbase, const unsigned (&woff)[NR], int K, const char *xbase,
+                                          const unsigned (&xoff)[NT], f32x4 (&acc)[NR][NT]) {
+  const unsigned kq = (unsigned)lane_id() >> 4;
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    constexpr int WH = WD == DT_FP8 ? 1 : 2;
+    u32x4 w[NR][WH], x[NT][2];
+    if constexpr (WD == DT_FP8) {
+      const unsigned c = (unsigned)k0 + kq * 16u;  // the lane's 16 columns
+#pragma unroll
+      for (int r = 0; r < NR; ++r) w[r][0] = ld16_nt(wbase, woff[r] + c);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        x0[t] = *(const u32x4 *)(xb[t] + (size_t)c * 2);
-        x1[t] = *(const u32x4 *)(xb[t] + (size_t)(c + 8) * 2);
+        x[t][0] = ld16(xbase, xoff[t] + c * 2u);
+        x[t][1] = ld16(xbase, xoff[t] + (c + 8u) * 2u);
       }
+    } else {
+      const unsigned c0 = (unsigned)k0 + kq * 8u, c1 = c0 + 32u;  // K groups of this and the next 32 columns
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const u32x4 lo = fp8x8_to_bf16(w[r].x, w[r].y), hi = fp8x8_to_bf16(w[r].z, w[r].w);
+        w[r][0] = ld16_nt(wbase, woff[r] + c0 * 2u);
+        w[r][1] = ld16_nt(wbase, woff[r] + c1 * 2u);
+      }
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          acc[r][t] = mfma16(lo, x0[t], acc[r][t]);
-          acc[r][t] = mfma16(hi, x1[t], acc[r][t]);
-        }
+      for (int t = 0; t < NT; ++t) {
+        x[t][0] = ld16(xbase, xoff[t] + c0 * 2u);
+        x[t][1] = ld16(xbase, xoff[t] + c1 * 2u);
       }
     }
-  } else {
-    for (int k0 = 0; k0 < K; k0 += 32) {
-      const int c = k0 + kq * 8;
-      u32x4 w[NR], x[NT];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    mfma_wait(w);
+    mfma_wait(x);
+    if constexpr (WD == DT_FP8) {
 #pragma unroll
-      for (int r = 0; r < NR; ++r) w[r] = ldw(wa[r] + (size_t)c * 2);
+      for (int r = 0; r < NR; ++r) {
+        const u32x4 lo = fp8x8_to_bf16(w[r][0].x, w[r][0].y), hi = fp8x8_to_bf16(w[r][0].z, w[r][0].w);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) x[t] = *(const u32x4 *)(xb[t] + (size_t)c * 2);
+        for (int t = 0; t < NT; ++t) {
+          acc[r][t] = mfma16(lo, x[t][0], acc[r][t]);
+          acc[r][t] = mfma16(hi, x[t][1], acc[r][t]);
+        }
+      }
+    } else {
 #pragma unroll
-      for (int r = 0; r < NR; ++r)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[r][t] = mfma16(w[r], x[t], acc[r][t]);
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[r][t] = mfma16(w[r][h], x[t][h], acc[r][t]);
     }
   }
 }
@@ -1362,8 +1408,8 @@ __device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L,
   const int e = ulist[u], n = ucnt[u];
   const int r = lane & 15, kq = lane >> 4;
   const size_t rowb = (size_t)H * dsz<ED>();
-  const char *gu = (const char *)lp->egu + (size_t)e * 2 * I * rowb;
-  const char *const wa[2] = {gu + (size_t)(16 * jb + r) * rowb, gu + (size_t)(I + 16 * jb + r) * rowb};
+  const char *gu = (const char *)lp->egu + (size_t)e * 2 * I * rowb;  // < 4 GB: 32-bit offsets
+  const unsigned wo[2] = {(unsigned)((16 * jb + r) * rowb), (unsigned)((I + 16 * jb + r) * rowb)};
   float gs = 1.f, us = 1.f;
   if constexpr (ED == DT_FP8) {
     const uint16_t *sc = lp->egus + (size_t)e * (2 * I / 128);
@@ -1371,18 +1417,18 @@ __device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L,
     us = __uint_as_float((uint32_t)sc[(I + 16 * jb) / 128] << 16);
   }
   with_token_tiles(n, [&]<int NT>() {
-    const char *xb[NT];
+    unsigned xo[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int c = min(16 * t + r, n - 1);  // columns past n repeat a valid token; discarded
-      xb[t] = (const char *)p->xa + (size_t)(pl[c] / k) * H * 2;
+      xo[t] = (unsigned)(pl[c] / k) * (unsigned)H * 2u;
     }
     f32x4 acc[2][NT];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_rows<ED, 2, NT>(wa, H, xb, acc);
+    mfma_rows<ED, 2, NT>(uni(gu), wo, H, (const char *)p->xa, xo, acc);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int c = 16 * t + r;
@@ -1407,15 +1453,16 @@ __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &
   const int *pl = L.at<int>(p->o_plist) + ustart[s];
   const int e = ulist[s], n = ucnt[s];
   const int r = lane & 15, kq = lane >> 4;
-  const char *const wa[1] = {(const char *)lp->ed + ((size_t)e * H + o0 + r) * I * dsz<ED>()};
+  const char *wbase = (const char *)lp->ed + (size_t)e * H * I * dsz<ED>();  // < 4 GB: 32-bit offsets
+  const unsigned wo[1] = {(unsigned)((size_t)(o0 + r) * I * dsz<ED>())};
   with_token_tiles(n, [&]<int NT>() {
-    const char *xb[NT];
+    unsigned xo[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) xb[t] = (const char *)p->hbuf + (size_t)pl[min(16 * t + r, n - 1)] * I * 2;
+    for (int t = 0; t < NT; ++t) xo[t] = (unsigned)pl[min(16 * t + r, n - 1)] * (unsigned)I * 2u;
     f32x4 acc[1][NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_rows<ED, 1, NT>(wa, I, xb, acc);
+    mfma_rows<ED, 1, NT>(uni(wbase), wo, I, (const char *)p->hbuf, xo, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int o = o0 + 4 * kq + i;
@@ -1430,6 +1477,16 @@ __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &
       }
     }
   });
+}
+
+// P1 cost of a GEMV row pair of an expert with n tokens and of an MFMA tile
+// (16 pairs, ceil(n/16) token tiles), in tenths of a one-token GEMV pair:
+// per-task timings on MI355X at the K3 share (B=64, every wave streaming).
+__device__ __forceinline__ int gemv_pair_cost(int n) { return n <= 1 ? 10 : n == 2 ? 15 : n <= 4 ? 21 : 11 + 4 * n; }
+__device__ __forceinline__ int mfma_tile_cost(int n) { return 190 + 30 * ((n + 15) / 16); }
+// all of a listed slot's P1 work
+__device__ __forceinline__ int slot_cost(KParams p, bool mfma, int n) {
+  return mfma ? (p->I / 16) * mfma_tile_cost(n) : p->I * gemv_pair_cost(n);
 }
 
 // Union slots split by token count: MFMA tiles (n >= kMfmaMin) and GEMV.
@@ -1453,6 +1510,23 @@ __device__ __attribute__((noinline)) void classify_slots(KParams p_arg, const Ld
       ng += __popcll(bg);
     }
     if (lane == 0) { sh.nM = nm; sh.nG = ng; }
+    // cost prefix over the listed slots (MFMA slots, then GEMV slots)
+    int *cpre = L.at<int>(p->o_cpre);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    int run = 0;
+    for (int i0 = 0; i0 < nm + ng; i0 += 64) {
+      const int i = i0 + lane;
+      const int c = i < nm + ng ? slot_cost(p, i < nm, ucnt[i < nm ? mslot[i] : gslot[i - nm]]) : 0;
+      int incl = c;  // inclusive prefix over the lanes
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int up = __shfl_up(incl, d);
+        if (lane >= d) incl += up;
+      }
+      if (i < nm + ng) cpre[i] = run + incl - c;
+      run += __shfl(incl, 63);
+    }
+    if (lane == 0) cpre[nm + ng] = run;
   }
   __syncthreads();
 }
@@ -1791,26 +1865,40 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       // P0: router slices, then shared gate/up
       p0_tasks<AD, RD, SD, false>(p, lp, L, b0);
 
-      // P1: routing (one wave per token), gather tables, expert gate/up. Each
-      // workgroup owns a contiguous share of the work in row units (an MFMA
-      // task is 16 rows, a GEMV task 1): the MFMA tasks of its share first,
-      // then its GEMV tasks, handed out to its waves through LDS counters.
+      // P1: routing (one wave per token), gather tables, expert gate/up. The
+      // tasks (MFMA tiles of the listed MFMA slots, then GEMV row pairs of the
+      // GEMV slots) have measured costs, and every wave of the grid takes the
+      // tasks whose starting cost falls in its equal, contiguous cost range.
       bar_wait(p, sh, b0 + BAR_ROUTER);
       for (int t = wv; t < p->B; t += kWaves) topk_token<false>(p, lp, L, t, blockIdx.x == 0);
       __syncthreads();
       build_tables(p, L);
       classify_slots(p, L);
       {
-        const int I = p->I, nb = I / 16, G = p->G, g = blockIdx.x;
-        const int nMU = sh.nM * I, C = (sh.nM + sh.nG) * I;
-        const int ca = share_lo(C, g, G), cz = share_lo(C, g + 1, G);
+        const int I = p->I, nb = I / 16, nM = sh.nM, nL = sh.nM + sh.nG;
         const int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
-        const int ma = (min(ca, nMU) + 15) / 16, mz = (min(cz, nMU) + 15) / 16;
-        for (int q = take(sh, 0, ma, mz); q >= 0; q = take(sh, 0, ma, mz))
-          mfma_gu_task<AD, ED>(p, lp, L, mslot[q / nb], q % nb);
-        const int ga = max(ca, nMU) - nMU, gz = max(cz, nMU) - nMU;
-        for (int q = take(sh, 1, ga, gz); q >= 0; q = take(sh, 1, ga, gz))
-          expert_gu_task<AD, ED, false>(p, lp, L, gslot[q / I], q % I);
+        const int *ucnt = L.at<int>(p->o_ucnt), *cpre = L.at<int>(p->o_cpre);
+        const int C = cpre[nL];
+        const int lo = share_lo(C, W, NW), hi = share_lo(C, W + 1, NW);
+        // listed slot i holding cost lo: the last i with cpre[i] <= lo
+        int a = 0, z = nL;
+        while (z - a > 1) {
+          const int m = (a + z) >> 1;
+          if (cpre[m] <= lo) a = m; else z = m;
+        }
+        for (int i = a; i < nL && cpre[i] < hi; ++i) {
+          const bool mf = i < nM;
+          const int slot = mf ? mslot[i] : gslot[i - nM];
+          const int uc = mf ? mfma_tile_cost(ucnt[slot]) : gemv_pair_cost(ucnt[slot]);
+          const int nt = mf ? nb : I;
+          // tasks j of this slot with cpre[i] + j*uc in [lo, hi)
+          const int j0 = lo > cpre[i] ? (lo - cpre[i] + uc - 1) / uc : 0;
+          const int j1 = min(nt, (hi - cpre[i] + uc - 1) / uc);
+          for (int j = j0; j < j1; ++j) {
+            if (mf) mfma_gu_task<AD, ED>(p, lp, L, slot, j);
+            else expert_gu_task<AD, ED, false>(p, lp, L, slot, j);
+          }
+        }
       }
       bar_arrive(p, sh, b0 + BAR_H);
 
@@ -2019,7 +2107,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   if (p.G < 1) return fail(MOE_ERR_DEVICE, "device reports no compute units");
   const bool small = small_regime(B);
   p.NSR = k_slices(d->hidden, d->router, 4);
-  p.NSS = small && d->shared_inter > 0 ? k_slices(d->hidden, d->shared, 2) : 1;
+  p.NSS = d->shared_inter > 0 ? k_slices(d->hidden, d->shared, 2) : 1;
   // the slices of a row are one workgroup's waves of one round: the shared
   // tasks start at a multiple of the workgroup's wave count, and the rounds
   // must fit the per-round slice counters and LDS slots (else every row is
@@ -2071,6 +2159,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     p.o_tmask = (int)o; o = align16(o + (size_t)E * 8);
     p.o_mslot = (int)o; o = align16(o + (size_t)nslot * 4);
     p.o_gslot = (int)o; o = align16(o + (size_t)nslot * 4);
+    p.o_cpre = (int)o; o = align16(o + (size_t)(nslot + 1) * 4);
   }
   p.o_slc = (int)o;
   o = align16(o + (size_t)rounds * kWaves * p.slw * sizeof(float));
