@@ -14,6 +14,14 @@ not the decode path).
     records the SHA-256 of the kernel source it was taken on, so that the
     benchmark reports the figure only while the kernel is unchanged.
 
+`python -m moe_decode_02_amd.profiling mfma <pmc_dir> <trace_dir> <out.txt> <command...>`
+    summarises a `rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
+    SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE` run of the decode kernel with
+    the kernel durations of a kernel-trace run of the same command: MFMA
+    work per dispatch (the MOPS counter counts units of 512 flops), the
+    achieved MFMA rate against the 2.5 PFLOP/s dense bf16 peak, and the
+    fraction of the kernel's active cycles in which MFMA units were busy.
+
 `<command...>` is the profiled command line, copied into the summary.
 """
 from __future__ import annotations
@@ -131,12 +139,42 @@ def read_traffic(path: str):
     return {"read": float(kv["hbm_read_bytes_per_launch"]), "write": float(kv["hbm_write_bytes_per_launch"])}
 
 
+def write_mfma(pmc_dir: str, trace_dir: str, out_txt: str, command: str) -> None:
+    mops = _pick(_counter_per_dispatch(pmc_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), DECODE_KERNEL)
+    busy = _pick(_counter_per_dispatch(pmc_dir, "SQ_VALU_MFMA_BUSY_CYCLES"), DECODE_KERNEL)
+    active = _pick(_counter_per_dispatch(pmc_dir, "GRBM_GUI_ACTIVE"), DECODE_KERNEL)
+    durs = _pick(kernel_durations(trace_dir), DECODE_KERNEL)
+    flops = statistics.mean(mops) * 512.0
+    t = statistics.mean(durs) * 1e-6
+    # SQ_VALU_MFMA_BUSY_CYCLES sums over the chip's SIMDs (4 per CU, 256 CUs);
+    # GRBM_GUI_ACTIVE counts cycles of the graphics block per XCD (8 XCDs)
+    simds, xcds = 4 * 256, 8
+    frac = statistics.mean(busy) / (statistics.mean(active) / xcds * simds)
+    lines = ["# MFMA use of the decode kernel from rocprofv3 --pmc (one pass) and --kernel-trace",
+             f"# command: {command}",
+             f"kernel_source_sha256 = {kernel_source_sha()}",
+             f"dispatches = {len(mops)}",
+             f"mfma_mops_bf16_per_dispatch = {statistics.mean(mops):.0f}",
+             f"mfma_flops_per_dispatch = {flops:.4g}",
+             f"kernel_avg_us = {statistics.mean(durs):.2f}",
+             f"mfma_tflops = {flops / t / 1e12:.2f}",
+             f"mfma_fraction_of_2500_tflops = {flops / t / 2.5e15:.5f}",
+             f"mfma_busy_cycles_per_dispatch = {statistics.mean(busy):.0f}",
+             f"gui_active_cycles_per_dispatch = {statistics.mean(active):.0f}",
+             f"mfma_busy_fraction_of_simd_cycles = {frac:.5f}"]
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main(argv) -> int:
     if len(argv) >= 4 and argv[1] == "stats":
         write_stats(argv[2], argv[3], " ".join(argv[4:]))
         return 0
     if len(argv) >= 5 and argv[1] == "traffic":
         write_traffic(argv[2], argv[3], argv[4], " ".join(argv[5:]))
+        return 0
+    if len(argv) >= 5 and argv[1] == "mfma":
+        write_mfma(argv[2], argv[3], argv[4], " ".join(argv[5:]))
         return 0
     print(__doc__, file=sys.stderr)
     return 2
