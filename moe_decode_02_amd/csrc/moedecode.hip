@@ -129,7 +129,7 @@ struct Params {
   float *hsh32;           // [B][Is]: the shared h, act-rounded, as fp32 (small regime)
   void *hbuf;             // [B*k][I] act
   void *hsbuf;             // [B][Is] act (general regime)
-  float *partbuf;          // [H][pstride] P2 partial sums (general regime)
+  float *partbuf;          // [pstride][H] P2 partial sums (general regime), column-major
   void *xbuf[2];          // [B][H] act, stack intermediates
   // LDS carve-up, byte offsets from the start of dynamic LDS
   int o_sel_idx, o_sel_w;           // routing of each token [B*k]
@@ -1189,11 +1189,12 @@ __device__ __forceinline__ void stage_shared_h_wave(KParams p, const Lds &L) {
 
 // One 4-row unit of a [rows][K] down matrix: row pointers wrow, columns
 // [0, I) of x rows xr (TG tokens); writes the row sums times sc[r] to
-// part[(o0 + r - pr0) * pstride + col[t]].
+// prow[(o0 + r - o0) * rs + col[t] * cs] (rs, cs: row and column strides of
+// the partial-sum buffer).
 template <int WD, int AD, bool XL, int TG>
 __device__ __forceinline__ void down_unit(const char *const (&wrow)[kRowBlock], int I,
                                           const typename XSrc<XL>::ptr (&xr)[TG], const float (&sc)[kRowBlock],
-                                          float *prow, int pstride, const int (&col)[TG], int nt) {
+                                          float *prow, int rs, int cs, const int (&col)[TG], int nt) {
 #pragma unroll
   for (int r0 = 0; r0 < kRowBlock; r0 += kDownRows) {
     const char *wr[kDownRows];
@@ -1210,17 +1211,21 @@ __device__ __forceinline__ void down_unit(const char *const (&wrow)[kRowBlock], 
 #pragma unroll
       for (int t = 0; t < TG; ++t) {
         const float v = wave_sum63(acc[r][t]) * sc[r0 + r];
-        if (t < nt && lane_id() == 63) prow[(r0 + r) * pstride + col[t]] = v;
+        if (t < nt && lane_id() == 63) prow[(r0 + r) * rs + col[t] * cs] = v;
       }
   }
 }
 
-// partial sums of P2: LDS rows of the pass (small regime) or global rows
+// partial sums of P2: the workgroup's rows in LDS, row-major (small regime),
+// or all rows in the workspace, column-major so that a unit's rows of one
+// column are contiguous (general regime)
 template <bool SMALL>
 __device__ __forceinline__ float *part_base(KParams p, const Lds &L) {
   if constexpr (SMALL) return L.at<float>(p->o_part);
   else return p->partbuf;
 }
+template <bool SMALL> __device__ __forceinline__ int part_rs(KParams p, int pstride) { return SMALL ? pstride : 1; }
+template <bool SMALL> __device__ __forceinline__ int part_cs(KParams p) { return SMALL ? 1 : p->H; }
 
 // Next P2 unit of this wave: handed out through an LDS counter (DYN, small
 // regime) or dealt round-robin from wave w0.
@@ -1264,7 +1269,8 @@ __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Ld
         else xr[t] = (const char *)p->hsbuf + ((size_t)tt * Is + (size_t)hf * I) * dsz<AD>();
         col[t] = P + (t0 + t) * nsh + hf;
       }
-      down_unit<SD, AD, SMALL, TG>(wrow, I, xr, one, part + (size_t)(o0 - prb) * pstride, pstride, col, nt);
+      down_unit<SD, AD, SMALL, TG>(wrow, I, xr, one, part + (size_t)(o0 - prb) * part_rs<SMALL>(p, pstride),
+                                   part_rs<SMALL>(p, pstride), part_cs<SMALL>(p), col, nt);
     });
   }
 }
@@ -1446,8 +1452,7 @@ __device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L,
 // the expert's tokens; rows >= lo go to the partial sums (rows below lo were
 // written by the previous tile of the same workgroup).
 template <int AD, int ED>
-__device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &L, int s, int o0, int lo, float *part,
-                                               int pstride) {
+__device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &L, int s, int o0, int lo, float *part) {
   const int H = p->H, I = p->I, lane = lane_id();
   const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   const int *pl = L.at<int>(p->o_plist) + ustart[s];
@@ -1472,7 +1477,7 @@ __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const int c = 16 * t + r;
-          if (c < n) part[(size_t)o * pstride + pl[c]] = acc[0][t][i] * sc;
+          if (c < n) part[(size_t)pl[c] * H + o] = acc[0][t][i] * sc;  // column-major
         }
       }
     }
@@ -1534,7 +1539,7 @@ __device__ __attribute__((noinline)) void classify_slots(KParams p_arg, const Ld
 // One routed expert's 4-row GEMV unit (slot s, rows [o0, o0+4)).
 template <int AD, int ED, bool SMALL>
 __device__ __forceinline__ void expert_down_gemv(KParams p, KLayer lp, const Lds &L, int s, int o0, float *prow,
-                                                 int pstride) {
+                                                 int rs, int cs) {
   const int H = p->H, I = p->I;
   const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   const int *plist = L.at<int>(p->o_plist);
@@ -1557,7 +1562,7 @@ __device__ __forceinline__ void expert_down_gemv(KParams p, KLayer lp, const Lds
       col[t] = pl[t0 + (t < nt ? t : 0)];
       xr[t] = (const char *)p->hbuf + (size_t)col[t] * I * dsz<AD>();
     }
-    down_unit<ED, AD, false, TG>(wrow, I, xr, sc, prow, pstride, col, nt);
+    down_unit<ED, AD, false, TG>(wrow, I, xr, sc, prow, rs, cs, col, nt);
   });
 }
 
@@ -1585,7 +1590,8 @@ __device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Ld
     const int nu = ub - ua;
     for (int un = next_unit<true>(L.head(), uc, cur, w0); un < nrb * nu; un = next_unit<true>(L.head(), uc, cur, w0)) {
       const int s = ua + un / nrb, o0 = pr0 + (un % nrb) * kRowBlock;
-      expert_down_gemv<AD, ED, SMALL>(p, lp, L, s, o0, part + (size_t)(o0 - prb) * pstride, pstride);
+      expert_down_gemv<AD, ED, SMALL>(p, lp, L, s, o0, part + (size_t)(o0 - prb) * part_rs<SMALL>(p, pstride),
+                                      part_rs<SMALL>(p, pstride), part_cs<SMALL>(p));
     }
   } else {
     const int nM = L.head().nM, nG = L.head().nG;
@@ -1596,11 +1602,12 @@ __device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Ld
         const int ti = un % ntile;
         const int o0 = min(pr0 + 16 * ti, pr1 - 16);  // the last tile ends at pr1
         const int lo = pr0 + 16 * ti;                 // rows below lo belong to the previous tile
-        mfma_down_tile<AD, ED>(p, lp, L, mslot[un / ntile], o0, lo, part, pstride);
+        mfma_down_tile<AD, ED>(p, lp, L, mslot[un / ntile], o0, lo, part);
       } else {
         const int g = un - nmu;
         const int s = gslot[g / nrb], o0 = pr0 + (g % nrb) * kRowBlock;
-        expert_down_gemv<AD, ED, false>(p, lp, L, s, o0, part + (size_t)(o0 - prb) * pstride, pstride);
+        expert_down_gemv<AD, ED, false>(p, lp, L, s, o0, part + (size_t)(o0 - prb) * part_rs<SMALL>(p, pstride),
+                                        part_rs<SMALL>(p, pstride), part_cs<SMALL>(p));
       }
     }
   }
@@ -1614,15 +1621,16 @@ __device__ __forceinline__ void combine(KParams p, KLayer lp, const Lds &L, int 
   const float *part = part_base<SMALL>(p, L);
   const int prb = SMALL ? pr0 : 0;
   const float *sel_w = L.at<float>(p->o_sel_w);
-  const int cells = (pr1 - pr0) * B;
+  const int nr = pr1 - pr0, cells = nr * B;
   for (int c = threadIdx.x; c < cells; c += kThreads) {
-    const int ro = c / B, t = c % B;
+    const int ro = c % nr, t = c / nr;  // consecutive threads: consecutive rows (coalesced x, y, partials)
     const int o = pr0 + ro;
-    const float *pp = part + (size_t)(o - prb) * pstride;
+    const int cs = part_cs<SMALL>(p);
+    const float *pp = part + (size_t)(o - prb) * part_rs<SMALL>(p, pstride);
     float sh = 0.f;
-    for (int hf = 0; hf < nsh; ++hf) sh += pp[P + t * nsh + hf];
+    for (int hf = 0; hf < nsh; ++hf) sh += pp[(size_t)(P + t * nsh + hf) * cs];
     float rt = 0.f;
-    for (int i = 0; i < k; ++i) rt = fmaf(sel_w[t * k + i], pp[t * k + i], rt);
+    for (int i = 0; i < k; ++i) rt = fmaf(sel_w[t * k + i], pp[(size_t)(t * k + i) * cs], rt);
     const float v = load_act<AD>(lp->x, (size_t)t * H + o) + sh + rt;
     store_act<AD>(lp->y, (size_t)t * H + o, v);
   }
