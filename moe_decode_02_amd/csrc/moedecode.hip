@@ -117,7 +117,6 @@ struct Params {
   int p0r, p0w;           // P0 rounds; waves per workgroup that take a task in the last round
   int G;                  // workgroups
   int rows_per_wg;        // P2 output rows per workgroup (multiple of kRowBlock)
-  int pass_rows;          // P2 rows per LDS pass
   float eps;
   long long timeout_ticks;  // s_memrealtime ticks (100 MHz) before a barrier wait gives up
   unsigned *ctrl;         // control words, kCtrlStride apart
@@ -141,7 +140,7 @@ struct Params {
   int o_xf, o_xa;                   // small regime: x-hat fp32 / act [B][H]
   int o_hs;                         // small regime: shared h [B][Is] (act)
   int o_slc;                        // slice sums of P0 tasks [round][wave][slw]
-  int o_part;                       // P2 partial sums [pass_rows][pstride] fp32
+  int o_part;                       // small regime: P2 partial sums [rows_per_wg][pstride] fp32
   LayerPtrs lp[kMaxL];
 };
 
@@ -156,7 +155,6 @@ struct SmemHead {
   int route_claim, route_ready;    // small regime: the first free wave does the routing
   int shared_claim, shared_ready;  // small regime: ... and the shared expert's h
   int unit_ctr[2 + kP1Groups];     // P2 units handed out to waves (shared, experts / expert group)
-  int task_ctr[3];                 // router / shared / expert gate-up tasks handed out
   int rcnt[kMaxRounds][kWaves];    // slices of a router row / shared pair done, per round and slice group
   int scnt[kMaxRounds][kWaves];
   int nM, nG;                      // general regime: union slots on MFMA tiles, on GEMV
@@ -978,7 +976,6 @@ __device__ __attribute__((noinline)) void topk_token(KParams p_arg, KLayer lp_ar
     const unsigned mk = lane < total ? ck[lane] : 0u;
     const int me = lane < total ? ci[lane] : 0x7FFFFFFF;
     int rank = 0;
-#pragma unroll 4
     for (int c = 0; c < total; ++c) {
       const unsigned ok = (unsigned)__builtin_amdgcn_readlane((int)mk, c);
       const int oe = __builtin_amdgcn_readlane(me, c);
@@ -1227,32 +1224,25 @@ __device__ __forceinline__ float *part_base(KParams p, const Lds &L) {
 template <bool SMALL> __device__ __forceinline__ int part_rs(KParams p, int pstride) { return SMALL ? pstride : 1; }
 template <bool SMALL> __device__ __forceinline__ int part_cs(KParams p) { return SMALL ? 1 : p->H; }
 
-// Next P2 unit of this wave: handed out through an LDS counter (DYN, small
-// regime) or dealt round-robin from wave w0.
-template <bool DYN>
-__device__ __forceinline__ int next_unit(SmemHead &sh, int which, int &cur, int w0) {
-  if constexpr (DYN) {
-    int u = 0;
-    if (lane_id() == 0) u = __hip_atomic_fetch_add(&sh.unit_ctr[which], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    return __builtin_amdgcn_readfirstlane(u);
-  } else {
-    cur = (cur < 0) ? (wave_id() + kWaves - w0 % kWaves) % kWaves : cur + kWaves;
-    return cur;
-  }
+// Next P2 unit of this wave, handed out through the workgroup's LDS counter
+// `which` (so a wave that starts late takes fewer).
+__device__ __forceinline__ int next_unit(SmemHead &sh, int which) {
+  int u = 0;
+  if (lane_id() == 0) u = __hip_atomic_fetch_add(&sh.unit_ctr[which], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_amdgcn_readfirstlane(u);
 }
 
 // shared-expert units of rows [pr0, pr1): (row block, column block hf); the
 // shared h comes from LDS (small regime) or global memory
 template <int AD, int SD, bool SMALL>
-__device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, int w0) {
+__device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1) {
   const int I = p->I, Is = p->Is, B = p->B;
   const int nsh = Is / I, P = B * p->k, pstride = P + B * nsh;
   const int nrb = (pr1 - pr0) / kRowBlock;
   float *part = part_base<SMALL>(p, L);
   const int prb = SMALL ? pr0 : 0;
   const float one[kRowBlock] = {1.f, 1.f, 1.f, 1.f};
-  int cur = -1;
-  for (int un = next_unit<true>(L.head(), 0, cur, w0); un < nrb * nsh; un = next_unit<true>(L.head(), 0, cur, w0)) {
+  for (int un = next_unit(L.head(), 0); un < nrb * nsh; un = next_unit(L.head(), 0)) {
     const int hf = un / nrb, rb = un % nrb;
     const int o0 = pr0 + rb * kRowBlock;
     const char *wrow[kRowBlock];
@@ -1575,20 +1565,19 @@ __device__ __forceinline__ void expert_down_gemv(KParams p, KLayer lp, const Lds
 // so a wave's consecutive units read consecutive rows. Small regime: the slots
 // [ua, ub) of one expert group, handed out through unit counter uc.
 template <int AD, int ED, bool SMALL>
-__device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, int w0,
+__device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1,
                                                   int ua = 0, int ub = 0, int uc = 1) {
   const int I = p->I, B = p->B;
   const int nsh = p->Is / I, P = B * p->k, pstride = P + B * nsh;
   const int nrb = (pr1 - pr0) / kRowBlock;
   float *part = part_base<SMALL>(p, L);
   const int prb = SMALL ? pr0 : 0;
-  int cur = -1;
   const int ntile = (pr1 - pr0) >= 16 ? (pr1 - pr0 + 15) / 16 : 0;
   if (SMALL || L.head().nM == 0 || ntile == 0) {
     // every slot on GEMV (also the MFMA slots of a workgroup with fewer than 16 rows)
     if (!SMALL) { ua = 0; ub = L.head().nU; uc = 1; }
     const int nu = ub - ua;
-    for (int un = next_unit<true>(L.head(), uc, cur, w0); un < nrb * nu; un = next_unit<true>(L.head(), uc, cur, w0)) {
+    for (int un = next_unit(L.head(), uc); un < nrb * nu; un = next_unit(L.head(), uc)) {
       const int s = ua + un / nrb, o0 = pr0 + (un % nrb) * kRowBlock;
       expert_down_gemv<AD, ED, SMALL>(p, lp, L, s, o0, part + (size_t)(o0 - prb) * part_rs<SMALL>(p, pstride),
                                       part_rs<SMALL>(p, pstride), part_cs<SMALL>(p));
@@ -1597,7 +1586,7 @@ __device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Ld
     const int nM = L.head().nM, nG = L.head().nG;
     const int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
     const int nmu = nM * ntile;
-    for (int un = next_unit<true>(L.head(), 1, cur, w0); un < nmu + nG * nrb; un = next_unit<true>(L.head(), 1, cur, w0)) {
+    for (int un = next_unit(L.head(), 1); un < nmu + nG * nrb; un = next_unit(L.head(), 1)) {
       if (un < nmu) {
         const int ti = un % ntile;
         const int o0 = min(pr0 + 16 * ti, pr1 - 16);  // the last tile ends at pr1
@@ -1682,15 +1671,6 @@ __device__ __forceinline__ unsigned prefetch_p0(KParams p, KLayer nl) {
 
 // ---------------------------------------------------------------------------
 // the kernel
-
-// Next task of this workgroup's share [a, z) (handed out through an LDS
-// counter, so waves that start late or run slow take fewer), or -1.
-__device__ __forceinline__ int take(SmemHead &sh, int which, int a, int z) {
-  int q = 0;
-  if (lane_id() == 0) q = __hip_atomic_fetch_add(&sh.task_ctr[which], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  q = __builtin_amdgcn_readfirstlane(q) + a;
-  return q < z ? q : -1;
-}
 
 // workgroup g's contiguous share of n tasks
 __device__ __forceinline__ int share_lo(int n, int g, int G) { return (int)((long long)n * g / G); }
@@ -1793,7 +1773,7 @@ __device__ __forceinline__ void layer_small(KParams p, KLayer lp, const Lds &L, 
   }
   const int r0 = g * p->rows_per_wg;
   const int r1 = min(p->H, r0 + p->rows_per_wg);
-  if (r0 < r1) shared_down_units<AD, SD, true>(p, lp, L, r0, r1, 0);
+  if (r0 < r1) shared_down_units<AD, SD, true>(p, lp, L, r0, r1);
   // the routed experts' rows, group by group: slots [ua, ub) end in group gi
   int ua = 0;
   for (int gi = 0; gi < nG; ++gi) {
@@ -1802,7 +1782,7 @@ __device__ __forceinline__ void layer_small(KParams p, KLayer lp, const Lds &L, 
     while (ub < sh.nU && ((ub + 1) * I - 1) / NW < rend) ++ub;
     if (ub > ua) {
       bar_wait(p, sh, b0 + BAR_H + gi);
-      if (r0 < r1) expert_down_units<AD, ED, true>(p, lp, L, r0, r1, 0, ua, ub, 2 + gi);
+      if (r0 < r1) expert_down_units<AD, ED, true>(p, lp, L, r0, r1, ua, ub, 2 + gi);
     }
     ua = ub;
   }
@@ -1841,7 +1821,6 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
     if (tid == 0) {
       sh.route_claim = sh.route_ready = sh.shared_claim = sh.shared_ready = 0;
       for (int i = 0; i < 2 + kP1Groups; ++i) sh.unit_ctr[i] = 0;
-      sh.task_ctr[0] = sh.task_ctr[1] = sh.task_ctr[2] = 0;
     }
     __syncthreads();
 
@@ -1915,9 +1894,9 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       const int r0 = blockIdx.x * p->rows_per_wg;
       const int r1 = min(p->H, r0 + p->rows_per_wg);
       bar_wait(p, sh, b0 + BAR_SHARED);
-      if (r0 < r1) shared_down_units<AD, SD, false>(p, lp, L, r0, r1, 0);
+      if (r0 < r1) shared_down_units<AD, SD, false>(p, lp, L, r0, r1);
       bar_wait(p, sh, b0 + BAR_H);
-      if (r0 < r1) expert_down_units<AD, ED, false>(p, lp, L, r0, r1, 0);
+      if (r0 < r1) expert_down_units<AD, ED, false>(p, lp, L, r0, r1);
       __syncthreads();
       if (r0 < r1) combine<AD, false>(p, lp, L, r0, r1);
       __syncthreads();
@@ -2176,7 +2155,6 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   // its rows); general regime: they go to the workspace
   const size_t per_row = (size_t)(P + B * nsh) * sizeof(float);
   const size_t lds_cap = (size_t)(di.max_lds > 0 ? di.max_lds : 65536);
-  p.pass_rows = rpw;
   const size_t lds = small ? o + (size_t)rpw * per_row : o;
   if (lds > lds_cap) return fail(MOE_ERR_UNSUPPORTED, "shape needs more LDS than the device's %zu bytes", lds_cap);
   p.use_mfma = (!small && d->expert != MOE_F32 && rpw >= 16) ? 1 : 0;

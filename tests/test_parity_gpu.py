@@ -168,6 +168,24 @@ def test_mfma_tiles_every_token(dev, expert, router, seed):
     log(f"mfma tiles ({expert}) max rel err {err:.2e}")
 
 
+@pytest.mark.parametrize("B,expert,seed", [(5, synth.BF16, 51), (7, synth.FP8, 53), (12, synth.BF16, 56)])
+def test_mfma_partial_token_tiles(dev, B, expert, seed):
+    """Small batches over 8 experts (top-4): experts get 1 to ~10 tokens, so
+    MFMA tiles run with mostly-unused token columns (an expert with 3 or more
+    tokens goes to MFMA) next to one- and two-token GEMV experts, under the
+    cost-balanced task split. Every token vs the oracle."""
+    w = small_workload(name="mfma_small", H=4096, E=8, k=4, I=256, Is=256, act=synth.BF16, router=synth.F32,
+                       expert=expert, shared=synth.BF16, seed=seed)
+    Lh = host_layer(w, experts=[])
+    x, _ = draw_tokens_with_margin(w, B, [Lh])
+    idx_r, _, _ = oracle_routes(w, Lh, x)
+    counts = np.bincount(idx_r.ravel(), minlength=w.E)
+    log(f"mfma small-batch test: expert token counts {sorted(counts.tolist(), reverse=True)}")
+    assert np.sum((counts >= 3) & (counts < 16)) >= 1 and np.sum((counts > 0) & (counts < 3)) >= 1
+    err = full_parity(w, B, dev, poison=True)
+    log(f"partial token tiles B={B} ({expert}) max rel err {err:.2e}")
+
+
 def test_k3_b1(dev):
     err = full_parity(synth.WORKLOADS["k3_b1"], 1, dev, poison=True)
     log(f"k3_b1 max rel err {err:.2e}")
