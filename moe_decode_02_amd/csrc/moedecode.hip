@@ -1556,48 +1556,49 @@ __device__ __forceinline__ void expert_down_gemv(KParams p, KLayer lp, const Lds
   });
 }
 
-// routed-expert units of rows [pr0, pr1), handed out through an LDS counter.
-// Small regime: (expert slot, row block), expert-major so a wave's
-// consecutive units read consecutive rows; h from LDS. General regime: the
-// MFMA tiles of the experts with many tokens first, then the GEMV units of the
-// others; h from global memory.
-// routed-expert units of rows [pr0, pr1): (union slot, 4-row block), slot-major
-// so a wave's consecutive units read consecutive rows. Small regime: the slots
-// [ua, ub) of one expert group, handed out through unit counter uc.
+// Small regime: routed-expert units of rows [pr0, pr1): (union slot, 4-row
+// block) for the slots [ua, ub) of one expert group, slot-major so a wave's
+// consecutive units read consecutive rows, handed out through counter uc.
 template <int AD, int ED, bool SMALL>
-__device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1,
-                                                  int ua = 0, int ub = 0, int uc = 1) {
+__device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, int ua, int ub,
+                                                  int uc) {
   const int I = p->I, B = p->B;
   const int nsh = p->Is / I, P = B * p->k, pstride = P + B * nsh;
   const int nrb = (pr1 - pr0) / kRowBlock;
   float *part = part_base<SMALL>(p, L);
   const int prb = SMALL ? pr0 : 0;
+  const int nu = ub - ua;
+  for (int un = next_unit(L.head(), uc); un < nrb * nu; un = next_unit(L.head(), uc)) {
+    const int s = ua + un / nrb, o0 = pr0 + (un % nrb) * kRowBlock;
+    expert_down_gemv<AD, ED, SMALL>(p, lp, L, s, o0, part + (size_t)(o0 - prb) * part_rs<SMALL>(p, pstride),
+                                    part_rs<SMALL>(p, pstride), part_cs<SMALL>(p));
+  }
+}
+
+// General regime: routed-expert units of rows [pr0, pr1) for listed slots
+// [ia, ib) (MFMA slots first, then GEMV slots), handed out through unit
+// counter uc: MFMA down tiles of 16 rows for the MFMA slots (GEMV units when
+// the workgroup has fewer than 16 rows), 4-row GEMV units for the others.
+template <int AD, int ED>
+__device__ __forceinline__ void expert_down_listed(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, int ia, int ib,
+                                                   int uc) {
+  const int nrb = (pr1 - pr0) / kRowBlock, nM = L.head().nM;
+  float *part = p->partbuf;
+  const int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
   const int ntile = (pr1 - pr0) >= 16 ? (pr1 - pr0 + 15) / 16 : 0;
-  if (SMALL || L.head().nM == 0 || ntile == 0) {
-    // every slot on GEMV (also the MFMA slots of a workgroup with fewer than 16 rows)
-    if (!SMALL) { ua = 0; ub = L.head().nU; uc = 1; }
-    const int nu = ub - ua;
-    for (int un = next_unit(L.head(), uc); un < nrb * nu; un = next_unit(L.head(), uc)) {
-      const int s = ua + un / nrb, o0 = pr0 + (un % nrb) * kRowBlock;
-      expert_down_gemv<AD, ED, SMALL>(p, lp, L, s, o0, part + (size_t)(o0 - prb) * part_rs<SMALL>(p, pstride),
-                                      part_rs<SMALL>(p, pstride), part_cs<SMALL>(p));
-    }
-  } else {
-    const int nM = L.head().nM, nG = L.head().nG;
-    const int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
-    const int nmu = nM * ntile;
-    for (int un = next_unit(L.head(), 1); un < nmu + nG * nrb; un = next_unit(L.head(), 1)) {
-      if (un < nmu) {
-        const int ti = un % ntile;
-        const int o0 = min(pr0 + 16 * ti, pr1 - 16);  // the last tile ends at pr1
-        const int lo = pr0 + 16 * ti;                 // rows below lo belong to the previous tile
-        mfma_down_tile<AD, ED>(p, lp, L, mslot[un / ntile], o0, lo, part);
-      } else {
-        const int g = un - nmu;
-        const int s = gslot[g / nrb], o0 = pr0 + (g % nrb) * kRowBlock;
-        expert_down_gemv<AD, ED, false>(p, lp, L, s, o0, part + (size_t)(o0 - prb) * part_rs<SMALL>(p, pstride),
-                                        part_rs<SMALL>(p, pstride), part_cs<SMALL>(p));
-      }
+  const int ma = min(ia, nM), mb = min(ib, nM);
+  const int nmu = (mb - ma) * (ntile > 0 ? ntile : nrb);
+  const int total = nmu + (max(ib, nM) - max(ia, nM)) * nrb;
+  for (int un = next_unit(L.head(), uc); un < total; un = next_unit(L.head(), uc)) {
+    if (un < nmu && ntile > 0) {
+      const int ti = un % ntile;
+      const int o0 = min(pr0 + 16 * ti, pr1 - 16);  // the last tile ends at pr1
+      const int lo = pr0 + 16 * ti;                 // rows below lo belong to the previous tile
+      mfma_down_tile<AD, ED>(p, lp, L, mslot[ma + un / ntile], o0, lo, part);
+    } else {
+      const int s = un < nmu ? mslot[ma + un / nrb] : gslot[max(ia, nM) - nM + (un - nmu) / nrb];
+      const int o0 = pr0 + ((un < nmu ? un : un - nmu) % nrb) * kRowBlock;
+      expert_down_gemv<AD, ED, false>(p, lp, L, s, o0, part + o0, 1, p->H);
     }
   }
 }
@@ -1710,6 +1711,47 @@ __device__ __forceinline__ void p0_tasks(KParams p, KLayer lp, const Lds &L, int
   } else {
     if (!routed) bar_arrive(p, sh, b0 + BAR_ROUTER);
     bar_arrive(p, sh, b0 + BAR_SHARED);
+  }
+}
+
+// General regime: the first listed slot of P1 group gi of nG: the first slot
+// whose cost prefix reaches gi/nG of the total (gi = nG gives nL).
+__device__ __forceinline__ int group_first_slot(const int *cpre, int nL, int gi, int nG) {
+  if (gi >= nG) return nL;
+  const int target = share_lo(cpre[nL], gi, nG);
+  int a = 0, z = nL;  // first i with cpre[i] >= target
+  while (a < z) {
+    const int m = (a + z) >> 1;
+    if (cpre[m] < target) a = m + 1; else z = m;
+  }
+  return a;
+}
+
+// General regime: the P1 tasks of listed slots [ia, ib) whose starting cost
+// falls in [lo, hi).
+template <int AD, int ED>
+__device__ __forceinline__ void p1_cost_range(KParams p, KLayer lp, const Lds &L, int ia, int ib, int lo, int hi) {
+  const int I = p->I, nb = I / 16, nM = L.head().nM;
+  const int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
+  const int *ucnt = L.at<int>(p->o_ucnt), *cpre = L.at<int>(p->o_cpre);
+  // the listed slot holding cost lo: the last i in [ia, ib) with cpre[i] <= lo
+  int a = ia, z = ib;
+  while (z - a > 1) {
+    const int m = (a + z) >> 1;
+    if (cpre[m] <= lo) a = m; else z = m;
+  }
+  for (int i = a; i < ib && cpre[i] < hi; ++i) {
+    const bool mf = i < nM;
+    const int slot = mf ? mslot[i] : gslot[i - nM];
+    const int uc = mf ? mfma_tile_cost(ucnt[slot]) : gemv_pair_cost(ucnt[slot]);
+    const int nt = mf ? nb : I;
+    // tasks j of this slot with cpre[i] + j*uc in [lo, hi)
+    const int j0 = lo > cpre[i] ? (lo - cpre[i] + uc - 1) / uc : 0;
+    const int j1 = min(nt, (hi - cpre[i] + uc - 1) / uc);
+    for (int j = j0; j < j1; ++j) {
+      if (mf) mfma_gu_task<AD, ED>(p, lp, L, slot, j);
+      else expert_gu_task<AD, ED, false>(p, lp, L, slot, j);
+    }
   }
 }
 
@@ -1854,49 +1896,37 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
 
       // P1: routing (one wave per token), gather tables, expert gate/up. The
       // tasks (MFMA tiles of the listed MFMA slots, then GEMV row pairs of the
-      // GEMV slots) have measured costs, and every wave of the grid takes the
-      // tasks whose starting cost falls in its equal, contiguous cost range.
+      // GEMV slots) have measured costs. The listed slots fall into up to
+      // kP1Groups groups of about equal cost, each closed by its barrier; in
+      // every group each wave of the grid takes the tasks whose starting cost
+      // falls in its equal share, so all waves finish group 0 first and the
+      // down projections of early groups overlap the later gate/up work.
       bar_wait(p, sh, b0 + BAR_ROUTER);
       for (int t = wv; t < p->B; t += kWaves) topk_token<false>(p, lp, L, t, blockIdx.x == 0);
       __syncthreads();
       build_tables(p, L);
       classify_slots(p, L);
-      {
-        const int I = p->I, nb = I / 16, nM = sh.nM, nL = sh.nM + sh.nG;
-        const int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
-        const int *ucnt = L.at<int>(p->o_ucnt), *cpre = L.at<int>(p->o_cpre);
-        const int C = cpre[nL];
-        const int lo = share_lo(C, W, NW), hi = share_lo(C, W + 1, NW);
-        // listed slot i holding cost lo: the last i with cpre[i] <= lo
-        int a = 0, z = nL;
-        while (z - a > 1) {
-          const int m = (a + z) >> 1;
-          if (cpre[m] <= lo) a = m; else z = m;
-        }
-        for (int i = a; i < nL && cpre[i] < hi; ++i) {
-          const bool mf = i < nM;
-          const int slot = mf ? mslot[i] : gslot[i - nM];
-          const int uc = mf ? mfma_tile_cost(ucnt[slot]) : gemv_pair_cost(ucnt[slot]);
-          const int nt = mf ? nb : I;
-          // tasks j of this slot with cpre[i] + j*uc in [lo, hi)
-          const int j0 = lo > cpre[i] ? (lo - cpre[i] + uc - 1) / uc : 0;
-          const int j1 = min(nt, (hi - cpre[i] + uc - 1) / uc);
-          for (int j = j0; j < j1; ++j) {
-            if (mf) mfma_gu_task<AD, ED>(p, lp, L, slot, j);
-            else expert_gu_task<AD, ED, false>(p, lp, L, slot, j);
-          }
-        }
+      const int nL = sh.nM + sh.nG, nGr = min(kP1Groups, nL);
+      const int *cpre = L.at<int>(p->o_cpre);
+      for (int gi = 0; gi < nGr; ++gi) {
+        const int ia = group_first_slot(cpre, nL, gi, nGr), ib = group_first_slot(cpre, nL, gi + 1, nGr);
+        const int Clo = cpre[ia], Chi = cpre[ib];
+        p1_cost_range<AD, ED>(p, lp, L, ia, ib, Clo + share_lo(Chi - Clo, W, NW), Clo + share_lo(Chi - Clo, W + 1, NW));
+        bar_arrive(p, sh, b0 + BAR_H + gi);
       }
-      bar_arrive(p, sh, b0 + BAR_H);
 
       // P2: this workgroup's output rows, partial sums in global memory; the
-      // shared expert's rows first, which fills the wait for the expert barrier
+      // shared expert's rows first, then each group's routed rows once its
+      // barrier has passed
       const int r0 = blockIdx.x * p->rows_per_wg;
       const int r1 = min(p->H, r0 + p->rows_per_wg);
       bar_wait(p, sh, b0 + BAR_SHARED);
       if (r0 < r1) shared_down_units<AD, SD, false>(p, lp, L, r0, r1);
-      bar_wait(p, sh, b0 + BAR_H);
-      if (r0 < r1) expert_down_units<AD, ED, false>(p, lp, L, r0, r1);
+      for (int gi = 0; gi < nGr; ++gi) {
+        bar_wait(p, sh, b0 + BAR_H + gi);
+        const int ia = group_first_slot(cpre, nL, gi, nGr), ib = group_first_slot(cpre, nL, gi + 1, nGr);
+        if (r0 < r1) expert_down_listed<AD, ED>(p, lp, L, r0, r1, ia, ib, 2 + gi);
+      }
       __syncthreads();
       if (r0 < r1) combine<AD, false>(p, lp, L, r0, r1);
       __syncthreads();
