@@ -110,6 +110,8 @@ struct Params {
   int H, E, k, I, Is, B, L;
   int route_only;
   int use_mfma;           // general regime: experts with >= kMfmaMin tokens go through MFMA tiles
+  int mfma_sh;            // general regime: the shared expert goes through MFMA tiles
+  int p0_end;             // P0 task indices in [0, p0_end): router slices, then shared slices (VALU)
   int NSR;                // router K-slices
   int NSS;                // shared gate/up K-slices
   int s0;                 // first P0 task index of the shared slices (a multiple of the wave count of a workgroup)
@@ -141,6 +143,7 @@ struct Params {
   int o_hs;                         // small regime: shared h [B][Is] (act)
   int o_slc;                        // slice sums of P0 tasks [round][wave][slw]
   int o_part;                       // small regime: P2 partial sums [rows_per_wg][pstride] fp32
+  int o_red;                        // shared MFMA tiles: partial tiles of the waves [kWaves][16][B] fp32
   LayerPtrs lp[kMaxL];
 };
 
@@ -1278,7 +1281,14 @@ __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Ld
 #ifndef MOE_MFMA_MIN
 #define MOE_MFMA_MIN 3
 #endif
+#ifndef MOE_MFMA_SHARED_MIN
+#define MOE_MFMA_SHARED_MIN 8
+#endif
 constexpr int kMfmaMin = MOE_MFMA_MIN;  // tokens of one expert from which its rows go through MFMA tiles
+constexpr int kMfmaSharedMin = MOE_MFMA_SHARED_MIN;  // batch from which the shared expert goes through MFMA tiles
+
+// workgroup g's contiguous share of n tasks
+__device__ __forceinline__ int share_lo(int n, int g, int G) { return (int)((long long)n * g / G); }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -1474,6 +1484,98 @@ __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &
   });
 }
 
+// Shared expert on MFMA tiles (general regime, bf16). Gate/up tile j is one
+// 16-row A operand: gate rows [8j, 8j + 8) over up rows [8j, 8j + 8), so
+// that g and u of one h element land in the same tile. The tiles are dealt
+// round-robin to the workgroups; the 16 waves of a workgroup split the K
+// columns of a tile in 64-column steps and sum their partial tiles in LDS in
+// wave order.
+__device__ __forceinline__ int shared_tile_row(int Is, int j, int r) { return r < 8 ? 8 * j + r : Is + 8 * j + r - 8; }
+__device__ __forceinline__ int shared_tile_k(int H, int w) { return share_lo(H / 64, w, kWaves) * 64; }
+
+template <int AD>
+__device__ __attribute__((noinline)) void shared_gu_mfma(KParams p_arg, KLayer lp_arg, const Lds &L) {
+  const KParams p = uni(p_arg);
+  const KLayer lp = uni(lp_arg);
+  const int H = p->H, Is = p->Is, B = p->B, lane = lane_id(), wv = wave_id();
+  const int r = lane & 15, kq = lane >> 4;
+  const int k0 = shared_tile_k(H, wv), k1 = shared_tile_k(H, wv + 1);
+  float *red = L.at<float>(p->o_red);  // [kWaves][16][B]
+  const char *xa = (const char *)p->xa + (size_t)k0 * 2;
+  for (int j = blockIdx.x; j < Is / 8; j += p->G) {
+    const char *wb = (const char *)lp->sgu + (size_t)k0 * 2;
+    const unsigned wo[1] = {(unsigned)((size_t)shared_tile_row(Is, j, r) * H * 2)};  // < 4 GB
+    with_token_tiles(B, [&]<int NT>() {
+      unsigned xo[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) xo[t] = (unsigned)min(16 * t + r, B - 1) * (unsigned)H * 2u;
+      f32x4 acc[1][NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mfma_rows<DT_BF16, 1, NT>(uni(wb), wo, k1 - k0, uni(xa), xo, acc);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int c = 16 * t + r;
+        if (c < B) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[(size_t)(wv * 16 + 4 * kq + i) * B + c] = acc[0][t][i];
+        }
+      }
+    });
+    __syncthreads();
+    for (int q = threadIdx.x; q < 8 * B; q += kThreads) {
+      const int jj = q / B, t = q % B;
+      float g = 0.f, u = 0.f;
+      for (int w = 0; w < kWaves; ++w) {
+        g += red[(size_t)(w * 16 + jj) * B + t];
+        u += red[(size_t)(w * 16 + 8 + jj) * B + t];
+      }
+      store_act<AD>(p->hsbuf, (size_t)t * Is + 8 * j + jj, silu_mul(g, u));
+    }
+    __syncthreads();
+  }
+}
+
+// Shared down on MFMA tiles (general regime, bf16): units (half hf of the
+// shared intermediate columns, 16-row tile of rows [pr0, pr1)) through unit
+// counter 0; the partial sums go to the shared expert's partial columns.
+template <int AD>
+__device__ __forceinline__ void shared_down_mfma(KParams p, KLayer lp, const Lds &L, int pr0, int pr1) {
+  const int H = p->H, I = p->I, Is = p->Is, B = p->B, lane = lane_id();
+  const int nsh = Is / I, P = B * p->k;
+  const int r = lane & 15, kq = lane >> 4;
+  const int ntile = (pr1 - pr0 + 15) / 16;
+  float *part = p->partbuf;
+  for (int un = next_unit(L.head(), 0); un < ntile * nsh; un = next_unit(L.head(), 0)) {
+    const int hf = un / ntile, ti = un % ntile;
+    const int o0 = min(pr0 + 16 * ti, pr1 - 16);  // the last tile ends at pr1
+    const int lo = pr0 + 16 * ti;                 // rows below lo belong to the previous tile
+    const char *wb = (const char *)lp->sd + (size_t)hf * I * 2;
+    const char *xb = (const char *)p->hsbuf + (size_t)hf * I * 2;
+    const unsigned wo[1] = {(unsigned)((size_t)(o0 + r) * Is * 2)};
+    with_token_tiles(B, [&]<int NT>() {
+      unsigned xo[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) xo[t] = (unsigned)min(16 * t + r, B - 1) * (unsigned)Is * 2u;
+      f32x4 acc[1][NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mfma_rows<DT_BF16, 1, NT>(uni(wb), wo, I, uni(xb), xo, acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = o0 + 4 * kq + i;
+        if (o >= lo) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const int c = 16 * t + r;
+            if (c < B) part[(size_t)(P + c * nsh + hf) * H + o] = acc[0][t][i];  // column-major
+          }
+        }
+      }
+    });
+  }
+}
+
 // P1 cost of a GEMV row pair of an expert with n tokens and of an MFMA tile
 // (16 pairs, ceil(n/16) token tiles), in tenths of a one-token GEMV pair:
 // per-task timings on MI355X at the K3 share (B=64, every wave streaming).
@@ -1647,19 +1749,19 @@ __device__ __forceinline__ int p0_task(KParams p, int r, int g, int wv) {
 
 // The weights this wave reads first in the next layer's P0 (its router and
 // shared gate/up slices), loaded while the layer barrier is pending.
-template <int RD, int SD>
+template <int RD, int SD, bool MSH>
 __device__ __forceinline__ unsigned prefetch_p0(KParams p, KLayer nl) {
   const int H = p->H, NSR = p->NSR, NSS = p->NSS, E = p->E, Is = p->Is;
   const int nrt = E * NSR;
   unsigned acc = 0;
   for (int r = 0; r < p->p0r; ++r) {
     const int tau = p0_task(p, r, blockIdx.x, wave_id());
-    if (tau < 0 || tau >= p->s0 + Is * NSS) continue;
+    if (tau < 0 || tau >= p->p0_end) continue;
     if (tau < nrt) {
       const int e = tau / NSR, s = tau % NSR;
       const size_t ks = (size_t)(H / NSR) * dsz<RD>();
       acc ^= touch_lines((const char *)nl->rw + (size_t)e * H * dsz<RD>() + s * ks, ks);
-    } else if (tau >= p->s0) {
+    } else if (!MSH && tau >= p->s0) {
       const int j = (tau - p->s0) / NSS, s = (tau - p->s0) % NSS;
       const size_t ks = (size_t)(H / NSS) * dsz<SD>();
       const size_t rowb = (size_t)H * dsz<SD>();
@@ -1667,14 +1769,19 @@ __device__ __forceinline__ unsigned prefetch_p0(KParams p, KLayer nl) {
       acc ^= touch_lines((const char *)nl->sgu + (size_t)(Is + j) * rowb + s * ks, ks);
     }
   }
+  if (MSH && (int)blockIdx.x < Is / 8) {
+    // this wave's columns of the workgroup's first shared MFMA tile
+    const int k0 = shared_tile_k(H, wave_id()), k1 = shared_tile_k(H, wave_id() + 1);
+    for (int r = 0; r < 16; ++r)
+      acc ^= touch_lines((const char *)nl->sgu + (size_t)shared_tile_row(Is, blockIdx.x, r) * H * dsz<SD>() +
+                             (size_t)k0 * dsz<SD>(),
+                         (size_t)(k1 - k0) * dsz<SD>());
+  }
   return acc;
 }
 
 // ---------------------------------------------------------------------------
 // the kernel
-
-// workgroup g's contiguous share of n tasks
-__device__ __forceinline__ int share_lo(int n, int g, int G) { return (int)((long long)n * g / G); }
 
 __device__ __forceinline__ void raise_flag(int &f) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -1691,10 +1798,10 @@ __device__ __forceinline__ void wait_flag(int &f) {
 // shared gate/up slices, arrival at the shared barrier. PUB: the small
 // regime's published stores and arrivals; there the routing waves poll the
 // logits themselves and no router barrier is kept.
-template <int AD, int RD, int SD, bool PUB>
+template <int AD, int RD, int SD, bool PUB, bool MSH>
 __device__ __forceinline__ void p0_tasks(KParams p, KLayer lp, const Lds &L, int b0) {
   SmemHead &sh = L.head();
-  const int nrt = p->E * p->NSR, s0 = p->s0, end = s0 + p->Is * p->NSS;
+  const int nrt = p->E * p->NSR, s0 = p->s0, end = p->p0_end;
   bool routed = false;  // arrived at the router barrier
   for (int r = 0; r < p->p0r; ++r) {
     const int tau = p0_task(p, r, blockIdx.x, wave_id());
@@ -1704,12 +1811,13 @@ __device__ __forceinline__ void p0_tasks(KParams p, KLayer lp, const Lds &L, int
       routed = true;
     }
     if (tau < nrt) router_task<RD, PUB>(p, lp, L, tau, r);
-    else if (tau >= s0) shared_gu_task<AD, SD, PUB>(p, lp, L, tau - s0, r);
+    else if (!MSH && tau >= s0) shared_gu_task<AD, SD, PUB>(p, lp, L, tau - s0, r);
   }
   if constexpr (PUB) {
     bar_arrive_published(p, sh, b0 + BAR_SHARED);
   } else {
     if (!routed) bar_arrive(p, sh, b0 + BAR_ROUTER);
+    if constexpr (MSH) shared_gu_mfma<AD>(p, lp, L);
     bar_arrive(p, sh, b0 + BAR_SHARED);
   }
 }
@@ -1771,7 +1879,7 @@ __device__ __forceinline__ void layer_small(KParams p, KLayer lp, const Lds &L, 
   stage_xhat<AD>(p, lp, L);
 
   // P0
-  p0_tasks<AD, RD, SD, true>(p, lp, L, b0);
+  p0_tasks<AD, RD, SD, true, false>(p, lp, L, b0);
 
   // routing, by the first wave out of P0 work
   int claimed = 0;
@@ -1841,7 +1949,8 @@ __device__ __forceinline__ void layer_small(KParams p, KLayer lp, const Lds &L, 
   __syncthreads();
 }
 
-template <int AD, int RD, int ED, int SD, bool SMALL>
+// SMALL: B <= kSmallB. MSH: general regime with the shared expert on MFMA tiles.
+template <int AD, int RD, int ED, int SD, bool SMALL, bool MSH>
 __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
   // read the parameters in place in the kernarg segment (scalar loads; no private copy)
   (void)params;
@@ -1892,7 +2001,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       bar_wait(p, sh, b0 + BAR_XHAT);
 
       // P0: router slices, then shared gate/up
-      p0_tasks<AD, RD, SD, false>(p, lp, L, b0);
+      p0_tasks<AD, RD, SD, false, MSH>(p, lp, L, b0);
 
       // P1: routing (one wave per token), gather tables, expert gate/up. The
       // tasks (MFMA tiles of the listed MFMA slots, then GEMV row pairs of the
@@ -1921,7 +2030,10 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       const int r0 = blockIdx.x * p->rows_per_wg;
       const int r1 = min(p->H, r0 + p->rows_per_wg);
       bar_wait(p, sh, b0 + BAR_SHARED);
-      if (r0 < r1) shared_down_units<AD, SD, false>(p, lp, L, r0, r1);
+      if (r0 < r1) {
+        if constexpr (MSH) shared_down_mfma<AD>(p, lp, L, r0, r1);
+        else shared_down_units<AD, SD, false>(p, lp, L, r0, r1);
+      }
       for (int gi = 0; gi < nGr; ++gi) {
         bar_wait(p, sh, b0 + BAR_H + gi);
         const int ia = group_first_slot(cpre, nL, gi, nGr), ib = group_first_slot(cpre, nL, gi + 1, nGr);
@@ -1934,7 +2046,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
 
     if (l + 1 < p->L) {
       bar_arrive(p, sh, b0 + BAR_LAYER);
-      sink ^= prefetch_p0<RD, SD>(p, &p->lp[l + 1]);
+      sink ^= prefetch_p0<RD, SD, MSH>(p, &p->lp[l + 1]);
       bar_wait(p, sh, b0 + BAR_LAYER);
     }
   }
@@ -2055,18 +2167,21 @@ WsLayout ws_layout(const moe_layer_desc *d, int B, int L) {
 
 typedef void (*kernel_fn)(Params);
 
-template <bool S>
+template <bool S, bool M>
 kernel_fn pick_kernel_t(const moe_layer_desc *d) {
-  if (d->act == MOE_F32) return moe_kernel<DT_F32, DT_F32, DT_F32, DT_F32, S>;
   if (d->expert == MOE_BF16)
-    return d->router == MOE_F32 ? moe_kernel<DT_BF16, DT_F32, DT_BF16, DT_BF16, S>
-                                : moe_kernel<DT_BF16, DT_BF16, DT_BF16, DT_BF16, S>;
-  return d->router == MOE_F32 ? moe_kernel<DT_BF16, DT_F32, DT_FP8, DT_BF16, S>
-                              : moe_kernel<DT_BF16, DT_BF16, DT_FP8, DT_BF16, S>;
+    return d->router == MOE_F32 ? moe_kernel<DT_BF16, DT_F32, DT_BF16, DT_BF16, S, M>
+                                : moe_kernel<DT_BF16, DT_BF16, DT_BF16, DT_BF16, S, M>;
+  return d->router == MOE_F32 ? moe_kernel<DT_BF16, DT_F32, DT_FP8, DT_BF16, S, M>
+                              : moe_kernel<DT_BF16, DT_BF16, DT_FP8, DT_BF16, S, M>;
 }
 
-kernel_fn pick_kernel(const moe_layer_desc *d, bool small) {
-  return small ? pick_kernel_t<true>(d) : pick_kernel_t<false>(d);
+// msh: the shared expert on MFMA tiles (general regime, bf16 activations only)
+kernel_fn pick_kernel(const moe_layer_desc *d, bool small, bool msh) {
+  if (d->act == MOE_F32)
+    return small ? moe_kernel<DT_F32, DT_F32, DT_F32, DT_F32, true, false>
+                 : moe_kernel<DT_F32, DT_F32, DT_F32, DT_F32, false, false>;
+  return small ? pick_kernel_t<true, false>(d) : msh ? pick_kernel_t<false, true>(d) : pick_kernel_t<false, false>(d);
 }
 
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
@@ -2124,7 +2239,9 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   if (p.G < 1) return fail(MOE_ERR_DEVICE, "device reports no compute units");
   const bool small = small_regime(B);
   p.NSR = k_slices(d->hidden, d->router, 4);
-  p.NSS = d->shared_inter > 0 ? k_slices(d->hidden, d->shared, 2) : 1;
+  // general regime, bf16: the shared expert on MFMA tiles from kMfmaSharedMin tokens
+  p.mfma_sh = (!small && d->act == MOE_BF16 && d->shared_inter > 0 && B >= kMfmaSharedMin) ? 1 : 0;
+  p.NSS = (d->shared_inter > 0 && !p.mfma_sh) ? k_slices(d->hidden, d->shared, 2) : 1;
   // the slices of a row are one workgroup's waves of one round: the shared
   // tasks start at a multiple of the workgroup's wave count, and the rounds
   // must fit the per-round slice counters and LDS slots (else every row is
@@ -2134,7 +2251,8 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   auto plan_slices = [&]() {
     p.s0 = (p.E * p.NSR + kWaves - 1) / kWaves * kWaves;
     p.slw = p.NSS > 1 ? 2 * B : B;
-    const int ntask = p.s0 + p.Is * p.NSS;
+    const int ntask = p.mfma_sh ? p.E * p.NSR : p.s0 + p.Is * p.NSS;
+    p.p0_end = ntask;
     p.p0r = (ntask + NW - 1) / NW;
     // last round: as few waves per workgroup as cover the tasks left, a
     // multiple of the slice counts of the rows in that round
@@ -2180,6 +2298,8 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   }
   p.o_slc = (int)o;
   o = align16(o + (size_t)rounds * kWaves * p.slw * sizeof(float));
+  p.o_red = (int)o;
+  if (p.mfma_sh) o = align16(o + (size_t)kWaves * 16 * B * sizeof(float));
   p.o_part = (int)o;
   // small regime: the workgroup's P2 partial sums stay in LDS (one pass over
   // its rows); general regime: they go to the workspace
@@ -2218,7 +2338,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     lp.logits_out = logits;
     lp.lg = (small && !route_only) ? p.rlog + (size_t)(l & 1) * kSmallB * d->num_experts : p.rfin;
   }
-  kernel_fn fn = pick_kernel(d, small);
+  kernel_fn fn = pick_kernel(d, small, p.mfma_sh != 0);
   if (hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return fail(MOE_ERR_DEVICE, "hipFuncSetAttribute(%zu bytes of LDS) failed", lds);
   // the grid is persistent: one resident workgroup per CU is required
