@@ -110,7 +110,7 @@ struct Params {
   int H, E, k, I, Is, B, L;
   int route_only;
   int use_mfma;           // general regime: experts with >= kMfmaMin tokens go through MFMA tiles
-  int mfma_sh;            // general regime: the shared expert goes through MFMA tiles
+  int mfma_sh;            // general regime: the router and the shared expert go through MFMA tiles
   int p0_end;             // P0 task indices in [0, p0_end): router slices, then shared slices (VALU)
   int NSR;                // router K-slices
   int NSS;                // shared gate/up K-slices
@@ -1484,12 +1484,143 @@ __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &
   });
 }
 
-// Shared expert on MFMA tiles (general regime, bf16). Gate/up tile j is one
-// 16-row A operand: gate rows [8j, 8j + 8) over up rows [8j, 8j + 8), so
-// that g and u of one h element land in the same tile. The tiles are dealt
-// round-robin to the workgroups; the 16 waves of a workgroup split the K
-// columns of a tile in 64-column steps and sum their partial tiles in LDS in
+// P0 on MFMA tiles (general regime from kMfmaSharedMin tokens). Router tile i
+// (16 experts by all tokens over all K columns) goes to workgroup i; the
+// shared gate/up tiles go to the remaining workgroups round-robin, so that a
+// workgroup streams one router tile or up to a few shared tiles. Within a
+// tile the 16 waves split the K columns and sum their partial tiles in LDS in
 // wave order.
+__device__ __forceinline__ int router_tiles(int E) { return (E + 15) / 16; }
+// first shared tile of workgroup g, and the tile stride
+__device__ __forceinline__ int shared_tile0(KParams p, int g) {
+  const int ntr = router_tiles(p->E);
+  return p->G > ntr ? (g >= ntr ? g - ntr : p->Is / 8) : g;
+}
+__device__ __forceinline__ int shared_tile_step(KParams p) {
+  const int ntr = router_tiles(p->E);
+  return p->G > ntr ? p->G - ntr : p->G;
+}
+
+// Router tile: v_mfma_f32_16x16x4_f32 with lane l holding A[l%16][l/16] and
+// B[l/16][l%16] in fp32 (bf16 router weights widen exactly). In a 16-column
+// block lane l loads columns 4(l/16) .. 4(l/16)+3 of its expert row and of
+// its token row, and MFMA m of the block takes component m: k-slot q then
+// holds column 4q + m on both sides. The logits (with the bias) go to rfin.
+__device__ __forceinline__ int router_tile_blk(int H, int w) { return share_lo(H / 16, w, kWaves); }
+
+__device__ __forceinline__ f32x4 mfma4f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// 8-byte load at a uniform base plus a per-lane byte offset (see ld16)
+__device__ __forceinline__ u32x2 ld8_nt(const char *base, unsigned off) {
+  u32x2 v;
+  asm volatile("global_load_dwordx2 %0, %1, %2 nt" : "=v"(v) : "v"(off), "s"(base) : "memory");
+  return v;
+}
+template <int A>
+__device__ __forceinline__ void mfma_wait2(u32x2 (&a)[A]) {
+#pragma unroll
+  for (int i = 0; i < A; ++i) asm volatile("" : "+v"(a[i]));
+}
+
+template <int RD>
+__device__ __attribute__((noinline)) void router_mfma(KParams p_arg, KLayer lp_arg, const Lds &L) {
+  const KParams p = uni(p_arg);
+  const KLayer lp = uni(lp_arg);
+  const int H = p->H, E = p->E, B = p->B, lane = lane_id(), wv = wave_id();
+  const int r = lane & 15, kq = lane >> 4;
+  const int b0 = router_tile_blk(H, wv), b1 = router_tile_blk(H, wv + 1);
+  for (int tile = blockIdx.x; tile < router_tiles(E); tile += p->G) {
+    const unsigned wo = (unsigned)((size_t)min(16 * tile + r, E - 1) * H * dsz<RD>()) + (unsigned)(kq * 4 * dsz<RD>());
+    const char *wb = (const char *)lp->rw;
+    const char *xb = (const char *)p->xhat;
+    float *red = L.at<float>(p->o_red);  // [kWaves][16][B]
+    with_token_tiles(B, [&]<int NT>() {
+      unsigned xo[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) xo[t] = (unsigned)min(16 * t + r, B - 1) * (unsigned)H * 4u + (unsigned)kq * 16u;
+      f32x4 acc[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // two 16-column blocks per wait
+      for (int blk = b0; blk < b1; blk += 2) {
+        const int blk2 = blk + 1 < b1 ? blk + 1 : blk;  // a lone last block loads itself twice, used once
+        const unsigned c[2] = {(unsigned)blk * 16u, (unsigned)blk2 * 16u};
+        u32x4 x[2][NT];
+        float wf[2][4];
+        if constexpr (RD == DT_F32) {
+          u32x4 w[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) w[h] = ld16_nt(uni(wb), wo + c[h] * 4u);
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) x[h][t] = ld16(uni(xb), xo[t] + c[h] * 4u);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          u32x4 wt[1][2] = {{w[0], w[1]}};
+          mfma_wait(wt);
+          mfma_wait(x);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            wf[h][0] = __uint_as_float(wt[0][h].x); wf[h][1] = __uint_as_float(wt[0][h].y);
+            wf[h][2] = __uint_as_float(wt[0][h].z); wf[h][3] = __uint_as_float(wt[0][h].w);
+          }
+        } else {
+          u32x2 w[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) w[h] = ld8_nt(uni(wb), wo + c[h] * 2u);
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) x[h][t] = ld16(uni(xb), xo[t] + c[h] * 4u);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          mfma_wait2(w);
+          mfma_wait(x);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            wf[h][0] = bf_lo(w[h].x); wf[h][1] = bf_hi(w[h].x);
+            wf[h][2] = bf_lo(w[h].y); wf[h][3] = bf_hi(w[h].y);
+          }
+        }
+        const int nh = blk2 != blk ? 2 : 1;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h < nh) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+              for (int t = 0; t < NT; ++t) {
+                const uint32_t xm = m == 0 ? x[h][t].x : m == 1 ? x[h][t].y : m == 2 ? x[h][t].z : x[h][t].w;
+                acc[t] = mfma4f32(wf[h][m], __uint_as_float(xm), acc[t]);
+              }
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int cc = 16 * t + r;
+        if (cc < B) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[(size_t)(wv * 16 + 4 * kq + i) * B + cc] = acc[t][i];
+        }
+      }
+    });
+    __syncthreads();
+    for (int q = threadIdx.x; q < 16 * B; q += kThreads) {
+      const int i = q / B, t = q % B, e = 16 * tile + i;
+      float sum = 0.f;
+      for (int w = 0; w < kWaves; ++w) sum += red[(size_t)(w * 16 + i) * B + t];
+      if (e < E) lp->lg[(size_t)t * E + e] = sum + (lp->rb ? lp->rb[e] : 0.f);
+    }
+    __syncthreads();
+  }
+}
+
+// Shared expert on MFMA tiles (bf16). Gate/up tile j is one 16-row A
+// operand: gate rows [8j, 8j + 8) over up rows [8j, 8j + 8), so that g and u
+// of one h element land in the same tile; the waves split K in 64-column
+// steps.
 __device__ __forceinline__ int shared_tile_row(int Is, int j, int r) { return r < 8 ? 8 * j + r : Is + 8 * j + r - 8; }
 __device__ __forceinline__ int shared_tile_k(int H, int w) { return share_lo(H / 64, w, kWaves) * 64; }
 
@@ -1502,7 +1633,7 @@ __device__ __attribute__((noinline)) void shared_gu_mfma(KParams p_arg, KLayer l
   const int k0 = shared_tile_k(H, wv), k1 = shared_tile_k(H, wv + 1);
   float *red = L.at<float>(p->o_red);  // [kWaves][16][B]
   const char *xa = (const char *)p->xa + (size_t)k0 * 2;
-  for (int j = blockIdx.x; j < Is / 8; j += p->G) {
+  for (int j = shared_tile0(p, blockIdx.x); j < Is / 8; j += shared_tile_step(p)) {
     const char *wb = (const char *)lp->sgu + (size_t)k0 * 2;
     const unsigned wo[1] = {(unsigned)((size_t)shared_tile_row(Is, j, r) * H * 2)};  // < 4 GB
     with_token_tiles(B, [&]<int NT>() {
@@ -1769,11 +1900,22 @@ __device__ __forceinline__ unsigned prefetch_p0(KParams p, KLayer nl) {
       acc ^= touch_lines((const char *)nl->sgu + (size_t)(Is + j) * rowb + s * ks, ks);
     }
   }
-  if (MSH && (int)blockIdx.x < Is / 8) {
+  if (MSH) {
+    // this wave's columns of the workgroup's first router tile
+    if ((int)blockIdx.x < router_tiles(E)) {
+      const int tile = blockIdx.x;
+      const int b0 = router_tile_blk(H, wave_id()), b1 = router_tile_blk(H, wave_id() + 1);
+      for (int r = 0; r < 16 && 16 * tile + r < E; ++r)
+        acc ^= touch_lines((const char *)nl->rw + ((size_t)(16 * tile + r) * H + (size_t)b0 * 16) * dsz<RD>(),
+                           (size_t)(b1 - b0) * 16 * dsz<RD>());
+    }
+  }
+  if (MSH && shared_tile0(p, blockIdx.x) < Is / 8) {
     // this wave's columns of the workgroup's first shared MFMA tile
     const int k0 = shared_tile_k(H, wave_id()), k1 = shared_tile_k(H, wave_id() + 1);
+    const int j = shared_tile0(p, blockIdx.x);
     for (int r = 0; r < 16; ++r)
-      acc ^= touch_lines((const char *)nl->sgu + (size_t)shared_tile_row(Is, blockIdx.x, r) * H * dsz<SD>() +
+      acc ^= touch_lines((const char *)nl->sgu + (size_t)shared_tile_row(Is, j, r) * H * dsz<SD>() +
                              (size_t)k0 * dsz<SD>(),
                          (size_t)(k1 - k0) * dsz<SD>());
   }
@@ -1816,6 +1958,7 @@ __device__ __forceinline__ void p0_tasks(KParams p, KLayer lp, const Lds &L, int
   if constexpr (PUB) {
     bar_arrive_published(p, sh, b0 + BAR_SHARED);
   } else {
+    if constexpr (MSH) router_mfma<RD>(p, lp, L);
     if (!routed) bar_arrive(p, sh, b0 + BAR_ROUTER);
     if constexpr (MSH) shared_gu_mfma<AD>(p, lp, L);
     bar_arrive(p, sh, b0 + BAR_SHARED);
@@ -2240,7 +2383,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   const bool small = small_regime(B);
   p.NSR = k_slices(d->hidden, d->router, 4);
   // general regime, bf16: the shared expert on MFMA tiles from kMfmaSharedMin tokens
-  p.mfma_sh = (!small && d->act == MOE_BF16 && d->shared_inter > 0 && B >= kMfmaSharedMin) ? 1 : 0;
+  p.mfma_sh = (!small && !route_only && d->act == MOE_BF16 && d->shared_inter > 0 && B >= kMfmaSharedMin) ? 1 : 0;
   p.NSS = (d->shared_inter > 0 && !p.mfma_sh) ? k_slices(d->hidden, d->shared, 2) : 1;
   // the slices of a row are one workgroup's waves of one round: the shared
   // tasks start at a multiple of the workgroup's wave count, and the rounds
@@ -2251,7 +2394,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   auto plan_slices = [&]() {
     p.s0 = (p.E * p.NSR + kWaves - 1) / kWaves * kWaves;
     p.slw = p.NSS > 1 ? 2 * B : B;
-    const int ntask = p.mfma_sh ? p.E * p.NSR : p.s0 + p.Is * p.NSS;
+    const int ntask = p.mfma_sh ? 0 : p.s0 + p.Is * p.NSS;
     p.p0_end = ntask;
     p.p0r = (ntask + NW - 1) / NW;
     // last round: as few waves per workgroup as cover the tasks left, a
@@ -2261,6 +2404,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     p.p0w = ((left + p.G - 1) / p.G + unit - 1) / unit * unit;
     if (p.p0w > kWaves) p.p0w = kWaves;
     rounds = (p.NSR > 1 || p.NSS > 1) ? p.p0r : 0;
+    if (ntask == 0) p.p0r = p.p0w = rounds = 0;
   };
   plan_slices();
   if (rounds > kMaxRounds || (size_t)rounds * kWaves * p.slw * sizeof(float) > 16384) {
