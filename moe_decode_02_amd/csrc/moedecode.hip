@@ -1670,6 +1670,8 @@ __device__ __attribute__((noinline)) void shared_gu_mfma(KParams p_arg, KLayer l
 // Shared down on MFMA tiles (general regime, bf16): units (half hf of the
 // shared intermediate columns, 16-row tile of rows [pr0, pr1)) through unit
 // counter 0; the partial sums go to the shared expert's partial columns.
+// Needs pr1 >= 16 (the launch enables this path only when every workgroup
+// owns at least 16 rows).
 template <int AD>
 __device__ __forceinline__ void shared_down_mfma(KParams p, KLayer lp, const Lds &L, int pr0, int pr1) {
   const int H = p->H, I = p->I, Is = p->Is, B = p->B, lane = lane_id();
@@ -2381,9 +2383,19 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   p.G = di.cus;
   if (p.G < 1) return fail(MOE_ERR_DEVICE, "device reports no compute units");
   const bool small = small_regime(B);
+  // P2 output rows per workgroup, a multiple of the GEMV row block
+  int rpw = (p.H + p.G - 1) / p.G;
+  rpw = (rpw + kRowBlock - 1) / kRowBlock * kRowBlock;
+  p.rows_per_wg = rpw;
   p.NSR = k_slices(d->hidden, d->router, 4);
-  // general regime, bf16: the shared expert on MFMA tiles from kMfmaSharedMin tokens
-  p.mfma_sh = (!small && !route_only && d->act == MOE_BF16 && d->shared_inter > 0 && B >= kMfmaSharedMin) ? 1 : 0;
+  // general regime, bf16: the router and the shared expert on MFMA tiles
+  // from kMfmaSharedMin tokens. The shared down tiles are 16 rows that end at
+  // the workgroup's last row, so every workgroup must own at least 16 rows
+  // (with fewer, the first workgroup's tile would start at a negative row).
+  p.mfma_sh = (!small && !route_only && d->act == MOE_BF16 && d->shared_inter > 0 && B >= kMfmaSharedMin &&
+               rpw >= 16)
+                  ? 1
+                  : 0;
   p.NSS = (d->shared_inter > 0 && !p.mfma_sh) ? k_slices(d->hidden, d->shared, 2) : 1;
   // the slices of a row are one workgroup's waves of one round: the shared
   // tasks start at a multiple of the workgroup's wave count, and the rounds
@@ -2411,9 +2423,6 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     p.NSR = p.NSS = 1;
     plan_slices();
   }
-  int rpw = (p.H + p.G - 1) / p.G;
-  rpw = (rpw + kRowBlock - 1) / kRowBlock * kRowBlock;
-  p.rows_per_wg = rpw;
 
   // LDS carve-up
   const int E = d->num_experts, P = B * d->top_k, H = d->hidden;
