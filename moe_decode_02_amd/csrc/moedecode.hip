@@ -195,13 +195,6 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          false);
 }
 
-// OCP e4m3fn byte -> fp32, exact: the 7 magnitude bits land in the fp32
-// exponent/mantissa fields (exponent bias 127 instead of 7, so a factor 2^-120),
-// subnormal codes land on fp32 subnormals with the same factor.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  const float mag = __uint_as_float((b & 0x7Fu) << 20) * 0x1p120f;
-  return (b & 0x80u) ? -mag : mag;
-}
 
 template <int D> __device__ __forceinline__ float load_act(const void *p, size_t i) {
   if constexpr (D == DT_F32) return ((const float *)p)[i];
@@ -271,23 +264,47 @@ template <> struct Chunk<DT_BF16, DT_F32> {
   }
 };
 
+// 8 e4m3 codes (two words) -> 8 bf16 (exact: e4m3 values are bf16 values)
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+  r.y = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+  r.z = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
+  r.w = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
+  return r;
+}
+
+// 16 e4m3 codes against 16 bf16 activations: the codes become bf16 pairs
+// through the hardware conversion (exact), then bf16 dot2 as for bf16 weights
+// (a software decode costs ~6 VALU operations per code, which made the fp8
+// GEMV ALU-bound well below the HBM rate).
 template <> struct Chunk<DT_FP8, DT_BF16> {
   static constexpr int NX = 2;
-  __device__ static __forceinline__ float dot4(uint32_t w, uint32_t x01, uint32_t x23, float a) {
-    a = fmaf(e4m3_to_f32(w & 0xFFu), bf_lo(x01), a);
-    a = fmaf(e4m3_to_f32((w >> 8) & 0xFFu), bf_hi(x01), a);
-    a = fmaf(e4m3_to_f32((w >> 16) & 0xFFu), bf_lo(x23), a);
-    a = fmaf(e4m3_to_f32(w >> 24), bf_hi(x23), a);
-    return a;
-  }
   __device__ static __forceinline__ float dot(const u32x4 &w, const u32x4 *x, float a) {
-    a = dot4(w.x, x[0].x, x[0].y, a);
-    a = dot4(w.y, x[0].z, x[0].w, a);
-    a = dot4(w.z, x[1].x, x[1].y, a);
-    a = dot4(w.w, x[1].z, x[1].w, a);
+    const u32x4 lo = fp8x8_to_bf16(w.x, w.y), hi = fp8x8_to_bf16(w.z, w.w);
+    a = dot2_bf16(lo.x, x[0].x, a);
+    a = dot2_bf16(lo.y, x[0].y, a);
+    a = dot2_bf16(lo.z, x[0].z, a);
+    a = dot2_bf16(lo.w, x[0].w, a);
+    a = dot2_bf16(hi.x, x[1].x, a);
+    a = dot2_bf16(hi.y, x[1].y, a);
+    a = dot2_bf16(hi.z, x[1].z, a);
+    a = dot2_bf16(hi.w, x[1].w, a);
     return a;
   }
 };
+
+// A bf16 scale of fp8 weights is loaded when a task starts and applied when
+// it ends. It stays a raw word until late_scale(), whose empty asm keeps the
+// conversion, and with it the wait for the load, after the task's weight
+// loads; converted at once, each scale load cost a full memory round trip
+// before the first weight load was issued.
+__device__ __forceinline__ float late_scale(uint32_t raw) {
+  asm volatile("" : "+v"(raw));
+  return __uint_as_float(raw << 16);
+}
 
 // weight chunk: streamed once, so loaded non-temporal
 __device__ __forceinline__ u32x4 ldw(const char *p) { return __builtin_nontemporal_load((const u32x4 *)p); }
@@ -1120,12 +1137,12 @@ __device__ __forceinline__ void expert_gu_task(KParams p, KLayer lp, const Lds &
   const size_t rowb = (size_t)H * dsz<ED>();
   const char *gu = (const char *)lp->egu + (size_t)e * 2 * I * rowb;
   const char *const wrow[2] = {gu + (size_t)j * rowb, gu + (size_t)(I + j) * rowb};
-  float gs = 1.f, us = 1.f;
+  uint32_t graw = 0x3F80u, uraw = 0x3F80u;
   if constexpr (ED == DT_FP8) {
-    // e4m3_to_f32 is exact, so the bf16 row scale multiplies the finished dot
+    // the code conversion is exact, so the bf16 row scale multiplies the finished dot
     const uint16_t *sc = lp->egus + (size_t)e * (2 * I / 128);
-    gs = __uint_as_float((uint32_t)sc[j / 128] << 16);
-    us = __uint_as_float((uint32_t)sc[(I + j) / 128] << 16);
+    graw = sc[j / 128];
+    uraw = sc[(I + j) / 128];
   }
   for_token_groups(n, [&]<int TG>(int t0, int nt) {
     typename XSrc<XL>::ptr xr[TG];
@@ -1141,8 +1158,11 @@ __device__ __forceinline__ void expert_gu_task(KParams p, KLayer lp, const Lds &
     rows_dot<ED, AD, XL, 2, seg_gu<ED, TG>(), TG>(wrow, 0, H, xr, acc);
 #pragma unroll
     for (int t = 0; t < TG; ++t) {
-      const float g = wave_sum63(acc[0][t]) * gs;
-      const float uu = wave_sum63(acc[1][t]) * us;
+      float g = wave_sum63(acc[0][t]), uu = wave_sum63(acc[1][t]);
+      if constexpr (ED == DT_FP8) {
+        g *= late_scale(graw);
+        uu *= late_scale(uraw);
+      }
       if (t < nt && lane_id() == 63) {
         const float h = silu_mul(g, uu);
         // h in the act dtype (published in the small regime)
@@ -1188,12 +1208,13 @@ __device__ __forceinline__ void stage_shared_h_wave(KParams p, const Lds &L) {
 }
 
 // One 4-row unit of a [rows][K] down matrix: row pointers wrow, columns
-// [0, I) of x rows xr (TG tokens); writes the row sums times sc[r] to
+// [0, I) of x rows xr (TG tokens); writes the row sums (fp8 weights: times
+// the bf16 scale word sraw, common to the unit's rows) to
 // prow[(o0 + r - o0) * rs + col[t] * cs] (rs, cs: row and column strides of
 // the partial-sum buffer).
 template <int WD, int AD, bool XL, int TG>
 __device__ __forceinline__ void down_unit(const char *const (&wrow)[kRowBlock], int I,
-                                          const typename XSrc<XL>::ptr (&xr)[TG], const float (&sc)[kRowBlock],
+                                          const typename XSrc<XL>::ptr (&xr)[TG], uint32_t sraw,
                                           float *prow, int rs, int cs, const int (&col)[TG], int nt) {
 #pragma unroll
   for (int r0 = 0; r0 < kRowBlock; r0 += kDownRows) {
@@ -1210,7 +1231,8 @@ __device__ __forceinline__ void down_unit(const char *const (&wrow)[kRowBlock], 
     for (int r = 0; r < kDownRows; ++r)
 #pragma unroll
       for (int t = 0; t < TG; ++t) {
-        const float v = wave_sum63(acc[r][t]) * sc[r0 + r];
+        float v = wave_sum63(acc[r][t]);
+        if constexpr (WD == DT_FP8) v *= late_scale(sraw);
         if (t < nt && lane_id() == 63) prow[(r0 + r) * rs + col[t] * cs] = v;
       }
   }
@@ -1244,7 +1266,6 @@ __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Ld
   const int nrb = (pr1 - pr0) / kRowBlock;
   float *part = part_base<SMALL>(p, L);
   const int prb = SMALL ? pr0 : 0;
-  const float one[kRowBlock] = {1.f, 1.f, 1.f, 1.f};
   for (int un = next_unit(L.head(), 0); un < nrb * nsh; un = next_unit(L.head(), 0)) {
     const int hf = un / nrb, rb = un % nrb;
     const int o0 = pr0 + rb * kRowBlock;
@@ -1262,7 +1283,7 @@ __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Ld
         else xr[t] = (const char *)p->hsbuf + ((size_t)tt * Is + (size_t)hf * I) * dsz<AD>();
         col[t] = P + (t0 + t) * nsh + hf;
       }
-      down_unit<SD, AD, SMALL, TG>(wrow, I, xr, one, part + (size_t)(o0 - prb) * part_rs<SMALL>(p, pstride),
+      down_unit<SD, AD, SMALL, TG>(wrow, I, xr, 0x3F80u, part + (size_t)(o0 - prb) * part_rs<SMALL>(p, pstride),
                                    part_rs<SMALL>(p, pstride), part_cs<SMALL>(p), col, nt);
     });
   }
@@ -1296,18 +1317,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
-}
-
-// 8 e4m3 codes (two words) -> 8 bf16 (exact: e4m3 values are bf16 values)
-__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
-  u32x4 r;
-  r.x = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-  r.y = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
-  r.z = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
-  r.w = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
-  return r;
 }
 
 // 16-byte loads at a uniform base plus a per-lane 32-bit byte offset, issued
@@ -1416,11 +1425,11 @@ __device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L,
   const size_t rowb = (size_t)H * dsz<ED>();
   const char *gu = (const char *)lp->egu + (size_t)e * 2 * I * rowb;  // < 4 GB: 32-bit offsets
   const unsigned wo[2] = {(unsigned)((16 * jb + r) * rowb), (unsigned)((I + 16 * jb + r) * rowb)};
-  float gs = 1.f, us = 1.f;
+  uint32_t graw = 0x3F80u, uraw = 0x3F80u;
   if constexpr (ED == DT_FP8) {
     const uint16_t *sc = lp->egus + (size_t)e * (2 * I / 128);
-    gs = __uint_as_float((uint32_t)sc[(16 * jb) / 128] << 16);
-    us = __uint_as_float((uint32_t)sc[(I + 16 * jb) / 128] << 16);
+    graw = sc[(16 * jb) / 128];
+    uraw = sc[(I + 16 * jb) / 128];
   }
   with_token_tiles(n, [&]<int NT>() {
     unsigned xo[NT];
@@ -1442,7 +1451,8 @@ __device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L,
         const int slot = pl[c];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          store_act<AD>(p->hbuf, (size_t)slot * I + 16 * jb + 4 * kq + i, silu_mul(acc[0][t][i] * gs, acc[1][t][i] * us));
+          store_act<AD>(p->hbuf, (size_t)slot * I + 16 * jb + 4 * kq + i,
+                        silu_mul(acc[0][t][i] * late_scale(graw), acc[1][t][i] * late_scale(uraw)));
       }
     }
   });
@@ -1460,6 +1470,12 @@ __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &
   const int r = lane & 15, kq = lane >> 4;
   const char *wbase = (const char *)lp->ed + (size_t)e * H * I * dsz<ED>();  // < 4 GB: 32-bit offsets
   const unsigned wo[1] = {(unsigned)((size_t)(o0 + r) * I * dsz<ED>())};
+  // scales of the lane's output rows o0 + 4 kq + i, applied after the tile
+  uint32_t sraw[4] = {0x3F80u, 0x3F80u, 0x3F80u, 0x3F80u};
+  if constexpr (ED == DT_FP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sraw[i] = lp->eds[(size_t)e * (H / 128) + (o0 + 4 * kq + i) / 128];
+  }
   with_token_tiles(n, [&]<int NT>() {
     unsigned xo[NT];
 #pragma unroll
@@ -1472,7 +1488,7 @@ __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &
     for (int i = 0; i < 4; ++i) {
       const int o = o0 + 4 * kq + i;
       float sc = 1.f;
-      if constexpr (ED == DT_FP8) sc = __uint_as_float((uint32_t)lp->eds[(size_t)e * (H / 128) + o / 128] << 16);
+      if constexpr (ED == DT_FP8) sc = late_scale(sraw[i]);
       if (o >= lo) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -1772,13 +1788,11 @@ __device__ __forceinline__ void expert_down_gemv(KParams p, KLayer lp, const Lds
   const int n = ucnt[s];
   const int *pl = plist + ustart[s];
   const char *wrow[kRowBlock];
-  float sc[kRowBlock];
 #pragma unroll
-  for (int r = 0; r < kRowBlock; ++r) {
-    wrow[r] = (const char *)lp->ed + ((size_t)e * H + o0 + r) * I * dsz<ED>();
-    sc[r] = 1.f;
-    if constexpr (ED == DT_FP8) sc[r] = __uint_as_float((uint32_t)lp->eds[(size_t)e * (H / 128) + (o0 + r) / 128] << 16);
-  }
+  for (int r = 0; r < kRowBlock; ++r) wrow[r] = (const char *)lp->ed + ((size_t)e * H + o0 + r) * I * dsz<ED>();
+  // o0 is a multiple of the row block, which divides the 128-row scale group
+  uint32_t sraw = 0x3F80u;
+  if constexpr (ED == DT_FP8) sraw = lp->eds[(size_t)e * (H / 128) + o0 / 128];
   for_token_groups(n, [&]<int TG>(int t0, int nt) {
     typename XSrc<false>::ptr xr[TG];
     int col[TG];
@@ -1787,7 +1801,7 @@ __device__ __forceinline__ void expert_down_gemv(KParams p, KLayer lp, const Lds
       col[t] = pl[t0 + (t < nt ? t : 0)];
       xr[t] = (const char *)p->hbuf + (size_t)col[t] * I * dsz<AD>();
     }
-    down_unit<ED, AD, false, TG>(wrow, I, xr, sc, prow, rs, cs, col, nt);
+    down_unit<ED, AD, false, TG>(wrow, I, xr, sraw, prow, rs, cs, col, nt);
   });
 }
 
@@ -1838,9 +1852,11 @@ __device__ __forceinline__ void expert_down_listed(KParams p, KLayer lp, const L
   }
 }
 
-// y = x + shared + sum_i w_i d_i (rank order i) for rows [pr0, pr1)
+// y = x + shared + sum_i w_i d_i (rank order i) for rows [pr0, pr1). PUB:
+// y is the next layer's input, written with device-coherent stores so that
+// the layer barrier needs no L2 write-back.
 template <int AD, bool SMALL>
-__device__ __forceinline__ void combine(KParams p, KLayer lp, const Lds &L, int pr0, int pr1) {
+__device__ __forceinline__ void combine(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, bool pub) {
   const int H = p->H, k = p->k, B = p->B;
   const int nsh = p->Is / p->I, P = B * k, pstride = P + B * nsh;
   const float *part = part_base<SMALL>(p, L);
@@ -1857,7 +1873,8 @@ __device__ __forceinline__ void combine(KParams p, KLayer lp, const Lds &L, int 
     float rt = 0.f;
     for (int i = 0; i < k; ++i) rt = fmaf(sel_w[t * k + i], pp[(size_t)(t * k + i) * cs], rt);
     const float v = load_act<AD>(lp->x, (size_t)t * H + o) + sh + rt;
-    store_act<AD>(lp->y, (size_t)t * H + o, v);
+    if (pub) publish_act<AD>(lp->y, (size_t)t * H + o, v);
+    else store_act<AD>(lp->y, (size_t)t * H + o, v);
   }
 }
 
@@ -2090,7 +2107,7 @@ __device__ __forceinline__ void layer_small(KParams p, KLayer lp, const Lds &L, 
     for (int i = share_lo(n, g, G) + lane_id(); i < share_lo(n, g + 1, G); i += 64) publish(lp->lg + i, 0.f);
   }
   __syncthreads();
-  if (r0 < r1) combine<AD, true>(p, lp, L, r0, r1);
+  if (r0 < r1) combine<AD, true>(p, lp, L, r0, r1, b0 / kBarPerLayer + 1 < p->L);
   __syncthreads();
 }
 
@@ -2185,12 +2202,15 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
         if (r0 < r1) expert_down_listed<AD, ED>(p, lp, L, r0, r1, ia, ib, 2 + gi);
       }
       __syncthreads();
-      if (r0 < r1) combine<AD, false>(p, lp, L, r0, r1);
+      if (r0 < r1) combine<AD, false>(p, lp, L, r0, r1, l + 1 < p->L);
       __syncthreads();
     }
 
     if (l + 1 < p->L) {
-      bar_arrive(p, sh, b0 + BAR_LAYER);
+      // the next layer reads, before its own first barrier, only y (published
+      // by the combine) and values published by this layer; its workspace
+      // buffers are rewritten before other workgroups read them
+      bar_arrive_published(p, sh, b0 + BAR_LAYER);
       sink ^= prefetch_p0<RD, SD, MSH>(p, &p->lp[l + 1]);
       bar_wait(p, sh, b0 + BAR_LAYER);
     }
