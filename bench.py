@@ -15,6 +15,10 @@ workload's seed) and their own token batch; the routed-expert tensor is
 common to them (the routing of different instances picks nearly disjoint
 experts).
 
+With --unfused a step is one call of moe_decode_layer_unfused instead: the
+same layer as ten kernel launches with every intermediate in device memory,
+the baseline the fused kernel is measured against.
+
 `value` is tokens per second (B / step time). The roofline object gives the
 weight bytes the step must touch (router + shared + gain + every distinct
 selected expert, each counted once per step) over the measured kernel time,
@@ -59,6 +63,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=8, help="layer instances the timed loop rotates over")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the multi-launch path (moe_decode_layer_unfused) instead of the fused kernel")
     return ap.parse_args()
 
 
@@ -209,6 +215,11 @@ def main() -> int:
     idx = [torch.zeros((L, B, w.k), dtype=torch.int32, device=dev) for _ in range(C)]
     wts = [torch.zeros((L, B, w.k), dtype=torch.float32, device=dev) for _ in range(C)]
     ws = workspace(d, B, L, dev)
+    if args.unfused:
+        if L != 1:
+            log("bench: --unfused times one layer; the workload is a stack")
+            return 2
+        ws_unf = torch.empty(md.moe_unfused_workspace_bytes(d, B), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"bench: inputs ready in {time.time() - t0:.1f} s, {torch.cuda.memory_allocated() / 2**30:.1f} GiB on the GPU")
 
@@ -216,7 +227,10 @@ def main() -> int:
 
     def step(i):
         c = i % C
-        if L == 1:
+        if args.unfused:
+            md.moe_decode_layer_unfused(d, insts[c][0].weights, xs[c], ys[c], B, idx[c], wts[c], ws_unf,
+                                        stream=stream)
+        elif L == 1:
             md.moe_decode_layer(d, insts[c][0].weights, xs[c], ys[c], B, idx[c], wts[c], ws, stream=stream)
         else:
             md.moe_decode_stack(d, [li.weights for li in insts[c]], xs[c], ys[c], B, idx[c], wts[c], ws,
@@ -285,7 +299,7 @@ def main() -> int:
     # HBM bytes per launch measured by the committed FETCH_SIZE / WRITE_SIZE
     # profile of this workload, if it was taken on the current kernel source
     from moe_decode_02_amd.profiling import read_traffic
-    tr = read_traffic(os.path.join(ROOT, "profiles", f"moe_kernel_{w.name}_B{B}_traffic.txt"))
+    tr = None if args.unfused else read_traffic(os.path.join(ROOT, "profiles", f"moe_kernel_{w.name}_B{B}_traffic.txt"))
     hbm_bytes = None if tr is None else tr["read"] + tr["write"]
     traffic = None if tr is None else hbm_bytes / (ms_step * 1e-3) / 1e9
 
@@ -306,7 +320,8 @@ def main() -> int:
         "dtype": {synth.F32: "f32", synth.BF16: "bf16", synth.FP8: "fp8e4m3"}[w.expert],
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {WORKLOAD_NOTES[w.name]}", "batch": B, "layers": L,
-                   "rotated_instances": C, "kernel_launches_per_step": 1},
+                   "rotated_instances": C, "path": "unfused" if args.unfused else "fused",
+                   "kernel_launches_per_step": (10 if w.Is > 0 else 7) if args.unfused else 1},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes, "hbm_bytes_per_launch": hbm_bytes},

@@ -75,6 +75,7 @@ class moe_layer_weights(ctypes.Structure):
 
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_decode_layer", "moe_decode_stack",
+           "moe_unfused_workspace_bytes", "moe_decode_layer_unfused",
            "moe_check_workspace", "moe_status_string", "moe_last_error")
 
 
@@ -93,6 +94,10 @@ def lib():
     L.moe_decode_layer.restype = ctypes.c_int
     L.moe_decode_stack.argtypes = [D, Wt, i32, vp, vp, i32, vp, vp, vp, sz, vp]
     L.moe_decode_stack.restype = ctypes.c_int
+    L.moe_unfused_workspace_bytes.argtypes = [D, i32]
+    L.moe_unfused_workspace_bytes.restype = sz
+    L.moe_decode_layer_unfused.argtypes = [D, Wt, vp, vp, i32, vp, vp, vp, sz, vp]
+    L.moe_decode_layer_unfused.restype = ctypes.c_int
     L.moe_check_workspace.argtypes = [vp, sz, vp]
     L.moe_check_workspace.restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
@@ -168,6 +173,19 @@ def moe_decode_stack(desc, layers, x, y, B, topk_idx, topk_w, ws, ws_bytes=None,
     st = lib().moe_decode_stack(ctypes.byref(desc), arr, len(layers), _addr(x), _addr(y), B,
                                 _addr(topk_idx), _addr(topk_w), _addr(ws),
                                 _bytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
+    if check:
+        _check(st)
+    return st
+
+
+def moe_unfused_workspace_bytes(desc: moe_layer_desc, max_tokens: int) -> int:
+    return lib().moe_unfused_workspace_bytes(ctypes.byref(desc), max_tokens)
+
+
+def moe_decode_layer_unfused(desc, weights, x, y, B, topk_idx, topk_w, ws, ws_bytes=None, stream=None, check=True):
+    st = lib().moe_decode_layer_unfused(ctypes.byref(desc), ctypes.byref(weights), _addr(x), _addr(y), B,
+                                        _addr(topk_idx), _addr(topk_w), _addr(ws),
+                                        _bytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
     if check:
         _check(st)
     return st

@@ -48,6 +48,8 @@
 // kernels).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include <stdarg.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -2230,6 +2232,149 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Multi-launch path (moe_decode_layer_unfused): the same layer as ten
+// separate kernels with every intermediate (x-hat, logits, routing, gate/up
+// outputs, h, down outputs, the shared expert's) in HBM, the way an unfused
+// decode step runs it. It is the measured baseline of the fusion above. Its
+// GEMVs use the same streaming core: one wave per weight row, activation rows
+// from global memory, the expert weights read once per (token, expert) pair.
+
+constexpr int kUfThreads = 256;
+constexpr int kUfRows = kUfThreads / 64;  // GEMV kernels: one weight row per wave
+
+// x-hat of token blockIdx.x: fp32 (router input) and act (FFN input; for
+// fp32 activations xa is xf)
+template <int AD>
+__global__ void __launch_bounds__(kUfThreads) uf_rmsnorm(const void *x, const void *gamma, int H, float eps,
+                                                          float *xf, void *xa) {
+  __shared__ float red[kUfRows];
+  const size_t t = blockIdx.x;
+  float ss = 0.f;
+  for (int h = threadIdx.x; h < H; h += kUfThreads) {
+    const float v = load_act<AD>(x, t * H + h);
+    ss = fmaf(v, v, ss);
+  }
+  ss = readlane_f(wave_sum63(ss), 63);
+  if (lane_id() == 0) red[wave_id()] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < kUfRows; ++w) tot += red[w];
+  const float r = 1.0f / sqrtf(tot / (float)H + eps);
+  for (int h = threadIdx.x; h < H; h += kUfThreads) {
+    const float v = load_act<AD>(x, t * H + h) * r * load_act<AD>(gamma, h);
+    xf[t * H + h] = v;
+    if constexpr (AD != DT_F32) store_act<AD>(xa, t * H + h, v);
+  }
+}
+
+// Gathered GEMV. Job j (blockIdx.y) uses matrix m = idx ? idx[j] : 0 and,
+// for TG = 1, activation row j / x_div; for TG > 1, rows TG j .. TG j + TG - 1
+// (those below nx). out[row][r] = scale * sum_k W_m[r][k] X[row][k] + bias[r];
+// fp8 weights take the bf16 scale of their 128-row group.
+struct UfGemv {
+  const char *w;          // matrix 0, rows of K elements
+  size_t mat_bytes;       // bytes from one matrix to the next
+  const int32_t *idx;     // [jobs] matrix of each job, or NULL
+  int R, K;               // rows, columns
+  const char *x;          // activation rows of K elements
+  int x_div, nx;
+  const uint16_t *scale;  // fp8: [m][R / 128] bf16
+  const float *bias;      // [R] or NULL
+  float *out;             // [rows][R]
+};
+
+template <int WD, int XD, int TG>
+__global__ void __launch_bounds__(kUfThreads) uf_gemv(UfGemv a) {
+  const int r = blockIdx.x * kUfRows + wave_id(), j = blockIdx.y;
+  if (r >= a.R) return;
+  const int m = a.idx ? a.idx[j] : 0;
+  const char *const wrow[1] = {a.w + (size_t)m * a.mat_bytes + (size_t)r * a.K * dsz<WD>()};
+  const char *xr[TG];
+  int row[TG];
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    row[t] = TG == 1 ? j / a.x_div : min(TG * j + t, a.nx - 1);
+    xr[t] = a.x + (size_t)row[t] * a.K * dsz<XD>();
+  }
+  float acc[1][TG];
+#pragma unroll
+  for (int t = 0; t < TG; ++t) acc[0][t] = 0.f;
+  rows_dot<WD, XD, false, 1, 2, TG>(wrow, 0, a.K, xr, acc);
+  float sc = 1.f;
+  if constexpr (WD == DT_FP8) sc = __uint_as_float((uint32_t)a.scale[(size_t)m * (a.R / 128) + r / 128] << 16);
+  const float b = a.bias ? a.bias[r] : 0.f;
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    const float v = wave_sum63(acc[0][t]) * sc + b;
+    const int orow = TG == 1 ? j : TG * j + t;
+    if (lane_id() == 63 && (TG == 1 || orow < a.nx)) a.out[(size_t)orow * a.R + r] = v;
+  }
+}
+
+// top-k of token blockIdx.x (one wave): k rounds of wave argmax (larger
+// logit, then lower index), then the softmax restricted to the selection
+__global__ void __launch_bounds__(64) uf_topk(const float *logits, int E, int k, int32_t *idx, float *w) {
+  const int t = blockIdx.x, lane = lane_id();
+  float v[kMaxE / 64];
+#pragma unroll
+  for (int q = 0; q < kMaxE / 64; ++q) {
+    const int e = lane + 64 * q;
+    v[q] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+  }
+  float my_l = 0.f;
+  int my_e = 0;
+  for (int i = 0; i < k; ++i) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int q = 0; q < kMaxE / 64; ++q)
+      if (lane + 64 * q < E && (v[q] > bv || bi == 0x7FFFFFFF)) {
+        bv = v[q];
+        bi = lane + 64 * q;
+      }
+    wave_argmax(bv, bi);
+    if (lane == i) {
+      my_l = bv;
+      my_e = bi;
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxE / 64; ++q)
+      if (lane + 64 * q == bi) v[q] = -INFINITY;
+  }
+  const float lmax = readlane_f(my_l, 0);
+  const float pe = lane < k ? expf(my_l - lmax) : 0.f;
+  const float sum = readlane_f(wave_sum63(pe), 63);
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = my_e;
+    w[(size_t)t * k + lane] = pe / sum;
+  }
+}
+
+// h[j][i] = act(SiLU(g) u) from the gate/up outputs gu[j] = (g[0..I), u[0..I))
+template <int AD>
+__global__ void __launch_bounds__(kUfThreads) uf_silu_mul(const float *gu, int I, int J, void *h) {
+  const size_t n = (size_t)J * I;
+  for (size_t q = (size_t)blockIdx.x * kUfThreads + threadIdx.x; q < n; q += (size_t)gridDim.x * kUfThreads) {
+    const size_t j = q / I, i = q % I;
+    store_act<AD>(h, q, silu_mul(gu[j * 2 * I + i], gu[j * 2 * I + I + i]));
+  }
+}
+
+// y[t][h] = act(x + s + sum_i w[t][i] d[t k + i][h]) (s: shared expert or NULL)
+template <int AD>
+__global__ void __launch_bounds__(kUfThreads) uf_combine(const void *x, const float *s, const float *d,
+                                                          const float *w, int H, int k, int B, void *y) {
+  const size_t n = (size_t)B * H;
+  for (size_t q = (size_t)blockIdx.x * kUfThreads + threadIdx.x; q < n; q += (size_t)gridDim.x * kUfThreads) {
+    const size_t t = q / H, h = q % H;
+    float rt = 0.f;
+    for (int i = 0; i < k; ++i) rt = fmaf(w[t * k + i], d[(t * k + i) * H + h], rt);
+    store_act<AD>(y, q, load_act<AD>(x, q) + (s ? s[q] : 0.f) + rt);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host runtime
 
@@ -2525,6 +2670,121 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   return MOE_OK;
 }
 
+
+// workspace of the multi-launch path
+struct UfLayout {
+  size_t xf, xa, lg, idx, w, gu, h, d, sgu, hs, ds, total;
+};
+
+UfLayout uf_layout(const moe_layer_desc *d, int B) {
+  UfLayout u{};
+  const size_t act = (size_t)dsize(d->act), H = (size_t)d->hidden, P = (size_t)B * d->top_k;
+  const size_t I = (size_t)d->expert_inter, Is = (size_t)d->shared_inter;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += up256(bytes > 0 ? bytes : 1); return o; };
+  u.xf = take((size_t)B * H * 4);
+  u.xa = take((size_t)B * H * act);
+  u.lg = take((size_t)B * d->num_experts * 4);
+  u.idx = take(P * 4);
+  u.w = take(P * 4);
+  u.gu = take(P * 2 * I * 4);
+  u.h = take(P * I * act);
+  u.d = take(P * H * 4);
+  u.sgu = take((size_t)B * 2 * Is * 4);
+  u.hs = take((size_t)B * Is * act);
+  u.ds = take((size_t)B * H * 4);
+  u.total = off;
+  return u;
+}
+
+unsigned uf_blocks(size_t n) { return (unsigned)std::min<size_t>((n + kUfThreads - 1) / kUfThreads, 8192); }
+
+template <int AD, int RD, int ED, int SD>
+void uf_launch_all(const moe_layer_desc *d, const moe_layer_weights *wt, const void *x, void *y, int B,
+                   int32_t *idx, float *wts, unsigned char *ws, const UfLayout &u, hipStream_t st) {
+  const int H = d->hidden, E = d->num_experts, k = d->top_k, I = d->expert_inter, Is = d->shared_inter;
+  const int P = B * k;
+  float *xf = (float *)(ws + u.xf);
+  void *xa = AD == DT_F32 ? (void *)xf : (void *)(ws + u.xa);
+  float *lg = (float *)(ws + u.lg), *gu = (float *)(ws + u.gu), *dd = (float *)(ws + u.d);
+  float *sgu = (float *)(ws + u.sgu), *ds = (float *)(ws + u.ds);
+  void *h = ws + u.h, *hs = ws + u.hs;
+  const dim3 blk(kUfThreads);
+  // 1. RMSNorm
+  hipLaunchKernelGGL(uf_rmsnorm<AD>, dim3(B), blk, 0, st, x, wt->rms_gamma, H, d->rms_eps, xf, xa);
+  // 2. router: one weight row per wave for up to 4 tokens
+  UfGemv a{};
+  a.w = (const char *)wt->router_w; a.R = E; a.K = H; a.x = (const char *)xf; a.x_div = 1; a.nx = B;
+  a.bias = wt->router_bias; a.out = lg;
+  if (B > 1) hipLaunchKernelGGL((uf_gemv<RD, DT_F32, 4>), dim3((E + kUfRows - 1) / kUfRows, (B + 3) / 4), blk, 0, st, a);
+  else hipLaunchKernelGGL((uf_gemv<RD, DT_F32, 1>), dim3((E + kUfRows - 1) / kUfRows, 1), blk, 0, st, a);
+  // 3. top-k + softmax
+  hipLaunchKernelGGL(uf_topk, dim3(B), dim3(64), 0, st, (const float *)lg, E, k, idx, wts);
+  // 4. expert gate/up of every (token, expert) pair
+  a = UfGemv{};
+  a.w = (const char *)wt->expert_gate_up; a.mat_bytes = (size_t)2 * I * H * dsize(d->expert); a.idx = idx;
+  a.R = 2 * I; a.K = H; a.x = (const char *)xa; a.x_div = k; a.nx = B;
+  a.scale = (const uint16_t *)wt->expert_gate_up_scale; a.out = gu;
+  hipLaunchKernelGGL((uf_gemv<ED, AD, 1>), dim3((2 * I + kUfRows - 1) / kUfRows, P), blk, 0, st, a);
+  // 5. SiLU * mul
+  hipLaunchKernelGGL(uf_silu_mul<AD>, dim3(uf_blocks((size_t)P * I)), blk, 0, st, (const float *)gu, I, P, h);
+  // 6. expert down
+  a = UfGemv{};
+  a.w = (const char *)wt->expert_down; a.mat_bytes = (size_t)H * I * dsize(d->expert); a.idx = idx;
+  a.R = H; a.K = I; a.x = (const char *)h; a.x_div = 1; a.nx = P;
+  a.scale = (const uint16_t *)wt->expert_down_scale; a.out = dd;
+  hipLaunchKernelGGL((uf_gemv<ED, AD, 1>), dim3((H + kUfRows - 1) / kUfRows, P), blk, 0, st, a);
+  if (Is > 0) {
+    // 7.-9. shared expert: gate/up, SiLU * mul, down
+    a = UfGemv{};
+    a.w = (const char *)wt->shared_gate_up; a.R = 2 * Is; a.K = H; a.x = (const char *)xa; a.x_div = 1; a.nx = B;
+    a.out = sgu;
+    hipLaunchKernelGGL((uf_gemv<SD, AD, 1>), dim3((2 * Is + kUfRows - 1) / kUfRows, B), blk, 0, st, a);
+    hipLaunchKernelGGL(uf_silu_mul<AD>, dim3(uf_blocks((size_t)B * Is)), blk, 0, st, (const float *)sgu, Is, B, hs);
+    a = UfGemv{};
+    a.w = (const char *)wt->shared_down; a.R = H; a.K = Is; a.x = (const char *)hs; a.x_div = 1; a.nx = B;
+    a.out = ds;
+    hipLaunchKernelGGL((uf_gemv<SD, AD, 1>), dim3((H + kUfRows - 1) / kUfRows, B), blk, 0, st, a);
+  }
+  // 10. weighted combine + residual
+  hipLaunchKernelGGL(uf_combine<AD>, dim3(uf_blocks((size_t)B * H)), blk, 0, st, x, Is > 0 ? (const float *)ds : nullptr,
+                     (const float *)dd, (const float *)wts, H, k, B, y);
+}
+
+moe_status launch_unfused(const moe_layer_desc *d, const moe_layer_weights *wt, const void *x, void *y, int B,
+                          int32_t *idx, float *wts, void *ws, size_t ws_bytes, void *stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (B < 1 || B > kMaxB) return fail(MOE_ERR_UNSUPPORTED, "batch %d outside 1..64", B);
+  if ((st = check_weights(d, wt)) != MOE_OK) return st;
+  if (!x || !y || !ws) return fail(MOE_ERR_INVALID_ARGUMENT, "x, y or workspace is NULL");
+  const void *ptrs[] = {x, y, idx, wts, ws};
+  for (const void *q : ptrs)
+    if (q && !aligned16(q)) return fail(MOE_ERR_INVALID_ARGUMENT, "pointer %p is not 16-byte aligned", q);
+  const size_t xbytes = (size_t)B * d->hidden * dsize(d->act);
+  if (y != x && overlap(x, xbytes, y, xbytes)) return fail(MOE_ERR_INVALID_ARGUMENT, "x and y partially overlap");
+  const UfLayout u = uf_layout(d, B);
+  if (ws_bytes < u.total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes, u.total);
+  if (overlap(ws, u.total, x, xbytes) || overlap(ws, u.total, y, xbytes))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "workspace overlaps x or y");
+  unsigned char *wsb = (unsigned char *)ws;
+  if (!idx) idx = (int32_t *)(wsb + u.idx);
+  if (!wts) wts = (float *)(wsb + u.w);
+  const hipStream_t s = (hipStream_t)stream;
+  if (d->act == MOE_F32) {
+    uf_launch_all<DT_F32, DT_F32, DT_F32, DT_F32>(d, wt, x, y, B, idx, wts, wsb, u, s);
+  } else if (d->expert == MOE_BF16) {
+    if (d->router == MOE_F32) uf_launch_all<DT_BF16, DT_F32, DT_BF16, DT_BF16>(d, wt, x, y, B, idx, wts, wsb, u, s);
+    else uf_launch_all<DT_BF16, DT_BF16, DT_BF16, DT_BF16>(d, wt, x, y, B, idx, wts, wsb, u, s);
+  } else {
+    if (d->router == MOE_F32) uf_launch_all<DT_BF16, DT_F32, DT_FP8, DT_BF16>(d, wt, x, y, B, idx, wts, wsb, u, s);
+    else uf_launch_all<DT_BF16, DT_BF16, DT_FP8, DT_BF16>(d, wt, x, y, B, idx, wts, wsb, u, s);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2569,6 +2829,18 @@ moe_status moe_check_workspace(void *ws, size_t ws_bytes, void *stream) {
     return fail(MOE_ERR_TIMEOUT, "a launch on this workspace stopped at its barrier watchdog");
   }
   return MOE_OK;
+}
+
+size_t moe_unfused_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens) {
+  if (check_desc(desc) != MOE_OK) return 0;
+  if (max_tokens < 1 || max_tokens > kMaxB) return 0;
+  return uf_layout(desc, max_tokens).total;
+}
+
+moe_status moe_decode_layer_unfused(const moe_layer_desc *desc, const moe_layer_weights *weights, const void *x,
+                                    void *y, int32_t B, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                                    void *stream) {
+  return launch_unfused(desc, weights, x, y, B, topk_idx, topk_w, ws, ws_bytes, stream);
 }
 
 const char *moe_status_string(moe_status s) {

@@ -67,12 +67,14 @@ def _weights():
     ("bad_hidden", md.MOE_ERR_UNSUPPORTED), ("fp8_no_scales", md.MOE_ERR_INVALID_ARGUMENT),
     ("k_too_big", md.MOE_ERR_UNSUPPORTED), ("null_desc", md.MOE_ERR_INVALID_ARGUMENT),
 ])
-def test_layer_argument_errors(lib, case, status):
+@pytest.mark.parametrize("entry", ["fused", "unfused"])
+def test_layer_argument_errors(lib, case, status, entry):
     w = synth.WORKLOADS["k3_b1"]
     d = desc_of(w)
     wt = _weights()
     B, x, y = 1, FAKE + (1 << 30), FAKE + (2 << 30)
-    ws, wsb = FAKE + (3 << 30), md.moe_workspace_bytes(d, 64, 1)
+    ws = FAKE + (3 << 30)
+    wsb = md.moe_workspace_bytes(d, 64, 1) if entry == "fused" else md.moe_unfused_workspace_bytes(d, 64)
     if case == "batch0":
         B = 0
     elif case == "batch65":
@@ -91,10 +93,13 @@ def test_layer_argument_errors(lib, case, status):
         d = desc_of(synth.WORKLOADS["k3_stack4_fp8"])
     elif case == "k_too_big":
         d.top_k = 33
+    fused = entry == "fused"
     if case == "null_desc":
-        st = lib.moe_decode_layer(None, ctypes.byref(wt), x, y, B, None, None, ws, wsb, None)
+        fn = lib.moe_decode_layer if fused else lib.moe_decode_layer_unfused
+        st = fn(None, ctypes.byref(wt), x, y, B, None, None, ws, wsb, None)
     else:
-        st = md.moe_decode_layer(d, wt, x, y, B, None, None, ws, wsb, check=False)
+        fn = md.moe_decode_layer if fused else md.moe_decode_layer_unfused
+        st = fn(d, wt, x, y, B, None, None, ws, wsb, check=False)
     assert st == status, (case, md.moe_last_error())
     assert md.moe_last_error()
 
@@ -110,3 +115,11 @@ def test_route_and_stack_argument_errors(lib):
     assert md.moe_decode_stack(d, [wt, wt], x, x, 1, None, None, ws, 4096, check=False) == \
         md.MOE_ERR_WORKSPACE_TOO_SMALL
     assert md.moe_check_workspace(None, 0) == md.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_unfused_workspace_bytes(lib):
+    d = desc_of(synth.WORKLOADS["k3_b1"])
+    n1, n64 = md.moe_unfused_workspace_bytes(d, 1), md.moe_unfused_workspace_bytes(d, 64)
+    # at least the fp32 gate/up and down outputs of every (token, expert) pair
+    assert n64 >= 64 * 16 * (2 * 1024 + 7168) * 4 > n1 > 0
+    assert md.moe_unfused_workspace_bytes(d, 0) == 0 and md.moe_unfused_workspace_bytes(d, 65) == 0
