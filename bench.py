@@ -243,12 +243,6 @@ def main() -> int:
         log("bench: a warm-up launch hit its barrier watchdog")
         return 1
 
-    # algorithmic bytes of each instance: weights touched, each counted once per step
-    per_inst = []
-    for c in range(C):
-        sel = idx[c].cpu().numpy()
-        per_inst.append(sum(insts[c][l].touched_bytes(sel[l]) for l in range(L)))
-
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -264,6 +258,12 @@ def main() -> int:
         log("bench: a timed launch hit its barrier watchdog")
         return 1
     ms_step = ms_total / args.steps
+    # algorithmic bytes of each instance that the timed steps ran (its routing
+    # as its last call left it): weights touched, each counted once per step
+    per_inst = {}
+    for c in sorted({i % C for i in range(args.steps)}):
+        sel = idx[c].cpu().numpy()
+        per_inst[c] = sum(insts[c][l].touched_bytes(sel[l]) for l in range(L))
     nbytes = sum(per_inst[i % C] for i in range(args.steps)) / args.steps
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     for c in range(C):
