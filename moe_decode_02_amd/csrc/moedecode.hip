@@ -11,41 +11,50 @@
 //           larger B workgroup t normalises token t into global memory and a
 //           barrier publishes it.
 //   P0      The router GEMV, split over K into slices of about 7 KB of weights
-//           (partial logits, summed later in a fixed order), then the shared
+//           (partial logits, summed in a fixed order), then the shared
 //           expert's gate/up rows, which do not depend on routing; the pages
 //           run the shared expert on its own stream beside routing (smzdm.com
-//           post, section "what changed", MoE de-duplication item). Every wave
-//           announces "router done" before its shared rows, so the router
-//           barrier has completed by the time anyone waits on it.
-//   P1      Every workgroup redoes softmax + top-k + renormalisation (same
-//           inputs, same code, same result: no extra barrier), builds the
-//           expert gather tables in LDS (union of selected experts, each
-//           expert's token list), then streams the selected experts' gate/up
-//           rows: h = SiLU(g) * u.
-//   P2      Each workgroup owns a block of output rows. It first reduces the
-//           shared expert's down rows (their input is ready since P0), which
-//           fills the wait for the expert barrier, then every selected
-//           expert's down rows, then combines in a fixed order with the
-//           routing weights and the residual.
+//           post, section "what changed", MoE de-duplication item). From 8
+//           tokens both run on MFMA tiles instead.
+//   routing Softmax + top-k + renormalisation and the expert gather tables
+//           (union of selected experts, each expert's token list) in LDS.
+//           At B <= 2 one spare wave per workgroup polls the published logits
+//           (no router barrier) while the others stream shared rows; at
+//           larger B every workgroup routes the batch after a router barrier.
+//   P1      The selected experts' gate/up rows, h = SiLU(g) * u: GEMV rows,
+//           or MFMA tiles for experts that several tokens select. The work
+//           falls into groups, each closed by its own barrier.
+//   P2      Each workgroup owns a block of output rows. It reduces the shared
+//           expert's down rows first (their input is ready since P0), then
+//           each group's routed down rows once that group's barrier has
+//           passed, overlapping later gate/up work, then combines in a fixed
+//           order with the routing weights and the residual.
 //   stack   Between layers one more barrier; while waiting for it, a
 //           workgroup loads the next layer's router and shared-expert rows
 //           that it will read first, so they come from cache.
 //
 // Weight rows stream through 16-byte non-temporal loads, whole chunks of 64
 // lanes with no per-lane guard, all loads of a step in flight before the
-// first use. Cross-lane sums and the top-k argmax use DPP row operations.
-// All reductions are fixed-order (no float atomics), so identical router rows
-// give bit-identical logits and repeated runs give identical outputs.
+// first use; fp8 codes become bf16 through the hardware conversion and meet
+// the bf16 activations in dot2 instructions. Cross-lane sums and the top-k
+// argmax use DPP row operations. All reductions are fixed-order (no float
+// atomics), so identical router rows give bit-identical logits and repeated
+// runs give identical outputs.
 //
 // Memory ordering across the 8 XCDs: every wave releases its stores at
-// workgroup scope and counts itself in LDS; the workgroup's last wave releases
-// at agent scope (L2 write-back) and adds one to the barrier's global counter.
-// One wave per workgroup polls the counter, acquires at agent scope and raises
-// an LDS flag for the others. Weights are static and may be loaded before a
-// barrier; activations are read only after it (a compiler that hoisted an
-// activation load above a sync wait was one of the bugs found in the pages'
-// review: aiposthub.com article, section on how vLLM verifies AI-written
-// kernels).
+// workgroup scope and counts itself in LDS; the workgroup's last wave adds one
+// to the barrier's global counter, after an agent-scope release (L2
+// write-back) where plain stores must reach other XCDs (B > 2), or with none
+// where every value other workgroups read went out through device-coherent
+// stores (B <= 2, and the barrier between stack layers). One wave per
+// workgroup polls the counter, acquires at agent scope and raises an LDS flag
+// for the others. Weights are static and may be loaded before a barrier;
+// activations are read only after it (a compiler that hoisted an activation
+// load above a sync wait was one of the bugs found in the pages' review:
+// aiposthub.com article, section on how vLLM verifies AI-written kernels).
+//
+// The end of the file holds the multi-launch path (moe_decode_layer_unfused):
+// the same layer as ten kernel launches, the measured baseline of the fusion.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
