@@ -139,16 +139,18 @@ moe_status moe_decode_stack(const moe_layer_desc *desc, const moe_layer_weights 
  * tokens of this shape; 0 if desc is invalid or outside the envelope. */
 size_t moe_unfused_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens);
 
-/* The same layer as moe_decode_layer, computed by ten separate kernel
- * launches (RMSNorm, router, top-k, expert gate/up, SiLU*mul, expert down,
- * shared gate/up, shared SiLU*mul, shared down, combine) with every
+/* The same layer as moe_decode_layer, computed by eleven separate kernel
+ * launches (RMSNorm, router, top-k, expert grouping, expert gate/up,
+ * SiLU*mul, expert down, shared gate/up, shared SiLU*mul, shared down,
+ * combine) with every
  * intermediate in device memory: the launch-per-op decode path the pages
  * describe before fusion (openai-hub.com "Kimi K3 ... 1.68x", section on why
  * decode suits a megakernel: many small separately launched norm, matmul,
  * activation and routing kernels; smzdm.com post, section "what changed":
  * 23 kernels and ~130 us per decoder layer before, 13 and ~69 us after). It
- * is the measured baseline of the fused kernel and reads each selected
- * expert's weights once per (token, expert) pair.
+ * is the measured baseline of the fused kernel. The grouping kernel sorts
+ * the (token, expert) pairs by expert, so each selected expert's rows are
+ * read once per group of up to 4 of its tokens.
  *   Arguments as for moe_decode_layer, except the workspace, which is sized
  *   by moe_unfused_workspace_bytes and needs no zero fill (every call writes
  *   it before reading it). topk_idx / topk_w may be NULL (the routing then

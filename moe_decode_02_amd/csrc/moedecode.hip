@@ -54,7 +54,7 @@
 // aiposthub.com article, section on how vLLM verifies AI-written kernels).
 //
 // The end of the file holds the multi-launch path (moe_decode_layer_unfused):
-// the same layer as ten kernel launches, the measured baseline of the fusion.
+// the same layer as eleven kernel launches, the measured baseline of the fusion.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -2243,12 +2243,14 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
 
 
 // ---------------------------------------------------------------------------
-// Multi-launch path (moe_decode_layer_unfused): the same layer as ten
-// separate kernels with every intermediate (x-hat, logits, routing, gate/up
-// outputs, h, down outputs, the shared expert's) in HBM, the way an unfused
-// decode step runs it. It is the measured baseline of the fusion above. Its
-// GEMVs use the same streaming core: one wave per weight row, activation rows
-// from global memory, the expert weights read once per (token, expert) pair.
+// Multi-launch path (moe_decode_layer_unfused): the same layer as eleven
+// separate kernels with every intermediate (x-hat, logits, routing, expert
+// grouping, gate/up outputs, h, down outputs, the shared expert's) in HBM, the
+// way an unfused decode step runs it. It is the measured baseline of the
+// fusion above. Its GEMVs use the same streaming core: one wave per weight
+// row, activation rows from global memory; an align kernel groups the
+// (token, expert) pairs by expert, so each selected expert's rows are read
+// once per group of up to 4 of its tokens.
 
 constexpr int kUfThreads = 256;
 constexpr int kUfRows = kUfThreads / 64;  // GEMV kernels: one weight row per wave
@@ -2358,6 +2360,119 @@ __global__ void __launch_bounds__(64) uf_topk(const float *logits, int E, int k,
   if (lane < k) {
     idx[(size_t)t * k + lane] = my_e;
     w[(size_t)t * k + lane] = pe / sum;
+  }
+}
+
+// Exclusive prefix of v over the 1024 threads of a workgroup (every thread
+// calls it); total receives the sum.
+__device__ __forceinline__ int uf_block_scan(int v, int *wtot, int &total) {
+  const int lane = lane_id(), wv = wave_id();
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int up = __shfl_up(incl, d);
+    if (lane >= d) incl += up;
+  }
+  if (lane == 63) wtot[wv] = incl;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    const int t = wtot[w];
+    if (w < wv) base += t;
+    total += t;
+  }
+  __syncthreads();
+  return base + incl - v;
+}
+
+// Expert grouping of the P (token, expert) pairs, one workgroup: the union of
+// the selected experts in ascending order (ulist, *nU of them), and each
+// expert's pairs in ascending pair order, so ascending tokens
+// (plist[ustart[u] .. ustart[u + 1])).
+__global__ void __launch_bounds__(kThreads) uf_align(const int32_t *idx, int P, int E, int *nU, int *ulist,
+                                                      int *ustart, int *plist) {
+  __shared__ int cnt[kMaxE], start[kMaxE], sidx[kMaxB * kMaxK], wtot[kWaves];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
+  for (int q = tid; q < P; q += kThreads) sidx[q] = idx[q];
+  __syncthreads();
+  for (int q = tid; q < P; q += kThreads) atomicAdd(&cnt[sidx[q]], 1);
+  __syncthreads();
+  const int c = tid < E ? cnt[tid] : 0, f = c > 0 ? 1 : 0;
+  int totc, totf;
+  const int sc = uf_block_scan(c, wtot, totc);  // first pair position of expert tid
+  const int sf = uf_block_scan(f, wtot, totf);  // union slot of expert tid
+  if (tid < E) {
+    start[tid] = sc;
+    if (f) {
+      ulist[sf] = tid;
+      ustart[sf] = sc;
+    }
+  }
+  if (tid == 0) {
+    *nU = totf;
+    ustart[totf] = totc;
+  }
+  __syncthreads();
+  // stable placement: pair q follows the earlier pairs of its expert
+  for (int q = tid; q < P; q += kThreads) {
+    const int e = sidx[q];
+    int r = 0;
+    for (int q2 = 0; q2 < q; ++q2) r += sidx[q2] == e ? 1 : 0;
+    plist[start[e] + r] = q;
+  }
+}
+
+// Grouped GEMV over the union: job u (blockIdx.y) below *nU is expert
+// ulist[u] with the pairs plist[ustart[u] .. ustart[u + 1]); each wave reads
+// its weight row once per group of up to 4 pairs and writes out[pair][r].
+// The activation row of pair q is q / x_div.
+struct UfGroup {
+  const char *w;          // matrix 0, rows of K elements
+  size_t mat_bytes;       // bytes from one expert's matrix to the next
+  int R, K;
+  const char *x;          // activation rows of K elements
+  int x_div;
+  const uint16_t *scale;  // fp8: [e][R / 128] bf16
+  const int *nU, *ulist, *ustart, *plist;
+  float *out;             // [pairs][R]
+};
+
+template <int WD, int XD, int TG>
+__device__ __forceinline__ void uf_group_pass(const UfGroup &a, const char *const (&wrow)[1], int r, int q, int nt,
+                                              float sc) {
+  const char *xr[TG];
+  int pr[TG];
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    pr[t] = a.plist[q + min(t, nt - 1)];
+    xr[t] = a.x + (size_t)(pr[t] / a.x_div) * a.K * dsz<XD>();
+  }
+  float acc[1][TG];
+#pragma unroll
+  for (int t = 0; t < TG; ++t) acc[0][t] = 0.f;
+  rows_dot<WD, XD, false, 1, 2, TG>(wrow, 0, a.K, xr, acc);
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    const float v = wave_sum63(acc[0][t]) * sc;
+    if (lane_id() == 63 && t < nt) a.out[(size_t)pr[t] * a.R + r] = v;
+  }
+}
+
+template <int WD, int XD>
+__global__ void __launch_bounds__(kUfThreads) uf_group_gemv(UfGroup a) {
+  const int r = blockIdx.x * kUfRows + wave_id(), u = blockIdx.y;
+  if (r >= a.R || u >= *a.nU) return;
+  const int m = a.ulist[u], q0 = a.ustart[u], q1 = a.ustart[u + 1];
+  const char *const wrow[1] = {a.w + (size_t)m * a.mat_bytes + (size_t)r * a.K * dsz<WD>()};
+  float sc = 1.f;
+  if constexpr (WD == DT_FP8) sc = __uint_as_float((uint32_t)a.scale[(size_t)m * (a.R / 128) + r / 128] << 16);
+  for (int q = q0; q < q1; q += 4) {
+    const int nt = min(4, q1 - q);
+    if (nt == 1) uf_group_pass<WD, XD, 1>(a, wrow, r, q, nt, sc);
+    else if (nt == 2) uf_group_pass<WD, XD, 2>(a, wrow, r, q, nt, sc);
+    else uf_group_pass<WD, XD, 4>(a, wrow, r, q, nt, sc);
   }
 }
 
@@ -2682,7 +2797,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
 
 // workspace of the multi-launch path
 struct UfLayout {
-  size_t xf, xa, lg, idx, w, gu, h, d, sgu, hs, ds, total;
+  size_t xf, xa, lg, idx, w, nu, ulist, ustart, plist, gu, h, d, sgu, hs, ds, total;
 };
 
 UfLayout uf_layout(const moe_layer_desc *d, int B) {
@@ -2696,6 +2811,11 @@ UfLayout uf_layout(const moe_layer_desc *d, int B) {
   u.lg = take((size_t)B * d->num_experts * 4);
   u.idx = take(P * 4);
   u.w = take(P * 4);
+  const size_t nslot = std::min(P, (size_t)d->num_experts);
+  u.nu = take(4);
+  u.ulist = take(nslot * 4);
+  u.ustart = take((nslot + 1) * 4);
+  u.plist = take(P * 4);
   u.gu = take(P * 2 * I * 4);
   u.h = take(P * I * act);
   u.d = take(P * H * 4);
@@ -2729,22 +2849,27 @@ void uf_launch_all(const moe_layer_desc *d, const moe_layer_weights *wt, const v
   else hipLaunchKernelGGL((uf_gemv<RD, DT_F32, 1>), dim3((E + kUfRows - 1) / kUfRows, 1), blk, 0, st, a);
   // 3. top-k + softmax
   hipLaunchKernelGGL(uf_topk, dim3(B), dim3(64), 0, st, (const float *)lg, E, k, idx, wts);
-  // 4. expert gate/up of every (token, expert) pair
-  a = UfGemv{};
-  a.w = (const char *)wt->expert_gate_up; a.mat_bytes = (size_t)2 * I * H * dsize(d->expert); a.idx = idx;
-  a.R = 2 * I; a.K = H; a.x = (const char *)xa; a.x_div = k; a.nx = B;
-  a.scale = (const uint16_t *)wt->expert_gate_up_scale; a.out = gu;
-  hipLaunchKernelGGL((uf_gemv<ED, AD, 1>), dim3((2 * I + kUfRows - 1) / kUfRows, P), blk, 0, st, a);
-  // 5. SiLU * mul
+  // 4. expert grouping: union of selected experts, each expert's pairs
+  int *nU = (int *)(ws + u.nu), *ulist = (int *)(ws + u.ulist), *ustart = (int *)(ws + u.ustart);
+  int *plist = (int *)(ws + u.plist);
+  const int nslot = std::min(P, E);
+  hipLaunchKernelGGL(uf_align, dim3(1), dim3(kThreads), 0, st, (const int32_t *)idx, P, E, nU, ulist, ustart, plist);
+  // 5. expert gate/up, each selected expert's rows read once for its tokens
+  UfGroup g{};
+  g.w = (const char *)wt->expert_gate_up; g.mat_bytes = (size_t)2 * I * H * dsize(d->expert);
+  g.R = 2 * I; g.K = H; g.x = (const char *)xa; g.x_div = k;
+  g.scale = (const uint16_t *)wt->expert_gate_up_scale;
+  g.nU = nU; g.ulist = ulist; g.ustart = ustart; g.plist = plist; g.out = gu;
+  hipLaunchKernelGGL((uf_group_gemv<ED, AD>), dim3((2 * I + kUfRows - 1) / kUfRows, nslot), blk, 0, st, g);
+  // 6. SiLU * mul
   hipLaunchKernelGGL(uf_silu_mul<AD>, dim3(uf_blocks((size_t)P * I)), blk, 0, st, (const float *)gu, I, P, h);
-  // 6. expert down
-  a = UfGemv{};
-  a.w = (const char *)wt->expert_down; a.mat_bytes = (size_t)H * I * dsize(d->expert); a.idx = idx;
-  a.R = H; a.K = I; a.x = (const char *)h; a.x_div = 1; a.nx = P;
-  a.scale = (const uint16_t *)wt->expert_down_scale; a.out = dd;
-  hipLaunchKernelGGL((uf_gemv<ED, AD, 1>), dim3((H + kUfRows - 1) / kUfRows, P), blk, 0, st, a);
+  // 7. expert down, grouped the same way
+  g.w = (const char *)wt->expert_down; g.mat_bytes = (size_t)H * I * dsize(d->expert);
+  g.R = H; g.K = I; g.x = (const char *)h; g.x_div = 1;
+  g.scale = (const uint16_t *)wt->expert_down_scale; g.out = dd;
+  hipLaunchKernelGGL((uf_group_gemv<ED, AD>), dim3((H + kUfRows - 1) / kUfRows, nslot), blk, 0, st, g);
   if (Is > 0) {
-    // 7.-9. shared expert: gate/up, SiLU * mul, down
+    // 8.-10. shared expert: gate/up, SiLU * mul, down
     a = UfGemv{};
     a.w = (const char *)wt->shared_gate_up; a.R = 2 * Is; a.K = H; a.x = (const char *)xa; a.x_div = 1; a.nx = B;
     a.out = sgu;
@@ -2755,7 +2880,7 @@ void uf_launch_all(const moe_layer_desc *d, const moe_layer_weights *wt, const v
     a.out = ds;
     hipLaunchKernelGGL((uf_gemv<SD, AD, 1>), dim3((H + kUfRows - 1) / kUfRows, B), blk, 0, st, a);
   }
-  // 10. weighted combine + residual
+  // 11. weighted combine + residual
   hipLaunchKernelGGL(uf_combine<AD>, dim3(uf_blocks((size_t)B * H)), blk, 0, st, x, Is > 0 ? (const float *)ds : nullptr,
                      (const float *)dd, (const float *)wts, H, k, B, y);
 }

@@ -1,5 +1,5 @@
-"""GPU parity of the multi-launch path (moe_decode_layer_unfused, ten kernel
-launches with every intermediate in device memory) against the CPU oracle,
+"""GPU parity of the multi-launch path (moe_decode_layer_unfused, eleven
+kernel launches with every intermediate in device memory) against the CPU oracle,
 with the bars of the fused kernel: expert indices bit-exact on tokens whose
 router margin is >= 1e-3, routing weights within 1e-4 relative, outputs within
 max relative error 2e-2 (bf16 / fp8 weights) or 1e-4 (fp32)."""
