@@ -22,6 +22,11 @@ not the decode path).
     achieved MFMA rate against the 2.5 PFLOP/s dense bf16 peak, and the
     fraction of the kernel's active cycles in which MFMA units were busy.
 
+`python -m moe_decode_02_amd.profiling counters <pmc_dir> <out.txt> <command...>`
+    the mean per dispatch of every counter of a `rocprofv3 --pmc` run, for
+    the decode kernel (for example LDS bank conflicts against LDS
+    instructions, or L2 hits against misses).
+
 `<command...>` is the profiled command line, copied into the summary.
 """
 from __future__ import annotations
@@ -166,12 +171,31 @@ def write_mfma(pmc_dir: str, trace_dir: str, out_txt: str, command: str) -> None
         f.write("\n".join(lines) + "\n")
 
 
+def write_counters(pmc_dir: str, out_txt: str, command: str) -> None:
+    path = _find(pmc_dir, "counter_collection.csv")
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if DECODE_KERNEL in r["Kernel_Name"]:
+                per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = ["# counters of the decode kernel from rocprofv3 --pmc (mean per dispatch)",
+             f"# command: {command}",
+             f"kernel_source_sha256 = {kernel_source_sha()}"]
+    for name in sorted(per):
+        lines.append(f"{name} = {statistics.mean(per[name]):.6g}   (dispatches {len(per[name])})")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main(argv) -> int:
     if len(argv) >= 4 and argv[1] == "stats":
         write_stats(argv[2], argv[3], " ".join(argv[4:]))
         return 0
     if len(argv) >= 5 and argv[1] == "traffic":
         write_traffic(argv[2], argv[3], argv[4], " ".join(argv[5:]))
+        return 0
+    if len(argv) >= 4 and argv[1] == "counters":
+        write_counters(argv[2], argv[3], " ".join(argv[4:]))
         return 0
     if len(argv) >= 5 and argv[1] == "mfma":
         write_mfma(argv[2], argv[3], argv[4], " ".join(argv[5:]))
