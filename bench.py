@@ -112,8 +112,18 @@ def cpu_baseline(w, B, budget_s):
         spent += time.perf_counter() - t0
         ntok += 1
         t += 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": ntok / spent, "unit": "tok/s", "cores": 1, "kind": "oracle",
-            "sample": f"{ntok} token(s) of {w.name}, one at a time, {spent:.1f} s of single-threaded oracle time"}
+            "sample": f"{ntok} token(s) of {w.name}, one at a time, {spent:.1f} s of single-threaded oracle time",
+            "s_per_step": B * spent / ntok, "cpu_model": model, "host_cores": os.cpu_count()}
 
 
 def stream_probe(torch, md, dev, stream, gib=4, reps=5):
