@@ -2228,11 +2228,18 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
   }
   if (sink == 0x9E3779B9u) sh.sink = sink;  // keeps the prefetch loads; practically never taken
 
-  // last workgroup out resets the counters for the next launch on this workspace
+  // last workgroup out resets the counters for the next launch on this
+  // workspace. Every wave first waits for its own memory operations, barrier
+  // increments included (a workgroup need not wait on every barrier it
+  // arrived at), so all of a workgroup's increments are complete before it
+  // counts itself out, and the reset follows every workgroup's increments. A
+  // relaxed count then suffices; the end of the launch makes y visible. An
+  // acquire-release count wrote back L2 on the last workgroup's critical path.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
     const unsigned old =
-        __hip_atomic_fetch_add(ctrl_word(p, CTRL_DONE), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(ctrl_word(p, CTRL_DONE), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (unsigned)p->G - 1u) {
       for (int b = 0; b < kBarPerLayer * p->L; ++b)
         __hip_atomic_store(ctrl_word(p, CTRL_BAR + b), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
