@@ -2262,28 +2262,53 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
 constexpr int kUfThreads = 256;
 constexpr int kUfRows = kUfThreads / 64;  // GEMV kernels: one weight row per wave
 
-// x-hat of token blockIdx.x: fp32 (router input) and act (FFN input; for
-// fp32 activations xa is xf)
+// x-hat of token blockIdx.x (one 1024-thread workgroup, 16-byte chunks):
+// fp32 (router input) and act (FFN input; for fp32 activations xa is xf)
 template <int AD>
-__global__ void __launch_bounds__(kUfThreads) uf_rmsnorm(const void *x, const void *gamma, int H, float eps,
-                                                          float *xf, void *xa) {
-  __shared__ float red[kUfRows];
+__global__ void __launch_bounds__(kThreads) uf_rmsnorm(const void *x, const void *gamma, int H, float eps,
+                                                        float *xf, void *xa) {
+  __shared__ float red[kWaves];
+  constexpr int EPC = 16 / dsz<AD>(), NC = act_chunks_max<AD>();
   const size_t t = blockIdx.x;
+  const int tid = threadIdx.x, nch = H / EPC;
+  u32x4 xv[NC], gv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = tid + c * kThreads, cc = ch < nch ? ch : 0;
+    xv[c] = *(const u32x4 *)((const char *)x + (t * nch + cc) * 16);
+    gv[c] = *(const u32x4 *)((const char *)gamma + (size_t)cc * 16);
+  }
   float ss = 0.f;
-  for (int h = threadIdx.x; h < H; h += kUfThreads) {
-    const float v = load_act<AD>(x, t * H + h);
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (tid + c * kThreads < nch) {
+      float f[8];
+      act_chunk_vals<AD>(xv[c], f);
+#pragma unroll
+      for (int q = 0; q < EPC; ++q) ss = fmaf(f[q], f[q], ss);
+    }
   }
   ss = readlane_f(wave_sum63(ss), 63);
   if (lane_id() == 0) red[wave_id()] = ss;
   __syncthreads();
   float tot = 0.f;
-  for (int w = 0; w < kUfRows; ++w) tot += red[w];
+  for (int w = 0; w < kWaves; ++w) tot += red[w];
   const float r = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int h = threadIdx.x; h < H; h += kUfThreads) {
-    const float v = load_act<AD>(x, t * H + h) * r * load_act<AD>(gamma, h);
-    xf[t * H + h] = v;
-    if constexpr (AD != DT_F32) store_act<AD>(xa, t * H + h, v);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = tid + c * kThreads;
+    if (ch < nch) {
+      float f[8], g[8];
+      act_chunk_vals<AD>(xv[c], f);
+      act_chunk_vals<AD>(gv[c], g);
+#pragma unroll
+      for (int q = 0; q < EPC; ++q) {
+        const float v = f[q] * r * g[q];
+        const size_t h = (size_t)ch * EPC + q;
+        xf[t * H + h] = v;
+        if constexpr (AD != DT_F32) store_act<AD>(xa, t * H + h, v);
+      }
+    }
   }
 }
 
@@ -2335,7 +2360,7 @@ __global__ void __launch_bounds__(kUfThreads) uf_gemv(UfGemv a) {
 // logit, then lower index), then the softmax restricted to the selection
 __global__ void __launch_bounds__(64) uf_topk(const float *logits, int E, int k, int32_t *idx, float *w) {
   const int t = blockIdx.x, lane = lane_id();
-  float v[kMaxE / 64];
+  float v[kMaxE / 64];  // slots past E hold -inf and never win against a logit
 #pragma unroll
   for (int q = 0; q < kMaxE / 64; ++q) {
     const int e = lane + 64 * q;
@@ -2344,22 +2369,22 @@ __global__ void __launch_bounds__(64) uf_topk(const float *logits, int E, int k,
   float my_l = 0.f;
   int my_e = 0;
   for (int i = 0; i < k; ++i) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    // the lane's best (strictly larger keeps the lower index), branch-free
+    float bv = v[0];
+    int bi = lane;
 #pragma unroll
-    for (int q = 0; q < kMaxE / 64; ++q)
-      if (lane + 64 * q < E && (v[q] > bv || bi == 0x7FFFFFFF)) {
-        bv = v[q];
-        bi = lane + 64 * q;
-      }
+    for (int q = 1; q < kMaxE / 64; ++q) {
+      const bool take = v[q] > bv;
+      bv = take ? v[q] : bv;
+      bi = take ? lane + 64 * q : bi;
+    }
     wave_argmax(bv, bi);
     if (lane == i) {
       my_l = bv;
       my_e = bi;
     }
 #pragma unroll
-    for (int q = 0; q < kMaxE / 64; ++q)
-      if (lane + 64 * q == bi) v[q] = -INFINITY;
+    for (int q = 0; q < kMaxE / 64; ++q) v[q] = lane + 64 * q == bi ? -INFINITY : v[q];
   }
   const float lmax = readlane_f(my_l, 0);
   const float pe = lane < k ? expf(my_l - lmax) : 0.f;
@@ -2847,7 +2872,7 @@ void uf_launch_all(const moe_layer_desc *d, const moe_layer_weights *wt, const v
   void *h = ws + u.h, *hs = ws + u.hs;
   const dim3 blk(kUfThreads);
   // 1. RMSNorm
-  hipLaunchKernelGGL(uf_rmsnorm<AD>, dim3(B), blk, 0, st, x, wt->rms_gamma, H, d->rms_eps, xf, xa);
+  hipLaunchKernelGGL(uf_rmsnorm<AD>, dim3(B), dim3(kThreads), 0, st, x, wt->rms_gamma, H, d->rms_eps, xf, xa);
   // 2. router: one weight row per wave for up to 4 tokens
   UfGemv a{};
   a.w = (const char *)wt->router_w; a.R = E; a.K = H; a.x = (const char *)xf; a.x_div = 1; a.nx = B;
