@@ -223,6 +223,22 @@ def test_envelope_edges(dev, case):
         free()
 
 
+@pytest.mark.parametrize("expert,router,seed", [(synth.BF16, synth.F32, 81), (synth.FP8, synth.BF16, 83)])
+def test_odd_multiples(dev, expert, router, seed):
+    """Sizes that are odd multiples of the envelope's units: H = 17 * 256
+    (20 output rows per workgroup, the last one 12, so the MFMA down tiles
+    end inside a partial share; router MFMA tiles of 17 blocks per wave), I =
+    3 * 128 (fp8 GEMV rows with a 256-element remainder), a partial router
+    tile (E = 24). B = 1, 2 (small batch), 9 and 40 (GEMV and MFMA experts,
+    router and shared expert on MFMA tiles at 40); every token vs the
+    oracle."""
+    w = small_workload(name="odd", H=4352, E=24, k=3, I=384, Is=768, act=synth.BF16, router=router,
+                       expert=expert, shared=synth.BF16, seed=seed)
+    for B in (1, 2, 9, 40):
+        err = full_parity(w, B, dev, poison=True)
+        log(f"odd multiples ({expert}) B={B} max rel err {err:.2e}")
+
+
 def test_k3_b1(dev):
     err = full_parity(synth.WORKLOADS["k3_b1"], 1, dev, poison=True)
     log(f"k3_b1 max rel err {err:.2e}")
