@@ -2703,85 +2703,94 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   p.B = B; p.L = L; p.route_only = route_only ? 1 : 0; p.eps = d->rms_eps;
   p.G = di.cus;
   if (p.G < 1) return fail(MOE_ERR_DEVICE, "device reports no compute units");
-  const bool small = small_regime(B);
-  // P2 output rows per workgroup, a multiple of the GEMV row block
-  int rpw = (p.H + p.G - 1) / p.G;
-  rpw = (rpw + kRowBlock - 1) / kRowBlock * kRowBlock;
-  p.rows_per_wg = rpw;
-  p.NSR = k_slices(d->hidden, d->router, 4);
-  // general regime, bf16: the router and the shared expert on MFMA tiles
-  // from kMfmaSharedMin tokens. The shared down tiles are 16 rows that end at
-  // the workgroup's last row, so every workgroup must own at least 16 rows
-  // (with fewer, the first workgroup's tile would start at a negative row).
-  p.mfma_sh = (!small && !route_only && d->act == MOE_BF16 && d->shared_inter > 0 && B >= kMfmaSharedMin &&
-               rpw >= 16)
-                  ? 1
-                  : 0;
-  p.NSS = (d->shared_inter > 0 && !p.mfma_sh) ? k_slices(d->hidden, d->shared, 2) : 1;
-  // the slices of a row are one workgroup's waves of one round: the shared
-  // tasks start at a multiple of the workgroup's wave count, and the rounds
-  // must fit the per-round slice counters and LDS slots (else every row is
-  // one slice)
-  const int NW = p.G * kWaves;
-  int rounds = 0;
-  auto plan_slices = [&]() {
-    p.s0 = (p.E * p.NSR + kWaves - 1) / kWaves * kWaves;
-    p.slw = p.NSS > 1 ? 2 * B : B;
-    const int ntask = p.mfma_sh ? 0 : p.s0 + p.Is * p.NSS;
-    p.p0_end = ntask;
-    p.p0r = (ntask + NW - 1) / NW;
-    // last round: as few waves per workgroup as cover the tasks left, a
-    // multiple of the slice counts of the rows in that round
-    const int left = ntask - (p.p0r - 1) * NW;
-    const int unit = (p.p0r - 1) * NW >= p.E * p.NSR ? p.NSS : (p.NSR > p.NSS ? p.NSR : p.NSS);
-    p.p0w = ((left + p.G - 1) / p.G + unit - 1) / unit * unit;
-    if (p.p0w > kWaves) p.p0w = kWaves;
-    rounds = (p.NSR > 1 || p.NSS > 1) ? p.p0r : 0;
-    if (ntask == 0) p.p0r = p.p0w = rounds = 0;
-  };
-  plan_slices();
-  if (rounds > kMaxRounds || (size_t)rounds * kWaves * p.slw * sizeof(float) > 16384) {
-    p.NSR = p.NSS = 1;
-    plan_slices();
-  }
-
-  // LDS carve-up
-  const int E = d->num_experts, P = B * d->top_k, H = d->hidden;
-  const int nsh = d->shared_inter > 0 ? d->shared_inter / d->expert_inter : 0;
-  const int nslot = P < E ? P : E;
-  const size_t act = (size_t)dsize(d->act);
-  size_t o = align16(sizeof(SmemHead));
-  p.o_sel_idx = (int)o; o = align16(o + (size_t)P * 4);
-  p.o_sel_w = (int)o; o = align16(o + (size_t)P * 4);
-  p.o_ulist = (int)o; o = align16(o + (size_t)nslot * 4);
-  p.o_ucnt = (int)o; o = align16(o + (size_t)nslot * 4);
-  p.o_ustart = (int)o; o = align16(o + (size_t)nslot * 4);
-  p.o_plist = (int)o; o = align16(o + (size_t)P * 4);
-  if (small) {
-    if (P > 64) return fail(MOE_ERR_UNSUPPORTED, "small-batch routing needs batch*top_k <= 64");
-    p.o_xf = (int)o; o = align16(o + (size_t)B * H * 4);
-    p.o_xa = (int)o; o = align16(o + (d->act == MOE_F32 ? 0 : (size_t)B * H * act));
-    p.o_hs = (int)o; o = align16(o + (size_t)B * (d->shared_inter > 0 ? d->shared_inter : 1) * act);
-  } else {
-    p.o_cnt = (int)o; o = align16(o + (size_t)E * 4);
-    p.o_start = (int)o; o = align16(o + (size_t)E * 4);
-    p.o_tmask = (int)o; o = align16(o + (size_t)E * 8);
-    p.o_mslot = (int)o; o = align16(o + (size_t)nslot * 4);
-    p.o_gslot = (int)o; o = align16(o + (size_t)nslot * 4);
-    p.o_cpre = (int)o; o = align16(o + (size_t)(nslot + 1) * 4);
-  }
-  p.o_slc = (int)o;
-  o = align16(o + (size_t)rounds * kWaves * p.slw * sizeof(float));
-  p.o_red = (int)o;
-  if (p.mfma_sh) o = align16(o + (size_t)kWaves * 16 * B * sizeof(float));
-  p.o_part = (int)o;
-  // small regime: the workgroup's P2 partial sums stay in LDS (one pass over
-  // its rows); general regime: they go to the workspace
-  const size_t per_row = (size_t)(P + B * nsh) * sizeof(float);
+  // the regime: B <= kSmallB keeps x-hat in every workgroup's LDS when it
+  // fits; otherwise (or for larger B) the general regime
+  bool small = small_regime(B);
+  size_t lds = 0;
   const size_t lds_cap = (size_t)(di.max_lds > 0 ? di.max_lds : 65536);
-  const size_t lds = small ? o + (size_t)rpw * per_row : o;
-  if (lds > lds_cap) return fail(MOE_ERR_UNSUPPORTED, "shape needs more LDS than the device's %zu bytes", lds_cap);
-  p.use_mfma = (!small && d->expert != MOE_F32 && rpw >= 16) ? 1 : 0;
+  for (;;) {
+    // P2 output rows per workgroup, a multiple of the GEMV row block
+    int rpw = (p.H + p.G - 1) / p.G;
+    rpw = (rpw + kRowBlock - 1) / kRowBlock * kRowBlock;
+    p.rows_per_wg = rpw;
+    p.NSR = k_slices(d->hidden, d->router, 4);
+    // general regime, bf16: the router and the shared expert on MFMA tiles
+    // from kMfmaSharedMin tokens. The shared down tiles are 16 rows that end at
+    // the workgroup's last row, so every workgroup must own at least 16 rows
+    // (with fewer, the first workgroup's tile would start at a negative row).
+    p.mfma_sh = (!small && !route_only && d->act == MOE_BF16 && d->shared_inter > 0 && B >= kMfmaSharedMin &&
+                 rpw >= 16)
+                    ? 1
+                    : 0;
+    p.NSS = (d->shared_inter > 0 && !p.mfma_sh) ? k_slices(d->hidden, d->shared, 2) : 1;
+    // the slices of a row are one workgroup's waves of one round: the shared
+    // tasks start at a multiple of the workgroup's wave count, and the rounds
+    // must fit the per-round slice counters and LDS slots (else every row is
+    // one slice)
+    const int NW = p.G * kWaves;
+    int rounds = 0;
+    auto plan_slices = [&]() {
+      p.s0 = (p.E * p.NSR + kWaves - 1) / kWaves * kWaves;
+      p.slw = p.NSS > 1 ? 2 * B : B;
+      const int ntask = p.mfma_sh ? 0 : p.s0 + p.Is * p.NSS;
+      p.p0_end = ntask;
+      p.p0r = (ntask + NW - 1) / NW;
+      // last round: as few waves per workgroup as cover the tasks left, a
+      // multiple of the slice counts of the rows in that round
+      const int left = ntask - (p.p0r - 1) * NW;
+      const int unit = (p.p0r - 1) * NW >= p.E * p.NSR ? p.NSS : (p.NSR > p.NSS ? p.NSR : p.NSS);
+      p.p0w = ((left + p.G - 1) / p.G + unit - 1) / unit * unit;
+      if (p.p0w > kWaves) p.p0w = kWaves;
+      rounds = (p.NSR > 1 || p.NSS > 1) ? p.p0r : 0;
+      if (ntask == 0) p.p0r = p.p0w = rounds = 0;
+    };
+    plan_slices();
+    if (rounds > kMaxRounds || (size_t)rounds * kWaves * p.slw * sizeof(float) > 16384) {
+      p.NSR = p.NSS = 1;
+      plan_slices();
+    }
+
+    // LDS carve-up
+    const int E = d->num_experts, P = B * d->top_k, H = d->hidden;
+    const int nsh = d->shared_inter > 0 ? d->shared_inter / d->expert_inter : 0;
+    const int nslot = P < E ? P : E;
+    const size_t act = (size_t)dsize(d->act);
+    size_t o = align16(sizeof(SmemHead));
+    p.o_sel_idx = (int)o; o = align16(o + (size_t)P * 4);
+    p.o_sel_w = (int)o; o = align16(o + (size_t)P * 4);
+    p.o_ulist = (int)o; o = align16(o + (size_t)nslot * 4);
+    p.o_ucnt = (int)o; o = align16(o + (size_t)nslot * 4);
+    p.o_ustart = (int)o; o = align16(o + (size_t)nslot * 4);
+    p.o_plist = (int)o; o = align16(o + (size_t)P * 4);
+    if (small) {
+      if (P > 64) return fail(MOE_ERR_UNSUPPORTED, "small-batch routing needs batch*top_k <= 64");
+      p.o_xf = (int)o; o = align16(o + (size_t)B * H * 4);
+      p.o_xa = (int)o; o = align16(o + (d->act == MOE_F32 ? 0 : (size_t)B * H * act));
+      p.o_hs = (int)o; o = align16(o + (size_t)B * (d->shared_inter > 0 ? d->shared_inter : 1) * act);
+    } else {
+      p.o_cnt = (int)o; o = align16(o + (size_t)E * 4);
+      p.o_start = (int)o; o = align16(o + (size_t)E * 4);
+      p.o_tmask = (int)o; o = align16(o + (size_t)E * 8);
+      p.o_mslot = (int)o; o = align16(o + (size_t)nslot * 4);
+      p.o_gslot = (int)o; o = align16(o + (size_t)nslot * 4);
+      p.o_cpre = (int)o; o = align16(o + (size_t)(nslot + 1) * 4);
+    }
+    p.o_slc = (int)o;
+    o = align16(o + (size_t)rounds * kWaves * p.slw * sizeof(float));
+    p.o_red = (int)o;
+    if (p.mfma_sh) o = align16(o + (size_t)kWaves * 16 * B * sizeof(float));
+    p.o_part = (int)o;
+    // small regime: the workgroup's P2 partial sums stay in LDS (one pass over
+    // its rows); general regime: they go to the workspace
+    const size_t per_row = (size_t)(P + B * nsh) * sizeof(float);
+    lds = small ? o + (size_t)rpw * per_row : o;
+    p.use_mfma = (!small && d->expert != MOE_F32 && rpw >= 16) ? 1 : 0;
+    if (lds <= lds_cap) break;
+    if (!small) return fail(MOE_ERR_UNSUPPORTED, "shape needs more LDS than the device's %zu bytes", lds_cap);
+    // x-hat of every token does not fit a workgroup's LDS (from H = 16384 at
+    // B = 2): the general regime keeps it in global memory instead
+    small = false;
+  }
 
   p.timeout_ticks = 200000000LL;  // 2 s at 100 MHz
   // test hook: a tiny limit makes every barrier wait give up at once (no hang, no fault)

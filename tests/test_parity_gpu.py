@@ -192,8 +192,8 @@ def test_envelope_edges(dev, case):
     the most experts and the largest top-k (E=1024, k=32; B=2 fills the
     small-batch routing's 64 pairs), k=1 with no shared expert, every expert
     selected (k=E), and the largest hidden size (H=16384). At H=16384 two
-    tokens' x-hat no longer fits a workgroup's LDS: the small-batch path
-    refuses B=2 before any launch."""
+    tokens' x-hat no longer fits a workgroup's LDS, so B=2 runs in the
+    general regime (x-hat in global memory)."""
     if case == "max_experts_k32":
         w = small_workload(name="edge_e1024", H=256, E=1024, k=32, I=128, Is=128, seed=71)
         batches = (1, 2, 3)
@@ -208,19 +208,10 @@ def test_envelope_edges(dev, case):
     else:
         w = small_workload(name="edge_h16k", H=16384, E=16, k=2, I=128, Is=128, act=synth.BF16, router=synth.F32,
                            expert=synth.BF16, shared=synth.BF16, seed=74)
-        batches = (1, 3)
+        batches = (1, 2, 3)
     for B in batches:
         err = full_parity(w, B, dev, poison=True)
         log(f"edge {case} B={B} max rel err {err:.2e}")
-    if case == "max_hidden":
-        d = desc_of(w)
-        dl = DeviceLayer(w, device=dev, experts=[0, 1])
-        x = torch.zeros((2, w.H), dtype=torch.bfloat16, device=dev)
-        ws = workspace(d, 2, 1, dev)
-        st = md.moe_decode_layer(d, dl.weights, x, x, 2, None, None, ws, check=False)
-        assert st == md.MOE_ERR_UNSUPPORTED, md.moe_last_error()
-        del dl
-        free()
 
 
 @pytest.mark.parametrize("expert,router,seed", [(synth.BF16, synth.F32, 81), (synth.FP8, synth.BF16, 83)])
