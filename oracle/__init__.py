@@ -58,6 +58,8 @@ def lib():
     L.orc_rmsnorm.argtypes = [vp, vp, vp, vp, vp]
     L.orc_router_logits.argtypes = [vp, vp, vp, vp]
     L.orc_route.argtypes = [vp, vp, vp, vp]
+    L.orc_route_weights.argtypes = [vp, vp, vp, vp]
+    L.orc_layer_token_given.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.orc_ffn.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.orc_layer_token.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.orc_layer.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp]
@@ -147,6 +149,15 @@ def route(d: OrcDesc, logits: np.ndarray):
     return idx, w
 
 
+def route_weights(d: OrcDesc, logits: np.ndarray, idx) -> np.ndarray:
+    """Weights of a given selection idx [k]: the restricted, renormalised softmax."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    w = np.zeros(d.top_k, np.float32)
+    _check(lib().orc_route_weights(ctypes.byref(d), _p(logits), _p(idx), _p(w)))
+    return w
+
+
 def ffn(d: OrcDesc, dtype: int, inter: int, gate_up, down, xact, gate_up_scale=None, down_scale=None):
     h = np.zeros(inter, np.float32)
     out = np.zeros(d.hidden, np.float32)
@@ -167,6 +178,20 @@ def layer(d: OrcDesc, L: Layer, x: np.ndarray):
     _check(lib().orc_layer(ctypes.byref(d), ctypes.byref(pin.w), _p(x), B, _p(y), _p(idx), _p(w),
                            _p(logits)))
     return y, idx, w, logits
+
+
+def layer_given(d: OrcDesc, L: Layer, x_t: np.ndarray, idx):
+    """One token x_t [H] through the layer with the selection idx [k] (rank order)
+    in place of the top-k -> (y [H], w [k], logits [E])."""
+    x_t = np.ascontiguousarray(x_t)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    y = np.zeros_like(x_t)
+    w = np.zeros(d.top_k, np.float32)
+    logits = np.zeros(d.num_experts, np.float32)
+    pin = _Pinned(d, L)
+    _check(lib().orc_layer_token_given(ctypes.byref(d), ctypes.byref(pin.w), _p(x_t), _p(idx), _p(y), _p(w),
+                                       _p(logits)))
+    return y, w, logits
 
 
 def stack(d: OrcDesc, layers, x: np.ndarray):

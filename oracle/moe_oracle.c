@@ -153,20 +153,39 @@ static int ranks_before(const float *l, int32_t a, int32_t b) {
   return l[a] > l[b] || (l[a] == l[b] && a < b);
 }
 
-/* Softmax over all E logits, top-k by logit (ties: lower index), then the k
- * selected probabilities renormalised to sum to one. idx/wts in rank order. */
-int orc_route(const orc_desc *d, const float *logits, int32_t *idx, float *wts) {
+/* Weights of a given selection S (k distinct experts, rank order): the
+ * softmax over all E logits, restricted to S and renormalised to sum to one,
+ * w_i = p_{S_i} / sum_j p_{S_j}. */
+int orc_route_weights(const orc_desc *d, const float *logits, const int32_t *idx, float *wts) {
   if (!desc_ok(d) || !logits || !idx || !wts) return ORC_EINVAL;
   const int32_t E = d->num_experts, k = d->top_k;
+  for (int32_t i = 0; i < k; ++i) {
+    if (idx[i] < 0 || idx[i] >= E) return ORC_EINVAL;
+    for (int32_t j = 0; j < i; ++j)
+      if (idx[j] == idx[i]) return ORC_EINVAL;
+  }
   double *p = (double *)malloc(sizeof(double) * (size_t)E);
-  char *taken = (char *)calloc((size_t)E, 1);
-  if (!p || !taken) { free(p); free(taken); return ORC_ENOMEM; }
+  if (!p) return ORC_ENOMEM;
   double lmax = (double)logits[0];
   for (int32_t e = 1; e < E; ++e)
     if ((double)logits[e] > lmax) lmax = (double)logits[e];
   double z = 0.0;
   for (int32_t e = 0; e < E; ++e) { p[e] = exp((double)logits[e] - lmax); z += p[e]; }
   for (int32_t e = 0; e < E; ++e) p[e] /= z;
+  double sel = 0.0;
+  for (int32_t i = 0; i < k; ++i) sel += p[idx[i]];
+  for (int32_t i = 0; i < k; ++i) wts[i] = (float)(p[idx[i]] / sel);
+  free(p);
+  return 0;
+}
+
+/* Top-k by logit (ties: lower index), in rank order, then the weights of that
+ * selection (orc_route_weights). */
+int orc_route(const orc_desc *d, const float *logits, int32_t *idx, float *wts) {
+  if (!desc_ok(d) || !logits || !idx || !wts) return ORC_EINVAL;
+  const int32_t E = d->num_experts, k = d->top_k;
+  char *taken = (char *)calloc((size_t)E, 1);
+  if (!taken) return ORC_ENOMEM;
   for (int32_t i = 0; i < k; ++i) {
     int32_t best = -1;
     for (int32_t e = 0; e < E; ++e)
@@ -174,12 +193,8 @@ int orc_route(const orc_desc *d, const float *logits, int32_t *idx, float *wts) 
     taken[best] = 1;
     idx[i] = best;
   }
-  double sel = 0.0;
-  for (int32_t i = 0; i < k; ++i) sel += p[idx[i]];
-  for (int32_t i = 0; i < k; ++i) wts[i] = (float)(p[idx[i]] / sel);
-  free(p);
   free(taken);
-  return 0;
+  return orc_route_weights(d, logits, idx, wts);
 }
 
 /* ---- SwiGLU FFN (routed or shared expert) ------------------------------- */
@@ -220,25 +235,16 @@ int orc_ffn(const orc_desc *dsc, int32_t dtype, int32_t inter, const void *gate_
 
 /* ---- the layer --------------------------------------------------------- */
 
-int orc_layer_token(const orc_desc *d, const orc_weights *w, const void *x_t, void *y_t,
-                    int32_t *idx, float *wts, float *logits) {
-  if (!desc_ok(d) || !w || !x_t || !y_t || !idx || !wts) return ORC_EINVAL;
-  const int32_t H = d->hidden, E = d->num_experts, k = d->top_k;
-  float *xhat = (float *)malloc(sizeof(float) * (size_t)H);
-  float *xact = (float *)malloc(sizeof(float) * (size_t)H);
-  float *lg = (float *)malloc(sizeof(float) * (size_t)E);
+/* The rest of a token's layer once its selection (idx, wts) is fixed:
+ * y = act(x + shared(xact) + sum_i wts_i expert_{idx_i}(xact)), the routed sum
+ * in rank order. */
+static int finish_token(const orc_desc *d, const orc_weights *w, const void *x_t, const float *xact,
+                        const int32_t *idx, const float *wts, void *y_t) {
+  const int32_t H = d->hidden, k = d->top_k;
   float *dv = (float *)malloc(sizeof(float) * (size_t)H);
   double *routed = (double *)calloc((size_t)H, sizeof(double));
   int rc = ORC_ENOMEM;
-  if (!xhat || !xact || !lg || !dv || !routed) goto done;
-
-  rc = orc_rmsnorm(d, x_t, w->rms_gamma, xhat, xact);
-  if (rc) goto done;
-  rc = orc_router_logits(d, w, xhat, lg);
-  if (rc) goto done;
-  rc = orc_route(d, lg, idx, wts);
-  if (rc) goto done;
-  if (logits) memcpy(logits, lg, sizeof(float) * (size_t)E);
+  if (!dv || !routed) goto done;
 
   /* routed experts: sum_i w_i * expert_{S_i}(xact), in rank order */
   for (int32_t i = 0; i < k; ++i) {
@@ -270,8 +276,45 @@ int orc_layer_token(const orc_desc *d, const orc_weights *w, const void *x_t, vo
   }
   rc = 0;
 done:
-  free(xhat); free(xact); free(lg); free(dv); free(routed);
+  free(dv); free(routed);
   return rc;
+}
+
+/* One token through the layer. With given != 0 the selection is the caller's
+ * idx (k distinct experts in rank order) instead of the top-k; its weights are
+ * still the restricted softmax of this token's logits. */
+static int layer_token(const orc_desc *d, const orc_weights *w, const void *x_t, void *y_t, int32_t *idx,
+                       float *wts, float *logits, int given) {
+  if (!desc_ok(d) || !w || !x_t || !y_t || !idx || !wts) return ORC_EINVAL;
+  const int32_t H = d->hidden, E = d->num_experts;
+  float *xhat = (float *)malloc(sizeof(float) * (size_t)H);
+  float *xact = (float *)malloc(sizeof(float) * (size_t)H);
+  float *lg = (float *)malloc(sizeof(float) * (size_t)E);
+  int rc = ORC_ENOMEM;
+  if (!xhat || !xact || !lg) goto done;
+
+  rc = orc_rmsnorm(d, x_t, w->rms_gamma, xhat, xact);
+  if (rc) goto done;
+  rc = orc_router_logits(d, w, xhat, lg);
+  if (rc) goto done;
+  rc = given ? orc_route_weights(d, lg, idx, wts) : orc_route(d, lg, idx, wts);
+  if (rc) goto done;
+  if (logits) memcpy(logits, lg, sizeof(float) * (size_t)E);
+  rc = finish_token(d, w, x_t, xact, idx, wts, y_t);
+done:
+  free(xhat); free(xact); free(lg);
+  return rc;
+}
+
+int orc_layer_token(const orc_desc *d, const orc_weights *w, const void *x_t, void *y_t,
+                    int32_t *idx, float *wts, float *logits) {
+  return layer_token(d, w, x_t, y_t, idx, wts, logits, 0);
+}
+
+int orc_layer_token_given(const orc_desc *d, const orc_weights *w, const void *x_t, const int32_t *idx,
+                          void *y_t, float *wts, float *logits) {
+  /* with given != 0, idx is only read */
+  return layer_token(d, w, x_t, y_t, (int32_t *)idx, wts, logits, 1);
 }
 
 static size_t act_bytes(const orc_desc *d) { return d->act == ORC_BF16 ? 2u : 4u; }

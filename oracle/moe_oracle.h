@@ -74,6 +74,8 @@ double orc_e4m3_value(uint8_t code);     /* OCP E4M3FN */
 int orc_rmsnorm(const orc_desc *d, const void *x_t, const void *gamma, float *xhat, float *xact);
 int orc_router_logits(const orc_desc *d, const orc_weights *w, const float *xhat, float *logits);
 int orc_route(const orc_desc *d, const float *logits, int32_t *idx, float *wts);
+/* weights of a given selection idx [k] (distinct, in range): restricted, renormalised softmax */
+int orc_route_weights(const orc_desc *d, const float *logits, const int32_t *idx, float *wts);
 int orc_ffn(const orc_desc *d, int32_t dtype, int32_t inter, const void *gate_up, const void *down,
             const uint16_t *gate_up_scale, const uint16_t *down_scale, const float *xact,
             float *h_out, float *d_out);
@@ -81,6 +83,10 @@ int orc_ffn(const orc_desc *d, int32_t dtype, int32_t inter, const void *gate_up
 /* one token through one layer; logits may be NULL */
 int orc_layer_token(const orc_desc *d, const orc_weights *w, const void *x_t, void *y_t,
                     int32_t *idx, float *wts, float *logits);
+/* one token through one layer with the caller's selection idx [k] (rank order) in place of
+ * the top-k; wts receives that selection's weights; logits may be NULL */
+int orc_layer_token_given(const orc_desc *d, const orc_weights *w, const void *x_t, const int32_t *idx,
+                          void *y_t, float *wts, float *logits);
 /* B tokens: x, y [B][H] act dtype; idx, wts [B][k]; logits [B][E] or NULL */
 int orc_layer(const orc_desc *d, const orc_weights *w, const void *x, int32_t B, void *y,
               int32_t *idx, float *wts, float *logits);

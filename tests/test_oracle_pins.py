@@ -222,6 +222,36 @@ def test_layer_fp8_vs_torch():
     _layer_vs_torch(w, L, synth.x_tokens(w, 2), 8e-3)
 
 
+@pytest.mark.parametrize("dt", [F32, BF16])
+def test_layer_with_given_selection_vs_torch(dt):
+    """A layer evaluated on a selection that is not the top-k (the k-th expert
+    swapped with the (k+1)-th, the order reversed): weights are the softmax
+    restricted to that selection, the output the torch composition with it."""
+    w = small_workload(H=384, E=20, k=5, I=128, Is=256, act=dt, router=F32, expert=dt, shared=dt, zipf_s=1.1)
+    L = host_layer(w, random_gamma=True)
+    d = oracle.desc_of(w)
+    x = synth.x_tokens(w, 2)
+    y, idx, wts, lg = oracle.layer(d, L, x)
+    # the top-k itself gives the layer's result bit for bit
+    y0, w0, l0 = oracle.layer_given(d, L, x[0], idx[0])
+    assert np.array_equal(y0, y[0]) and np.array_equal(w0, wts[0]) and np.array_equal(l0, lg[0])
+    for t in range(2):
+        order = np.argsort(-lg[t], kind="stable")
+        sel = np.concatenate([order[: w.k - 1], order[w.k: w.k + 1]])[::-1].astype(np.int32)
+        yg, wg, _ = oracle.layer_given(d, L, x[t], sel)
+        ry, ridx, rw = torch_ref.layer_token(d, L, x[t], given=sel)
+        assert np.array_equal(ridx, sel)
+        assert np.allclose(wg, rw, rtol=1e-6)
+        p = scipy.special.softmax(lg[t].astype(np.float64))
+        assert np.allclose(wg, p[sel] / p[sel].sum(), rtol=1e-6)
+        assert max_rel_err(to_f64(yg, w.act), ry.numpy()) <= (1e-6 if dt == F32 else 8e-3)
+        assert max_rel_err(to_f64(yg, w.act), to_f64(y[t], w.act)) > 1e-4  # a different expert set
+    with pytest.raises(RuntimeError, match="invalid"):
+        oracle.layer_given(d, L, x[0], np.array([0, 0, 1, 2, 3], np.int32))  # repeated expert
+    with pytest.raises(RuntimeError, match="invalid"):
+        oracle.layer_given(d, L, x[0], np.array([0, 1, 2, 3, w.E], np.int32))  # out of range
+
+
 def test_identical_experts_collapse_to_dense_ffn():
     w = small_workload(H=256, E=8, k=3, I=128, Is=128)
     L = host_layer(w)

@@ -39,8 +39,9 @@ def ffn(gate_up: torch.Tensor, down: torch.Tensor, xa: torch.Tensor, act: int):
     return (down @ h).to(torch.float32).to(torch.float64), h
 
 
-def layer_token(d, L, x_t: np.ndarray):
-    """d: oracle.OrcDesc-like (attributes); L: oracle.Layer. Returns (y float64, idx, w)."""
+def layer_token(d, L, x_t: np.ndarray, given=None):
+    """d: oracle.OrcDesc-like (attributes); L: oracle.Layer. Returns (y float64, idx, w).
+    given: a selection (k expert ids in rank order) used in place of the top-k."""
     act = d.act
     x = decode(x_t, act)
     gamma = decode(L.gamma, act)
@@ -51,6 +52,8 @@ def layer_token(d, L, x_t: np.ndarray):
         logits = logits + torch.from_numpy(L.router_bias)
     p = torch.softmax(logits.to(torch.float64), dim=0)
     order = torch.argsort(-logits, stable=True)[: d.top_k]
+    if given is not None:
+        order = torch.as_tensor(np.asarray(given, np.int64))
     w = (p[order] / p[order].sum()).to(torch.float32)
     routed = torch.zeros_like(x)
     for i, e in enumerate(order.tolist()):
