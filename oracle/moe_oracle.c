@@ -84,14 +84,15 @@ static float act_round(int32_t dtype, double v) {
 }
 
 /* weight element (row, col) of a [rows][cols] matrix; fp8 rows share one bf16
- * scale per `group` rows */
+ * scale per `group` rows, and e4m3 holds orc_e4m3_value of every code (a
+ * lookup table of that function, filled by the caller) */
 static double w_get(int32_t dtype, const void *p, const uint16_t *scale, int32_t group, size_t row,
-                    size_t cols, size_t col) {
+                    size_t cols, size_t col, const double *e4m3) {
   size_t i = row * cols + col;
   switch (dtype) {
     case ORC_F32: return (double)((const float *)p)[i];
     case ORC_BF16: return orc_bf16_value(((const uint16_t *)p)[i]);
-    default: return orc_e4m3_value(((const uint8_t *)p)[i]) * orc_bf16_value(scale[row / (size_t)group]);
+    default: return e4m3[((const uint8_t *)p)[i]] * orc_bf16_value(scale[row / (size_t)group]);
   }
 }
 
@@ -140,7 +141,7 @@ int orc_router_logits(const orc_desc *d, const orc_weights *w, const float *xhat
   for (int32_t e = 0; e < E; ++e) {
     double acc = 0.0;
     for (int32_t h = 0; h < H; ++h)
-      acc += w_get(d->router, w->router_w, NULL, 1, (size_t)e, (size_t)H, (size_t)h) * (double)xhat[h];
+      acc += w_get(d->router, w->router_w, NULL, 1, (size_t)e, (size_t)H, (size_t)h, NULL) * (double)xhat[h];
     float l = (float)acc;
     if (w->router_bias) l = l + w->router_bias[e];
     logits[e] = l;
@@ -210,11 +211,13 @@ int orc_ffn(const orc_desc *dsc, int32_t dtype, int32_t inter, const void *gate_
   const int32_t H = dsc->hidden, G = dsc->scale_group;
   float *h = (float *)malloc(sizeof(float) * (size_t)inter);
   if (!h) return ORC_ENOMEM;
+  double e4m3[256];
+  for (int c = 0; c < 256; ++c) e4m3[c] = orc_e4m3_value((uint8_t)c);
   for (int32_t j = 0; j < inter; ++j) {
     double g = 0.0, u = 0.0;
     for (int32_t c = 0; c < H; ++c) {
-      g += w_get(dtype, gate_up, gate_up_scale, G, (size_t)j, (size_t)H, (size_t)c) * (double)xact[c];
-      u += w_get(dtype, gate_up, gate_up_scale, G, (size_t)(inter + j), (size_t)H, (size_t)c) * (double)xact[c];
+      g += w_get(dtype, gate_up, gate_up_scale, G, (size_t)j, (size_t)H, (size_t)c, e4m3) * (double)xact[c];
+      u += w_get(dtype, gate_up, gate_up_scale, G, (size_t)(inter + j), (size_t)H, (size_t)c, e4m3) * (double)xact[c];
     }
     const double gf = (double)(float)g, uf = (double)(float)u;
     const double silu = gf / (1.0 + exp(-gf));
@@ -225,7 +228,7 @@ int orc_ffn(const orc_desc *dsc, int32_t dtype, int32_t inter, const void *gate_
     for (int32_t o = 0; o < H; ++o) {
       double acc = 0.0;
       for (int32_t j = 0; j < inter; ++j)
-        acc += w_get(dtype, down, down_scale, G, (size_t)o, (size_t)inter, (size_t)j) * (double)h[j];
+        acc += w_get(dtype, down, down_scale, G, (size_t)o, (size_t)inter, (size_t)j, e4m3) * (double)h[j];
       d_out[o] = (float)acc;
     }
   }
