@@ -49,6 +49,14 @@
  *     outputs is an error.
  *   - Routing outputs list each token's k experts by descending logit, ties
  *     to the lower expert index; weights match that order and sum to 1.
+ *   - Co-residency: a fused launch is one 1024-thread workgroup per compute
+ *     unit whose grid barriers need every workgroup resident at once. Kernels
+ *     of other streams or processes that hold compute units delay it; every
+ *     in-kernel wait gives up after the watchdog limit (2 s by default, see
+ *     moe_set_watchdog_ticks). A launch in which a wait gave up still
+ *     completes, but writes NaN into the rows of y it can no longer trust and
+ *     -1 / NaN into every routing output (indices / weights / logits) it
+ *     wrote, and moe_check_workspace then returns MOE_ERR_TIMEOUT.
  */
 #ifndef MOEDECODE_H
 #define MOEDECODE_H
@@ -73,8 +81,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 
 /* Shape and dtypes of one layer (host struct).
  * Envelope (else MOE_ERR_UNSUPPORTED):
- *   hidden % 256 == 0, 256 <= hidden <= 16384; expert_inter % 128 == 0 and
- *   <= 4096; shared_inter == 0 or a multiple of expert_inter (<= 8192);
+ *   hidden % 128 == 0, hidden <= 16384; expert_inter % 128 == 0 and <= 4096;
+ *   shared_inter % 128 == 0 (0 = no shared expert) and <= 8192;
  *   1 <= top_k <= 32; top_k <= num_experts <= 1024; batch 1..64; layers 1..8;
  *   dtype sets: {act F32, router F32, expert F32, shared F32},
  *   {act BF16, router F32 or BF16, expert BF16, shared BF16},
@@ -110,7 +118,10 @@ typedef struct {
  * of this shape; 0 if desc is invalid or outside the envelope. */
 size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens, int32_t num_layers);
 
-/* Routing only: RMSNorm + router + softmax/top-k/renormalisation for B tokens.
+/* Routing only: RMSNorm + router + softmax/top-k/renormalisation for B tokens
+ * (the router scores every expert and each token keeps its top 16 of 896 in
+ * Kimi K3: smzdm.com post, section "what changed", MoE de-duplication item;
+ * aiposthub.com article, section on what the K3 decode path changed).
  *   x        [B][H] act dtype
  *   topk_idx [B][k] int32 out; topk_w [B][k] fp32 out
  *   logits   [B][E] fp32 out (router logits incl. bias), or NULL
@@ -119,7 +130,12 @@ moe_status moe_route(const moe_layer_desc *desc, const moe_layer_weights *weight
                      int32_t B, int32_t *topk_idx, float *topk_w, float *logits, void *ws,
                      size_t ws_bytes, void *stream);
 
-/* The whole layer for B tokens in one persistent kernel launch:
+/* The whole layer for B tokens in one persistent kernel launch: the decode
+ * step's normalisation, matmul, activation and routing ops fused into one
+ * kernel instead of one launch each (openai-hub.com "Kimi K3 ... 1.68x",
+ * section on why decode suits a megakernel), the shared expert's work beside
+ * the routing (smzdm.com post, section "what changed", MoE de-duplication
+ * item), batch 1-64 (smzdm.com post, section on who can use it).
  *   x [B][H] act dtype in; y [B][H] act dtype out (y == x allowed);
  *   topk_idx [B][k] / topk_w [B][k]: the routing used, or NULL. */
 moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *weights,
@@ -128,8 +144,13 @@ moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights 
 
 /* L layers of the same shape, each with its own weights (layers: host array of
  * L structs), in one persistent launch: y = layer_{L-1}(... layer_0(x)), each
- * layer's bf16 output feeding the next layer's RMSNorm. While a layer finishes,
- * the kernel already streams the next layer's router and shared-expert weights.
+ * layer's bf16 output feeding the next layer's RMSNorm. The layers stay in one
+ * launch (openai-hub.com "Kimi K3 ... 1.68x", section on why decode suits a
+ * megakernel), and while a layer's barrier is pending each wave loads the
+ * first router and shared gate/up slices it will read in the next layer, the
+ * single-GPU form of warming next-step weights while memory would idle
+ * (smzdm.com post, section "what changed", bandwidth-stealing prefetch item;
+ * aiposthub.com article, section on what the K3 decode path changed).
  *   topk_idx [L][B][k] / topk_w [L][B][k]: the routing of every layer, or NULL. */
 moe_status moe_decode_stack(const moe_layer_desc *desc, const moe_layer_weights *layers, int32_t L,
                             const void *x, void *y, int32_t B, int32_t *topk_idx, float *topk_w,
@@ -161,11 +182,19 @@ moe_status moe_decode_layer_unfused(const moe_layer_desc *desc, const moe_layer_
 
 /* Synchronises `stream`, then reads and clears the workspace's error word:
  * MOE_ERR_TIMEOUT if a launch on this workspace stopped at a watchdog (a grid
- * barrier or the small-batch logit wait gave up after 2 s), MOE_OK otherwise.
+ * barrier or the small-batch logit wait gave up after the watchdog limit),
+ * MOE_OK otherwise.
  * On MOE_ERR_TIMEOUT it also clears the small-batch logit buffers that the
  * stopped launch may have left written. A debugging aid, not for the hot
  * path. */
 moe_status moe_check_workspace(void *ws, size_t ws_bytes, void *stream);
+
+/* Limit of every in-kernel wait of later launches (grid barriers, the
+ * small-batch logit wait), in ticks of the GPU's 100 MHz realtime counter;
+ * a negative value restores the default of 2e8 (2 s). A limit of 0 makes each
+ * wait that would block give up at once, which exercises the timeout path
+ * (NaN outputs, MOE_ERR_TIMEOUT) without a hang. Process-wide. */
+void moe_set_watchdog_ticks(int64_t ticks);
 
 /* Static English name of a status. */
 const char *moe_status_string(moe_status status);

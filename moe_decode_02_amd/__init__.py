@@ -76,7 +76,7 @@ class moe_layer_weights(ctypes.Structure):
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_decode_layer", "moe_decode_stack",
            "moe_unfused_workspace_bytes", "moe_decode_layer_unfused",
-           "moe_check_workspace", "moe_status_string", "moe_last_error")
+           "moe_check_workspace", "moe_set_watchdog_ticks", "moe_status_string", "moe_last_error")
 
 
 @lru_cache(maxsize=None)
@@ -100,6 +100,8 @@ def lib():
     L.moe_decode_layer_unfused.restype = ctypes.c_int
     L.moe_check_workspace.argtypes = [vp, sz, vp]
     L.moe_check_workspace.restype = ctypes.c_int
+    L.moe_set_watchdog_ticks.argtypes = [ctypes.c_int64]
+    L.moe_set_watchdog_ticks.restype = None
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
@@ -189,6 +191,10 @@ def moe_decode_layer_unfused(desc, weights, x, y, B, topk_idx, topk_w, ws, ws_by
     if check:
         _check(st)
     return st
+
+
+def moe_set_watchdog_ticks(ticks: int) -> None:
+    lib().moe_set_watchdog_ticks(ticks)
 
 
 def moe_check_workspace(ws, ws_bytes=None, stream=None) -> int:

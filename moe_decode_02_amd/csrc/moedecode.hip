@@ -58,6 +58,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include <stdarg.h>
 #include <stddef.h>
@@ -119,6 +121,7 @@ struct LayerPtrs {
 
 struct Params {
   int H, E, k, I, Is, B, L;
+  int nsh;                // shared down: column blocks of width <= I (ceil(Is / I)), each a partial-sum column
   int route_only;
   int use_mfma;           // general regime: experts with >= kMfmaMin tokens go through MFMA tiles
   int mfma_sh;            // general regime: the router and the shared expert go through MFMA tiles
@@ -175,6 +178,7 @@ struct SmemHead {
   unsigned cand_key[kWaves][2 * 64];  // top-k candidates of each wave (ordered logit bits), then the ranked k
   int cand_idx[kWaves][2 * 64];
   unsigned sink;
+  int expired;                     // a wait of this workgroup gave up at its watchdog during this launch
 };
 
 // Kernel parameters are read in place from the kernarg segment (address space 4).
@@ -550,6 +554,7 @@ __device__ void bar_wait(KParams p, SmemHead &sh, int b) {
           __builtin_amdgcn_s_sleep(1);
           if (rt_now() - t0 > p->timeout_ticks) {
             __hip_atomic_store(ctrl_word(p, CTRL_ERR), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&sh.expired, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             break;
           }
         }
@@ -558,12 +563,23 @@ __device__ void bar_wait(KParams p, SmemHead &sh, int b) {
       } else {
         while (__hip_atomic_load(&sh.bar_flag[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
           __builtin_amdgcn_s_sleep(1);
-          if (rt_now() - t0 > 2 * p->timeout_ticks) break;
+          if (rt_now() - t0 > 2 * p->timeout_ticks) {
+            __hip_atomic_store(&sh.expired, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            break;
+          }
         }
       }
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// The workspace's error word, read device-coherently. A wait that gave up
+// stores it before its workgroup arrives at any later barrier (every wave's
+// arrival first waits for its own stores), so a workgroup that passed a later
+// barrier and then reads it sees every expiry that preceded that barrier.
+__device__ __forceinline__ unsigned err_word(KParams p) {
+  return __hip_atomic_load(ctrl_word(p, CTRL_ERR), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -903,7 +919,10 @@ __device__ __forceinline__ void load_logits(KParams p, KLayer lp, int t, float (
       for (int j = 0; j < PER; ++j) missing |= __float_as_uint(v[j]) == 0u;
       if (__ballot(missing) == 0ull) break;
       if (rt_now() - t0 > p->timeout_ticks) {
-        if (lane == 0) __hip_atomic_store(ctrl_word(p, CTRL_ERR), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) {
+          __hip_atomic_store(ctrl_word(p, CTRL_ERR), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&Lds{}.head().expired, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
         break;
       }
       __builtin_amdgcn_s_sleep(2);
@@ -1218,13 +1237,13 @@ __device__ __forceinline__ void stage_shared_h_wave(KParams p, const Lds &L) {
   }
 }
 
-// One 4-row unit of a [rows][K] down matrix: row pointers wrow, columns
-// [0, I) of x rows xr (TG tokens); writes the row sums (fp8 weights: times
+// One 4-row unit of a down matrix: row pointers wrow, columns [0, K) of x
+// rows xr (TG tokens); writes the row sums (fp8 weights: times
 // the bf16 scale word sraw, common to the unit's rows) to
 // prow[(o0 + r - o0) * rs + col[t] * cs] (rs, cs: row and column strides of
 // the partial-sum buffer).
 template <int WD, int AD, bool XL, int TG>
-__device__ __forceinline__ void down_unit(const char *const (&wrow)[kRowBlock], int I,
+__device__ __forceinline__ void down_unit(const char *const (&wrow)[kRowBlock], int K,
                                           const typename XSrc<XL>::ptr (&xr)[TG], uint32_t sraw,
                                           float *prow, int rs, int cs, const int (&col)[TG], int nt) {
 #pragma unroll
@@ -1237,7 +1256,7 @@ __device__ __forceinline__ void down_unit(const char *const (&wrow)[kRowBlock], 
 #pragma unroll
       for (int t = 0; t < TG; ++t) acc[r][t] = 0.f;
     }
-    rows_dot<WD, AD, XL, kDownRows, seg_down<WD, TG>(), TG>(wr, 0, I, xr, acc);
+    rows_dot<WD, AD, XL, kDownRows, seg_down<WD, TG>(), TG>(wr, 0, K, xr, acc);
 #pragma unroll
     for (int r = 0; r < kDownRows; ++r)
 #pragma unroll
@@ -1273,13 +1292,14 @@ __device__ __forceinline__ int next_unit(SmemHead &sh, int which) {
 template <int AD, int SD, bool SMALL>
 __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1) {
   const int I = p->I, Is = p->Is, B = p->B;
-  const int nsh = Is / I, P = B * p->k, pstride = P + B * nsh;
+  const int nsh = p->nsh, P = B * p->k, pstride = P + B * nsh;
   const int nrb = (pr1 - pr0) / kRowBlock;
   float *part = part_base<SMALL>(p, L);
   const int prb = SMALL ? pr0 : 0;
   for (int un = next_unit(L.head(), 0); un < nrb * nsh; un = next_unit(L.head(), 0)) {
     const int hf = un / nrb, rb = un % nrb;
     const int o0 = pr0 + rb * kRowBlock;
+    const int kw = min(I, Is - hf * I);  // columns of block hf (the last may be partial)
     const char *wrow[kRowBlock];
 #pragma unroll
     for (int r = 0; r < kRowBlock; ++r)
@@ -1294,7 +1314,7 @@ __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Ld
         else xr[t] = (const char *)p->hsbuf + ((size_t)tt * Is + (size_t)hf * I) * dsz<AD>();
         col[t] = P + (t0 + t) * nsh + hf;
       }
-      down_unit<SD, AD, SMALL, TG>(wrow, I, xr, 0x3F80u, part + (size_t)(o0 - prb) * part_rs<SMALL>(p, pstride),
+      down_unit<SD, AD, SMALL, TG>(wrow, kw, xr, 0x3F80u, part + (size_t)(o0 - prb) * part_rs<SMALL>(p, pstride),
                                    part_rs<SMALL>(p, pstride), part_cs<SMALL>(p), col, nt);
     });
   }
@@ -1702,7 +1722,7 @@ __device__ __attribute__((noinline)) void shared_gu_mfma(KParams p_arg, KLayer l
 template <int AD>
 __device__ __forceinline__ void shared_down_mfma(KParams p, KLayer lp, const Lds &L, int pr0, int pr1) {
   const int H = p->H, I = p->I, Is = p->Is, B = p->B, lane = lane_id();
-  const int nsh = Is / I, P = B * p->k;
+  const int nsh = p->nsh, P = B * p->k;
   const int r = lane & 15, kq = lane >> 4;
   const int ntile = (pr1 - pr0 + 15) / 16;
   float *part = p->partbuf;
@@ -1720,7 +1740,7 @@ __device__ __forceinline__ void shared_down_mfma(KParams p, KLayer lp, const Lds
       f32x4 acc[1][NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mfma_rows<DT_BF16, 1, NT>(uni(wb), wo, I, uni(xb), xo, acc);
+      mfma_rows<DT_BF16, 1, NT>(uni(wb), wo, min(I, Is - hf * I), uni(xb), xo, acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int o = o0 + 4 * kq + i;
@@ -1823,7 +1843,7 @@ template <int AD, int ED, bool SMALL>
 __device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, int ua, int ub,
                                                   int uc) {
   const int I = p->I, B = p->B;
-  const int nsh = p->Is / I, P = B * p->k, pstride = P + B * nsh;
+  const int nsh = p->nsh, P = B * p->k, pstride = P + B * nsh;
   const int nrb = (pr1 - pr0) / kRowBlock;
   float *part = part_base<SMALL>(p, L);
   const int prb = SMALL ? pr0 : 0;
@@ -1863,13 +1883,14 @@ __device__ __forceinline__ void expert_down_listed(KParams p, KLayer lp, const L
   }
 }
 
-// y = x + shared + sum_i w_i d_i (rank order i) for rows [pr0, pr1). PUB:
+// y = x + shared + sum_i w_i d_i (rank order i) for rows [pr0, pr1). pub:
 // y is the next layer's input, written with device-coherent stores so that
-// the layer barrier needs no L2 write-back.
+// the layer barrier needs no L2 write-back. poison: a wait gave up during the
+// launch, so the rows are written as NaN instead.
 template <int AD, bool SMALL>
-__device__ __forceinline__ void combine(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, bool pub) {
+__device__ __forceinline__ void combine(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, bool pub, bool poison) {
   const int H = p->H, k = p->k, B = p->B;
-  const int nsh = p->Is / p->I, P = B * k, pstride = P + B * nsh;
+  const int nsh = p->nsh, P = B * k, pstride = P + B * nsh;
   const float *part = part_base<SMALL>(p, L);
   const int prb = SMALL ? pr0 : 0;
   const float *sel_w = L.at<float>(p->o_sel_w);
@@ -1883,7 +1904,8 @@ __device__ __forceinline__ void combine(KParams p, KLayer lp, const Lds &L, int 
     for (int hf = 0; hf < nsh; ++hf) sh += pp[(size_t)(P + t * nsh + hf) * cs];
     float rt = 0.f;
     for (int i = 0; i < k; ++i) rt = fmaf(sel_w[t * k + i], pp[(size_t)(t * k + i) * cs], rt);
-    const float v = load_act<AD>(lp->x, (size_t)t * H + o) + sh + rt;
+    // after a watchdog stop the rows are not trusted: NaN makes that visible in y
+    const float v = poison ? __builtin_nanf("") : load_act<AD>(lp->x, (size_t)t * H + o) + sh + rt;
     if (pub) publish_act<AD>(lp->y, (size_t)t * H + o, v);
     else store_act<AD>(lp->y, (size_t)t * H + o, v);
   }
@@ -2046,7 +2068,7 @@ __device__ __forceinline__ void p1_cost_range(KParams p, KLayer lp, const Lds &L
 // whose barrier has passed, while slower waves finish the later groups. The
 // first wave done with P1 stages the shared expert's h.
 template <int AD, int RD, int ED, int SD>
-__device__ __forceinline__ void layer_small(KParams p, KLayer lp, const Lds &L, int b0, int W, int NW) {
+__device__ __forceinline__ bool layer_small(KParams p, KLayer lp, const Lds &L, int b0, int W, int NW) {
   SmemHead &sh = L.head();
   const int G = p->G, g = blockIdx.x;
   stage_xhat<AD>(p, lp, L);
@@ -2098,13 +2120,17 @@ __device__ __forceinline__ void layer_small(KParams p, KLayer lp, const Lds &L, 
   const int r1 = min(p->H, r0 + p->rows_per_wg);
   if (r0 < r1) shared_down_units<AD, SD, true>(p, lp, L, r0, r1);
   // the routed experts' rows, group by group: slots [ua, ub) end in group gi
+  // (the last group always holds the last slot); the error word is read once
+  // the last group's barrier has passed, its latency hidden by the down rows
   int ua = 0;
+  unsigned gerr = 0;
   for (int gi = 0; gi < nG; ++gi) {
     const int rend = share_lo(R1, gi + 1, nG);
     int ub = ua;
     while (ub < sh.nU && ((ub + 1) * I - 1) / NW < rend) ++ub;
     if (ub > ua) {
       bar_wait(p, sh, b0 + BAR_H + gi);
+      if (gi == nG - 1) gerr = err_word(p);
       if (r0 < r1) expert_down_units<AD, ED, true>(p, lp, L, r0, r1, ua, ub, 2 + gi);
     }
     ua = ub;
@@ -2117,9 +2143,11 @@ __device__ __forceinline__ void layer_small(KParams p, KLayer lp, const Lds &L, 
     const int n = p->B * p->E;
     for (int i = share_lo(n, g, G) + lane_id(); i < share_lo(n, g + 1, G); i += 64) publish(lp->lg + i, 0.f);
   }
+  // one decision for the whole workgroup (its waves read the error word separately)
+  const bool poison = __syncthreads_or(gerr != 0 || sh.expired != 0);
+  if (r0 < r1) combine<AD, true>(p, lp, L, r0, r1, b0 / kBarPerLayer + 1 < p->L, poison);
   __syncthreads();
-  if (r0 < r1) combine<AD, true>(p, lp, L, r0, r1, b0 / kBarPerLayer + 1 < p->L);
-  __syncthreads();
+  return poison;
 }
 
 // SMALL: B <= kSmallB. MSH: general regime with the shared expert on MFMA tiles.
@@ -2135,9 +2163,10 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
   const int W = blockIdx.x * kWaves + wv;  // global wave id
 
   for (int i = tid; i < kMaxBarriers; i += kThreads) sh.bar_cnt[i] = sh.bar_claim[i] = sh.bar_flag[i] = 0;
-  if (tid == 0) sh.sink = 0;
+  if (tid == 0) sh.sink = sh.expired = 0;
 
   unsigned sink = 0;
+  bool poisoned = false;  // a wait gave up during this launch (this workgroup's, or one before a barrier it passed)
   for (int l = 0; l < p->L; ++l) {
     KLayer lp = &p->lp[l];
     const int b0 = kBarPerLayer * l;
@@ -2160,13 +2189,14 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       if constexpr (SMALL) bar_arrive_published(p, sh, b0 + BAR_ROUTER);
       else bar_arrive(p, sh, b0 + BAR_ROUTER);
       bar_wait(p, sh, b0 + BAR_ROUTER);
+      poisoned = err_word(p) != 0;
       if (blockIdx.x == 0)
         for (int t = wv; t < p->B; t += kWaves) topk_token<false>(p, lp, L, t, true);
       break;
     }
 
     if constexpr (SMALL) {
-      layer_small<AD, RD, ED, SD>(p, lp, L, b0, W, NW);
+      poisoned |= layer_small<AD, RD, ED, SD>(p, lp, L, b0, W, NW);
     } else {
       // x-hat
       produce_xhat<AD>(p, lp, L);
@@ -2207,13 +2237,16 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
         if constexpr (MSH) shared_down_mfma<AD>(p, lp, L, r0, r1);
         else shared_down_units<AD, SD, false>(p, lp, L, r0, r1);
       }
+      unsigned gerr = 0;
       for (int gi = 0; gi < nGr; ++gi) {
         bar_wait(p, sh, b0 + BAR_H + gi);
+        if (gi == nGr - 1) gerr = err_word(p);  // latency hidden by the last group's down rows
         const int ia = group_first_slot(cpre, nL, gi, nGr), ib = group_first_slot(cpre, nL, gi + 1, nGr);
         if (r0 < r1) expert_down_listed<AD, ED>(p, lp, L, r0, r1, ia, ib, 2 + gi);
       }
-      __syncthreads();
-      if (r0 < r1) combine<AD, false>(p, lp, L, r0, r1, l + 1 < p->L);
+      const bool poison = __syncthreads_or(gerr != 0 || sh.expired != 0);
+      poisoned |= poison;
+      if (r0 < r1) combine<AD, false>(p, lp, L, r0, r1, l + 1 < p->L, poison);
       __syncthreads();
     }
 
@@ -2227,6 +2260,22 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
     }
   }
   if (sink == 0x9E3779B9u) sh.sink = sink;  // keeps the prefetch loads; practically never taken
+
+  // after a watchdog stop the routing outputs are not trusted either: the
+  // workgroup that wrote them overwrites them with -1 / NaN
+  const bool poison_out = __syncthreads_or(poisoned || sh.expired != 0);
+  if (blockIdx.x == 0 && poison_out) {
+    const int n = p->B * p->k;
+    for (int l = 0; l < p->L; ++l) {
+      KLayer lp = &p->lp[l];
+      for (int i = tid; i < n; i += kThreads) {
+        if (lp->idx_out) lp->idx_out[i] = -1;
+        if (lp->w_out) lp->w_out[i] = __builtin_nanf("");
+      }
+      if (lp->logits_out)
+        for (int i = tid; i < p->B * p->E; i += kThreads) lp->logits_out[i] = __builtin_nanf("");
+    }
+  }
 
   // last workgroup out resets the counters for the next launch on this
   // workspace. Every wave first waits for its own memory operations, barrier
@@ -2545,25 +2594,74 @@ moe_status fail(moe_status s, const char *fmt, ...) {
   return s;
 }
 
+// Per-device facts and launch preparation, filled on first use and then
+// only read: the compute-unit count, the LDS limit, and for each kernel the
+// largest dynamic LDS size for which its attribute is set and one resident
+// workgroup per CU has been checked. One mutex guards it (calls are
+// thread-safe); a call after the first takes it once and makes no HIP query.
+constexpr int kMaxDevices = 64;
+constexpr int kMaxKernels = 64;
+
+struct KernelReady {
+  const void *fn;
+  size_t lds;
+};
+
 struct DevInfo {
   int cus = 0;
   int max_lds = 0;
+  int nk = 0;
+  KernelReady ready[kMaxKernels];
 };
 
-DevInfo g_dev[64];
+DevInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
 
-moe_status device_info(DevInfo &out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(MOE_ERR_DEVICE, "hipGetDevice failed");
-  if (g_dev[dev].cus == 0) {
+// every in-kernel wait gives up after this many ticks of the 100 MHz realtime counter
+constexpr long long kDefaultWatchdogTicks = 200000000LL;  // 2 s
+std::atomic<long long> g_watchdog_ticks{kDefaultWatchdogTicks};
+
+moe_status current_device(int &dev) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_DEVICE, "hipGetDevice failed");
+  return MOE_OK;
+}
+
+moe_status device_info(int dev, int &cus, int &max_lds) {
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DevInfo &di = g_dev[dev];
+  if (di.cus == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(MOE_ERR_DEVICE, "hipGetDeviceProperties failed");
     int lds = 0;
     if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) lds = 65536;
-    g_dev[dev].max_lds = lds;
-    g_dev[dev].cus = prop.multiProcessorCount;
+    di.max_lds = lds;
+    di.cus = prop.multiProcessorCount;
   }
-  out = g_dev[dev];
+  cus = di.cus;
+  max_lds = di.max_lds;
+  return MOE_OK;
+}
+
+// Set kernel fn's dynamic LDS limit to at least lds bytes and check that a
+// workgroup of it fits on a CU (the persistent grid needs one per CU), once
+// per (device, kernel, larger LDS size).
+moe_status prepare_kernel(int dev, const void *fn, int threads, size_t lds) {
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DevInfo &di = g_dev[dev];
+  int i = 0;
+  while (i < di.nk && di.ready[i].fn != fn) ++i;
+  if (i < di.nk && lds <= di.ready[i].lds) return MOE_OK;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return fail(MOE_ERR_DEVICE, "hipFuncSetAttribute(%zu bytes of LDS) failed", lds);
+  int resident = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident, fn, threads, lds) != hipSuccess || resident < 1)
+    return fail(MOE_ERR_DEVICE, "a %d-thread workgroup with %zu bytes of LDS cannot be resident", threads, lds);
+  if (i == di.nk) {
+    if (di.nk == kMaxKernels) return MOE_OK;  // not cached: checked again next time
+    di.ready[di.nk++] = KernelReady{fn, lds};
+  } else {
+    di.ready[i].lds = lds;
+  }
   return MOE_OK;
 }
 
@@ -2576,12 +2674,12 @@ moe_status check_desc(const moe_layer_desc *d) {
   if (d->hidden <= 0 || d->num_experts <= 0 || d->top_k <= 0 || d->expert_inter <= 0 || d->shared_inter < 0)
     return fail(MOE_ERR_INVALID_ARGUMENT, "non-positive size in desc");
   if (!(d->rms_eps >= 0.f)) return fail(MOE_ERR_INVALID_ARGUMENT, "rms_eps must be >= 0");
-  if (d->hidden % 256 || d->hidden > 16384)
-    return fail(MOE_ERR_UNSUPPORTED, "hidden=%d: need a multiple of 256, at most 16384", d->hidden);
+  if (d->hidden % 128 || d->hidden > 16384)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden=%d: need a multiple of 128, at most 16384", d->hidden);
   if (d->expert_inter % 128 || d->expert_inter > 4096)
     return fail(MOE_ERR_UNSUPPORTED, "expert_inter=%d: need a multiple of 128, at most 4096", d->expert_inter);
-  if (d->shared_inter % d->expert_inter || d->shared_inter > 8192)
-    return fail(MOE_ERR_UNSUPPORTED, "shared_inter=%d: need 0 or a multiple of expert_inter, at most 8192",
+  if (d->shared_inter % 128 || d->shared_inter > 8192)
+    return fail(MOE_ERR_UNSUPPORTED, "shared_inter=%d: need 0 or a multiple of 128, at most 8192",
                 d->shared_inter);
   if (d->top_k > kMaxK || d->top_k > d->num_experts || d->num_experts > kMaxE)
     return fail(MOE_ERR_UNSUPPORTED, "top_k=%d num_experts=%d: need 1<=k<=32, k<=E<=1024", d->top_k, d->num_experts);
@@ -2605,6 +2703,9 @@ int k_slices(int hidden, moe_dtype dt, int most) {
 
 bool small_regime(int B) { return B <= kSmallB; }
 
+// column blocks of the shared down projection: width I, the last one partial
+int shared_blocks(const moe_layer_desc *d) { return (d->shared_inter + d->expert_inter - 1) / d->expert_inter; }
+
 struct WsLayout {
   size_t rlog, xhat, xa, rfin, hsh32, hbuf, hsbuf, partbuf, xbuf0, xbuf1, total;
 };
@@ -2623,7 +2724,7 @@ WsLayout ws_layout(const moe_layer_desc *d, int B, int L) {
   w.hsh32 = off; off += up256((size_t)B * is * 4);
   w.hbuf = off; off += up256((size_t)B * d->top_k * d->expert_inter * act);
   w.hsbuf = off; off += up256((size_t)B * is * act);
-  const size_t pstride = (size_t)B * d->top_k + (size_t)B * (d->shared_inter / d->expert_inter);
+  const size_t pstride = (size_t)B * d->top_k + (size_t)B * shared_blocks(d);
   w.partbuf = off; off += up256((size_t)d->hidden * pstride * 4);
   w.xbuf0 = off; off += (L > 1) ? up256((size_t)B * d->hidden * act) : 0;
   w.xbuf1 = off; off += (L > 2) ? up256((size_t)B * d->hidden * act) : 0;
@@ -2695,19 +2796,20 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   if (overlap(ws, wl.total, x, xbytes) || (y && overlap(ws, wl.total, y, xbytes)))
     return fail(MOE_ERR_INVALID_ARGUMENT, "workspace overlaps x or y");
 
-  DevInfo di;
-  if ((st = device_info(di)) != MOE_OK) return st;
+  int dev = 0, cus = 0, max_lds = 0;
+  if ((st = current_device(dev)) != MOE_OK || (st = device_info(dev, cus, max_lds)) != MOE_OK) return st;
   Params p;
   memset(&p, 0, sizeof p);
   p.H = d->hidden; p.E = d->num_experts; p.k = d->top_k; p.I = d->expert_inter; p.Is = d->shared_inter;
   p.B = B; p.L = L; p.route_only = route_only ? 1 : 0; p.eps = d->rms_eps;
-  p.G = di.cus;
+  p.nsh = shared_blocks(d);
+  p.G = cus;
   if (p.G < 1) return fail(MOE_ERR_DEVICE, "device reports no compute units");
   // the regime: B <= kSmallB keeps x-hat in every workgroup's LDS when it
   // fits; otherwise (or for larger B) the general regime
   bool small = small_regime(B);
   size_t lds = 0;
-  const size_t lds_cap = (size_t)(di.max_lds > 0 ? di.max_lds : 65536);
+  const size_t lds_cap = (size_t)(max_lds > 0 ? max_lds : 65536);
   for (;;) {
     // P2 output rows per workgroup, a multiple of the GEMV row block
     int rpw = (p.H + p.G - 1) / p.G;
@@ -2752,7 +2854,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
 
     // LDS carve-up
     const int E = d->num_experts, P = B * d->top_k, H = d->hidden;
-    const int nsh = d->shared_inter > 0 ? d->shared_inter / d->expert_inter : 0;
+    const int nsh = shared_blocks(d);
     const int nslot = P < E ? P : E;
     const size_t act = (size_t)dsize(d->act);
     size_t o = align16(sizeof(SmemHead));
@@ -2792,9 +2894,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     small = false;
   }
 
-  p.timeout_ticks = 200000000LL;  // 2 s at 100 MHz
-  // test hook: a tiny limit makes every barrier wait give up at once (no hang, no fault)
-  if (const char *ev = getenv("MOE_DEBUG_BARRIER_TIMEOUT_TICKS")) p.timeout_ticks = atoll(ev);
+  p.timeout_ticks = g_watchdog_ticks.load(std::memory_order_relaxed);
   unsigned char *wsb = (unsigned char *)ws;
   p.ctrl = (unsigned *)wsb;
   p.xhat = (float *)(wsb + wl.xhat);
@@ -2822,13 +2922,8 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     lp.lg = (small && !route_only) ? p.rlog + (size_t)(l & 1) * kSmallB * d->num_experts : p.rfin;
   }
   kernel_fn fn = pick_kernel(d, small, p.mfma_sh != 0);
-  if (hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-    return fail(MOE_ERR_DEVICE, "hipFuncSetAttribute(%zu bytes of LDS) failed", lds);
   // the grid is persistent: one resident workgroup per CU is required
-  int resident = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident, (const void *)fn, kThreads, lds) != hipSuccess ||
-      resident < 1)
-    return fail(MOE_ERR_DEVICE, "a %d-thread workgroup with %zu bytes of LDS cannot be resident", kThreads, lds);
+  if ((st = prepare_kernel(dev, (const void *)fn, kThreads, lds)) != MOE_OK) return st;
   hipLaunchKernelGGL(fn, dim3(p.G), dim3(kThreads), lds, (hipStream_t)stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
@@ -3031,5 +3126,9 @@ const char *moe_status_string(moe_status s) {
 }
 
 const char *moe_last_error(void) { return g_err; }
+
+void moe_set_watchdog_ticks(int64_t ticks) {
+  g_watchdog_ticks.store(ticks < 0 ? kDefaultWatchdogTicks : (long long)ticks, std::memory_order_relaxed);
+}
 
 }  // extern "C"

@@ -1,6 +1,8 @@
 """Shared test helpers: host layers from the seeded generator, the error metric,
 and the router-margin redraw. Imports the oracle (test infrastructure)."""
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -82,3 +84,63 @@ def draw_tokens_with_margin(w, B, layers_host, min_margin=1e-3, max_attempts=64,
         else:
             raise RuntimeError(f"token {t}: no draw with margin >= {min_margin}")
     return synth.x_tokens(w, B, attempts), attempts
+
+
+# The oracle is plain single-threaded C called through ctypes, which releases
+# the GIL: independent tokens run side by side in threads, each through the
+# unchanged oracle functions.
+WORKERS = max(1, min(16, os.cpu_count() or 1))
+
+
+def pmap(fn, items):
+    items = list(items)
+    if len(items) <= 1:
+        return [fn(i) for i in items]
+    with ThreadPoolExecutor(min(WORKERS, len(items))) as ex:
+        return list(ex.map(fn, items))
+
+
+def oracle_layer_tokens(d, L, x):
+    """oracle.layer on every token of x [B][H], tokens in parallel threads ->
+    (y [B][H], idx [B][k], w [B][k], logits [B][E])."""
+    outs = pmap(lambda t: oracle.layer(d, L, np.ascontiguousarray(x[t:t + 1])), range(x.shape[0]))
+    return tuple(np.concatenate([o[i] for o in outs]) for i in range(4))
+
+
+def oracle_logits_tokens(d, L, x):
+    """Router logits [B][E] of every token of x (RMSNorm + router)."""
+    def one(t):
+        xhat, _ = oracle.rmsnorm(d, np.ascontiguousarray(x[t]), L.gamma)
+        return oracle.router_logits(d, L, xhat)
+    return np.stack(pmap(one, range(x.shape[0])))
+
+
+def add_experts(w, L, ids, layer=0):
+    """Materialise the experts `ids` of layer `layer` in L (host generator)."""
+    new = [e for e in sorted(set(int(i) for i in np.ravel(ids))) if e not in L.gate_up]
+    gen = lambda e: (synth.expert_gate_up(w, e, layer), synth.expert_down(w, e, layer))
+    # fp8 fills are single-threaded C: run them in the pool; bf16/fp32 fills thread internally
+    outs = pmap(gen, new) if w.expert == synth.FP8 else [gen(e) for e in new]
+    for e, ((gu, gus), (dn, dns)) in zip(new, outs):
+        L.gate_up[e], L.down[e] = gu, dn
+        if gus is not None:
+            L.gate_up_scale[e], L.down_scale[e] = gus, dns
+
+
+def drop_experts(L):
+    L.gate_up.clear(); L.down.clear(); L.gate_up_scale.clear(); L.down_scale.clear()
+
+
+def valid_selection(logits, sel, k, tol):
+    """sel is a top-k of some logit vector within tol of `logits`: k distinct
+    experts in range, none below the k-th largest logit by more than tol, none
+    left out above it by more than tol, and in non-increasing order up to 2 tol."""
+    lg = np.asarray(logits, np.float64)
+    sel = np.asarray(sel)
+    if len(set(sel.tolist())) != k or sel.min() < 0 or sel.max() >= lg.size:
+        return False
+    kth = np.sort(lg)[::-1][k - 1]
+    rest = np.setdiff1d(np.arange(lg.size), sel)
+    if np.any(lg[sel] < kth - tol) or (rest.size and np.any(lg[rest] > kth + tol)):
+        return False
+    return bool(np.all(np.diff(lg[sel]) <= 2 * tol))

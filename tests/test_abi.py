@@ -53,6 +53,22 @@ def test_workspace_bytes_and_envelope(lib):
     assert md.moe_workspace_bytes(bad, 1, 1) == 0
 
 
+@pytest.mark.parametrize("field,value,ok", [
+    ("hidden", 4224, True), ("hidden", 128, True), ("hidden", 16384, True), ("hidden", 16512, False),
+    ("hidden", 4160, False), ("expert_inter", 384, True), ("expert_inter", 4224, False),
+    ("expert_inter", 192, False), ("shared_inter", 0, True), ("shared_inter", 384, True),
+    ("shared_inter", 8192, True), ("shared_inter", 8320, False), ("shared_inter", 200, False),
+    ("top_k", 32, True), ("top_k", 33, False), ("num_experts", 1024, True), ("num_experts", 1025, False),
+])
+def test_envelope_edges_abi(lib, field, value, ok):
+    """The envelope: H, I and Is multiples of 128 (Is need not be a multiple of
+    I), H <= 16384, I <= 4096, Is <= 8192, k <= 32, E <= 1024."""
+    d = desc_of(synth.WORKLOADS["k3_b1"])
+    setattr(d, field, value)
+    assert (md.moe_workspace_bytes(d, 4, 1) > 0) == ok
+    assert (md.moe_unfused_workspace_bytes(d, 4) > 0) == ok
+
+
 FAKE = 1 << 40  # a 16-byte aligned address; validation fails before anything touches it
 
 

@@ -14,7 +14,8 @@ import torch
 import moe_decode_02_amd as md
 import oracle
 import synth
-from helpers import draw_tokens_with_margin, host_layer, margin, max_rel_err, small_workload, to_f64
+from helpers import (add_experts, draw_tokens_with_margin, drop_experts, host_layer, margin, max_rel_err,
+                     oracle_layer_tokens, oracle_logits_tokens, pmap, small_workload, to_f64, valid_selection)
 from synth.device import DeviceLayer, act_tensor, desc_of, to_device, to_host, workspace
 
 pytestmark = pytest.mark.gpu
@@ -54,15 +55,6 @@ def oracle_routes(w, Lh, x):
     return idx, wts, lg
 
 
-def add_experts(w, Lh, ids, layer=0):
-    for e in sorted(set(int(i) for i in np.ravel(ids))):
-        if e not in Lh.gate_up:
-            Lh.gate_up[e], s1 = synth.expert_gate_up(w, e, layer)
-            Lh.down[e], s2 = synth.expert_down(w, e, layer)
-            if s1 is not None:
-                Lh.gate_up_scale[e], Lh.down_scale[e] = s1, s2
-
-
 def gpu_layer(w, dl, x, B, dev, route=False):
     d = desc_of(w)
     xd = to_device(x, dev)
@@ -99,7 +91,7 @@ def full_parity(w, B, dev, poison=True, random_gamma=False):
     x, _ = draw_tokens_with_margin(w, B, [Lh])
     idx_r, w_r, lg_r = oracle_routes(w, Lh, x)
     add_experts(w, Lh, idx_r)
-    y_ref, idx_o, w_o, _ = oracle.layer(oracle.desc_of(w), Lh, x)
+    y_ref, idx_o, w_o, _ = oracle_layer_tokens(oracle.desc_of(w), Lh, x)
     assert np.array_equal(idx_o, idx_r)
     log(f"gpu: {w.name} B={B} poison={poison}")
     dl = DeviceLayer(w, device=dev, experts=idx_r if poison else None, random_gamma=random_gamma)
@@ -230,6 +222,32 @@ def test_odd_multiples(dev, expert, router, seed):
         log(f"odd multiples ({expert}) B={B} max rel err {err:.2e}")
 
 
+@pytest.mark.parametrize("case", ["h33x128_is_not_multiple_of_i", "h33x128_fp8", "is_below_i", "f32_h3x128"])
+def test_widened_envelope(dev, case):
+    """Sizes that are multiples of 128 but not of 256, and a shared width that
+    is not a multiple of the expert width (its down projection then runs in
+    column blocks of width I with a partial last block): every token vs the
+    oracle, small and general regimes, GEMV and MFMA paths."""
+    if case == "h33x128_is_not_multiple_of_i":
+        w = small_workload(name="h4224", H=4224, E=24, k=3, I=256, Is=384, act=synth.BF16, router=synth.F32,
+                           expert=synth.BF16, shared=synth.BF16, seed=91)
+        batches = (1, 2, 9, 40)
+    elif case == "h33x128_fp8":
+        w = small_workload(name="h4224f8", H=4224, E=24, k=3, I=256, Is=640, act=synth.BF16, router=synth.BF16,
+                           expert=synth.FP8, shared=synth.BF16, seed=92)
+        batches = (1, 2, 9, 40)
+    elif case == "is_below_i":
+        w = small_workload(name="is128", H=1152, E=16, k=4, I=256, Is=128, act=synth.BF16, router=synth.F32,
+                           expert=synth.BF16, shared=synth.BF16, seed=93)
+        batches = (1, 2, 9)
+    else:
+        w = small_workload(name="f32h384", H=384, E=8, k=2, I=128, Is=256, seed=94)
+        batches = (1, 3)
+    for B in batches:
+        err = full_parity(w, B, dev, poison=True)
+        log(f"widened envelope {case} B={B} max rel err {err:.2e}")
+
+
 def test_k3_b1(dev):
     err = full_parity(synth.WORKLOADS["k3_b1"], 1, dev, poison=True)
     log(f"k3_b1 max rel err {err:.2e}")
@@ -245,28 +263,12 @@ def test_k3_b8(dev):
 
 
 def test_k3_b64_zipf(dev):
-    """All 64 tokens' routing bit-exact; outputs of 4 sampled tokens vs the oracle."""
+    """B=64 with the log-Zipf router bias: every token's routing bit-exact and
+    every token's output against the oracle (the MFMA tiles of the popular
+    experts carry up to ~55 tokens)."""
     w = synth.WORKLOADS["k3_b64_zipf"]
-    B = 64
-    Lh = host_layer(w, experts=[])
-    x, _ = draw_tokens_with_margin(w, B, [Lh])
-    idx_r, w_r, lg_r = oracle_routes(w, Lh, x)
-    sample = [0, 21, 42, 63]
-    add_experts(w, Lh, idx_r[sample])
-    y_ref, idx_o, w_o, _ = oracle.layer(oracle.desc_of(w), Lh, x[sample])
-    log(f"gpu: {w.name} B={B}")
-    dl = DeviceLayer(w, device=dev, experts=idx_r)
-    got = gpu_layer(w, dl, x, B, dev, route=True)
-    assert np.array_equal(got["idx"], idx_r)
-    assert np.allclose(got["w"], w_r, rtol=1e-4, atol=1e-6)
-    assert np.array_equal(got["ridx"], idx_r)
-    assert np.max(np.abs(got["logits"] - lg_r)) <= 2e-4
-    sub = {"y": got["y"][sample], "idx": got["idx"][sample], "w": got["w"][sample]}
-    err = check_layer(w, sub, y_ref, idx_o, w_o)
-    assert np.all(np.isfinite(to_f64(got["y"], w.act)))
-    log(f"k3_b64_zipf sampled max rel err {err:.2e}, union {len(np.unique(idx_r))} experts")
-    del dl
-    free()
+    err = full_parity(w, 64, dev, poison=True)
+    log(f"k3_b64_zipf all 64 tokens max rel err {err:.2e}")
 
 
 @pytest.fixture(scope="module")
@@ -278,24 +280,6 @@ def stack4(dev):
     yield w, dls, hosts
     del dls
     free()
-
-
-def oracle_stack_token(w, hosts, xt):
-    """Oracle stack on one token, materialising the experts each layer selects."""
-    d = oracle.desc_of(w)
-    cur = xt[None, :]
-    idx_all, w_all, lg_all = [], [], []
-    for l, Lh in enumerate(hosts):
-        xhat, _ = oracle.rmsnorm(d, cur[0], Lh.gamma)
-        lg = oracle.router_logits(d, Lh, xhat)
-        idx, _ = oracle.route(d, lg)
-        add_experts(w, Lh, idx, layer=l)
-        cur, i, ww, g = oracle.layer(d, Lh, cur)
-        idx_all.append(i[0]); w_all.append(ww[0]); lg_all.append(g[0])
-    return cur[0], np.array(idx_all), np.array(w_all), np.array(lg_all)
-
-
-STACK_DEEP_MARGIN = 5e-3
 
 
 def gpu_stack(w, dls, x, B, L, dev):
@@ -314,73 +298,74 @@ def gpu_stack(w, dls, x, B, L, dev):
 
 @pytest.mark.parametrize("B", [1, 2, 4, 16, 64])
 def test_k3_stack4_fp8(dev, stack4, B):
-    """Persistent 4-layer fp8 stack in one launch.
+    """Persistent 4-layer fp8 stack in one launch, every layer of every token.
 
-    The parity bar (routing bit-exact, max relative error 2e-2) is the bar of
-    one layer call, so each layer is checked teacher-forced: the oracle's layer
-    l runs on the GPU's own input of layer l, which the prefix runs (the first
-    1..3 layers, same kernel, deterministic) return. Layer-0 routing of every
-    token whose margin is >= 1e-3 is checked too.
+    The bar of a layer call (routing bit-exact where the router margin is
+    >= 1e-3, outputs within max relative error 2e-2) is applied to each layer
+    teacher-forced: the oracle's layer l runs on the GPU's own input of layer
+    l, which the prefix runs (the first 1..3 layers, same kernel,
+    deterministic) return. Layer 0's inputs are drawn with margin >= 1e-3 for
+    every token. Deeper inputs are the GPU's bf16 outputs, so a few (token,
+    layer) pairs have an oracle margin below 1e-3; there the selection is not
+    unique: the GPU's selection must be a top-k of logits within 4e-4 of the
+    oracle's, and its output is checked against the oracle evaluated on that
+    selection.
 
-    Free-running, the two sides diverge slowly: layer l >= 1 sees the previous
-    layer's bf16 output, which each side rounds from fp32 sums taken in a
-    different order, so a few elements differ by one bf16 ulp and layer l's
-    logits move by up to ~2e-3 (measured). The sampled tokens are redrawn until
-    the oracle's own trajectory has margin >= 1e-3 at layer 0 and
-    >= STACK_DEEP_MARGIN deeper, so that the GPU's trajectory keeps margin
-    >= 1e-3 at every layer; the free-running output is held to the composed
-    bound of L per-layer tolerances."""
+    Free-running (the oracle's own stack from x), the two sides see inputs
+    that differ by bf16 roundings taken in a different order; the error of
+    the composition is printed, and held to L times the layer bar for tokens
+    whose free-running routing equals the GPU's at every layer."""
     w, dls, hosts = stack4
     d = oracle.desc_of(w)
-    sample = sorted({0, B - 1})
-    attempts = np.zeros(B, np.int64)
-    refs = {}
-    for t in sample:
-        for a in range(64):
-            xt = synth.fill_host((w.H,), synth.key(w.seed, 0, synth.T_X, t, a), w.act, synth.INPUT_SIGMA)
-            y, idx, ww, lg = oracle_stack_token(w, hosts, xt)
-            if margin(lg[0], w.k) >= 1e-3 and all(margin(lg[l], w.k) >= STACK_DEEP_MARGIN
-                                                   for l in range(1, w.layers)):
-                attempts[t] = a
-                refs[t] = y
-                break
-        else:
-            raise RuntimeError("no draw with the required margins")
-    x = synth.x_tokens(w, B, attempts)
-    idx0, w0, lg0 = oracle_routes(w, hosts[0], x)
-    ok0 = [t for t in range(B) if margin(lg0[t], w.k) >= 1e-3]
+    x, _ = draw_tokens_with_margin(w, B, [hosts[0]])
     log(f"gpu: {w.name} stack B={B}")
     runs = [gpu_stack(w, dls, x, B, L, dev) for L in range(1, w.layers + 1)]
     gy, gi, gw = runs[-1]
     for L in range(1, w.layers):  # a prefix run is the start of the full run
         assert np.array_equal(runs[L - 1][1], gi[:L]) and np.array_equal(runs[L - 1][2], gw[:L])
-    layer_in = [x] + [runs[L - 1][0] for L in range(1, w.layers)]
-    assert np.array_equal(gi[0, ok0], idx0[ok0])
-    assert np.allclose(gw[0, ok0], w0[ok0], rtol=1e-4, atol=1e-6)
     assert np.all(np.isfinite(to_f64(gy, w.act)))
-    for t in sample:
-        for l in range(w.layers):
-            xt = np.ascontiguousarray(layer_in[l][t:t + 1])
-            xhat, _ = oracle.rmsnorm(d, xt[0], hosts[l].gamma)
-            lg = oracle.router_logits(d, hosts[l], xhat)
-            assert margin(lg, w.k) >= 1e-3, (t, l, margin(lg, w.k))
-            ridx, _ = oracle.route(d, lg)
-            add_experts(w, hosts[l], ridx, layer=l)
-            yl, il, wl, _ = oracle.layer(d, hosts[l], xt)
-            assert np.array_equal(gi[l, t], il[0]), (t, l, gi[l, t], il[0])
-            assert np.allclose(gw[l, t], wl[0], rtol=1e-4, atol=1e-6), (t, l)
-            gout = runs[l][0][t]
-            err = max_rel_err(to_f64(gout, w.act), to_f64(yl[0], w.act))
-            log(f"stack B={B} token {t} layer {l} (teacher-forced): max rel err {err:.2e}")
-            assert err <= 2e-2
-        err = max_rel_err(to_f64(gy[t], w.act), to_f64(refs[t], w.act))
-        log(f"stack B={B} token {t} free-running {w.layers} layers: max rel err {err:.2e}")
-        assert err <= w.layers * 2e-2
-    # every token's selected experts are distinct and in range, weights sum to 1
+    layer_in = [x] + [runs[L - 1][0] for L in range(1, w.layers)]
+    fr = x.copy()                        # the oracle's free-running stack state
+    fr_agree = np.ones(B, bool)          # free-running routing equal to the GPU's so far
+    worst, low = 0.0, []
     for l in range(w.layers):
-        for t in range(B):
-            assert len(set(gi[l, t].tolist())) == w.k and gi[l, t].min() >= 0 and gi[l, t].max() < w.E
-            assert abs(float(gw[l, t].sum()) - 1) < 1e-5
+        Lh = hosts[l]
+        tf_lg = oracle_logits_tokens(d, Lh, layer_in[l])
+        fr_lg = oracle_logits_tokens(d, Lh, fr)
+        tf_idx = np.stack([oracle.route(d, tf_lg[t])[0] for t in range(B)])
+        fr_idx = np.stack([oracle.route(d, fr_lg[t])[0] for t in range(B)])
+        add_experts(w, Lh, np.concatenate([tf_idx.ravel(), fr_idx.ravel(), gi[l].ravel()]), layer=l)
+
+        def check(t):
+            xt = np.ascontiguousarray(layer_in[l][t])
+            m = margin(tf_lg[t], w.k)
+            if m >= 1e-3:
+                y, i, ww, _ = oracle.layer(d, Lh, xt[None, :])
+                y, ww = y[0], ww[0]
+                assert np.array_equal(gi[l, t], i[0]), (t, l, gi[l, t], i[0])
+            else:
+                assert valid_selection(tf_lg[t], gi[l, t], w.k, 4e-4), (t, l, m, gi[l, t], tf_idx[t])
+                y, ww, _ = oracle.layer_given(d, Lh, xt, gi[l, t])
+            assert np.allclose(gw[l, t], ww, rtol=1e-4, atol=1e-6), (t, l)
+            err = max_rel_err(to_f64(runs[l][0][t], w.act), to_f64(y, w.act))
+            assert err <= 2e-2, (t, l, err)
+            yf, _, _, _ = oracle.layer(d, Lh, np.ascontiguousarray(fr[t:t + 1]))
+            return err, m, yf[0]
+
+        res = pmap(check, range(B))
+        errs = [r[0] for r in res]
+        low += [(t, l, res[t][1]) for t in range(B) if res[t][1] < 1e-3]
+        worst = max(worst, max(errs))
+        log(f"stack B={B} layer {l} teacher-forced: every token within the bar, max rel err {max(errs):.2e}")
+        fr = np.stack([r[2] for r in res])
+        fr_agree &= np.all(fr_idx == gi[l], axis=1)
+        drop_experts(Lh)
+    fr_err = np.array([max_rel_err(to_f64(gy[t], w.act), to_f64(fr[t], w.act)) for t in range(B)])
+    log(f"stack B={B}: teacher-forced max rel err {worst:.2e}; margin < 1e-3 at (token, layer, margin) {low}")
+    log(f"stack B={B} free-running {w.layers} layers: max rel err {fr_err.max():.2e} over all tokens, "
+        f"{fr_err[fr_agree].max() if fr_agree.any() else 0:.2e} over the {int(fr_agree.sum())} tokens routed "
+        f"identically at every layer")
+    assert np.all(fr_err[fr_agree] <= w.layers * 2e-2)
 
 
 # ---- properties -----------------------------------------------------------------------
@@ -445,24 +430,43 @@ def test_repeatable_inplace_and_batch_invariant(dev):
     free()
 
 
-def test_watchdog_reports_timeout_then_recovers(dev, monkeypatch):
-    """A host-set limit of 0 ticks makes each barrier wait give up at once; the
-    launch still completes, the workspace reports MOE_ERR_TIMEOUT once, and the
-    next call on the same workspace is correct."""
+def test_watchdog_reports_timeout_then_recovers(dev):
+    """A host-set limit of 0 ticks makes each wait that would block give up at
+    once; the launch still completes, its untrusted outputs are visible (NaN
+    rows of y, -1 / NaN routing), the workspace reports MOE_ERR_TIMEOUT once,
+    and the next call on the same workspace is correct. Both regimes and the
+    stack."""
     w = synth.WORKLOADS["tiny_f32"]
     dl = DeviceLayer(w, device=dev)
     d = desc_of(w)
-    x = synth.x_tokens(w, 2)
-    ref = gpu_layer(w, dl, x, 2, dev)
-    xd, yd = to_device(x, dev), act_tensor(w, 2, dev)
-    ws = workspace(d, 2, 1, dev)
-    monkeypatch.setenv("MOE_DEBUG_BARRIER_TIMEOUT_TICKS", "0")
-    md.moe_decode_layer(d, dl.weights, xd, yd, 2, None, None, ws)
-    torch.cuda.synchronize()
-    monkeypatch.delenv("MOE_DEBUG_BARRIER_TIMEOUT_TICKS")
-    assert md.moe_check_workspace(ws) == md.MOE_ERR_TIMEOUT
-    assert md.moe_check_workspace(ws) == md.MOE_OK
-    md.moe_decode_layer(d, dl.weights, xd, yd, 2, None, None, ws)
-    torch.cuda.synchronize()
-    assert md.moe_check_workspace(ws) == md.MOE_OK
-    assert np.array_equal(to_host(yd), ref["y"])
+    for B, L in ((2, 1), (9, 1), (2, 3), (9, 3)):
+        x = synth.x_tokens(w, B)
+        xd, yd = to_device(x, dev), act_tensor(w, B, dev)
+        ws = workspace(d, B, L, dev)
+        idx = torch.zeros((L, B, w.k), dtype=torch.int32, device=dev)
+        wts = torch.zeros((L, B, w.k), dtype=torch.float32, device=dev)
+        md.moe_decode_stack(d, [dl.weights] * L, xd, yd, B, idx, wts, ws)
+        torch.cuda.synchronize()
+        ref = to_host(yd).copy()
+        assert md.moe_check_workspace(ws) == md.MOE_OK and np.all(np.isfinite(ref))
+        md.moe_set_watchdog_ticks(0)
+        try:
+            md.moe_decode_stack(d, [dl.weights] * L, xd, yd, B, idx, wts, ws)
+            torch.cuda.synchronize()
+        finally:
+            md.moe_set_watchdog_ticks(-1)
+        y0 = to_host(yd)
+        assert md.moe_check_workspace(ws) == md.MOE_ERR_TIMEOUT
+        assert md.moe_check_workspace(ws) == md.MOE_OK
+        nan_rows = np.isnan(y0).any(axis=1)
+        log(f"watchdog B={B} L={L}: {int(np.isnan(y0).sum())} NaN outputs, routing poisoned "
+            f"{bool((idx.cpu().numpy() == -1).all())}")
+        assert nan_rows.all()  # every token has untrusted rows
+        assert np.all(np.isnan(y0) | (y0 == ref))  # rows not written as NaN are the correct ones
+        assert (idx.cpu().numpy() == -1).all() and np.isnan(wts.cpu().numpy()).all()
+        md.moe_decode_stack(d, [dl.weights] * L, xd, yd, B, idx, wts, ws)
+        torch.cuda.synchronize()
+        assert md.moe_check_workspace(ws) == md.MOE_OK
+        assert np.array_equal(to_host(yd), ref)
+    del dl
+    free()

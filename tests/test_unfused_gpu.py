@@ -10,7 +10,8 @@ import torch
 import moe_decode_02_amd as md
 import oracle
 import synth
-from helpers import draw_tokens_with_margin, host_layer, max_rel_err, small_workload, to_f64
+from helpers import (add_experts, draw_tokens_with_margin, host_layer, max_rel_err, oracle_layer_tokens,
+                     small_workload, to_f64)
 from synth.device import DeviceLayer, act_tensor, desc_of, to_device, to_host
 
 pytestmark = pytest.mark.gpu
@@ -45,9 +46,9 @@ def unfused_layer(w, dl, x, B, dev):
     return {"y": to_host(yd), "idx": idx.cpu().numpy(), "w": wts.cpu().numpy()}
 
 
-def parity(w, B, dev, sample=None, random_gamma=False):
-    """Tokens `sample` (default all) of a B-token batch against the oracle;
-    unselected experts hold NaN, so a wrong gather poisons the output."""
+def parity(w, B, dev, random_gamma=False):
+    """Every token of a B-token batch against the oracle; unselected experts
+    hold NaN, so a wrong gather poisons the output."""
     Lh = host_layer(w, experts=[], random_gamma=random_gamma)
     x, _ = draw_tokens_with_margin(w, B, [Lh])
     d = oracle.desc_of(w)
@@ -55,14 +56,10 @@ def parity(w, B, dev, sample=None, random_gamma=False):
     for t in range(B):
         xhat, _ = oracle.rmsnorm(d, x[t], Lh.gamma)
         idx_r[t], _ = oracle.route(d, oracle.router_logits(d, Lh, xhat))
-    tok = list(range(B)) if sample is None else sample
-    for e in sorted(set(int(i) for i in idx_r[tok].ravel())):
-        Lh.gate_up[e], s1 = synth.expert_gate_up(w, e)
-        Lh.down[e], s2 = synth.expert_down(w, e)
-        if s1 is not None:
-            Lh.gate_up_scale[e], Lh.down_scale[e] = s1, s2
-    y_ref, idx_o, w_o, _ = oracle.layer(d, Lh, x[tok])
-    log(f"gpu unfused: {w.name} B={B} tokens {len(tok)}")
+    tok = list(range(B))
+    add_experts(w, Lh, idx_r)
+    y_ref, idx_o, w_o, _ = oracle_layer_tokens(d, Lh, x)
+    log(f"gpu unfused: {w.name} B={B}")
     dl = DeviceLayer(w, device=dev, experts=idx_r, random_gamma=random_gamma)
     got = unfused_layer(w, dl, x, B, dev)
     assert np.array_equal(got["idx"], idx_r)
@@ -103,5 +100,5 @@ def test_unfused_k3_b1(dev):
     parity(synth.WORKLOADS["k3_b1"], 1, dev)
 
 
-def test_unfused_k3_b8_sampled(dev):
-    parity(synth.WORKLOADS["k3_b8"], 8, dev, sample=[0, 7])
+def test_unfused_k3_b8(dev):
+    parity(synth.WORKLOADS["k3_b8"], 8, dev)
