@@ -17,6 +17,8 @@ from functools import lru_cache
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libmoedecode.so")
+# the ordering-stress build (same source, -DMOE_DEBUG_DELAY; include/moedecode_debug.h)
+DELAY_PATH = os.path.join(_HERE, "libmoedecode_delay.so")
 SOURCES = [os.path.join(_HERE, "csrc", "moedecode.hip")]
 INCLUDE = os.path.join(_ROOT, "include")
 HEADER = os.path.join(INCLUDE, "moedecode.h")
@@ -34,13 +36,20 @@ PROBE_SOURCES = [os.path.join(_HERE, "csrc", "bench_probe.hip")]
 
 
 def build(force: bool = True) -> str:
-    """Compile libmoedecode.so (and the benchmark's probe library) in-tree for
-    gfx950; hipcc cross-compiles without a GPU."""
-    for path, srcs in ((LIB_PATH, SOURCES), (PROBE_PATH, PROBE_SOURCES)):
+    """Compile libmoedecode.so, its ordering-stress build and the benchmark's
+    probe library in-tree for gfx950 (hipcc cross-compiles without a GPU); the
+    compilers run side by side."""
+    jobs = []
+    for path, srcs, extra in ((LIB_PATH, SOURCES, []), (DELAY_PATH, SOURCES, ["-DMOE_DEBUG_DELAY"]),
+                              (PROBE_PATH, PROBE_SOURCES, [])):
         if force or not os.path.exists(path):
             tmp = path + ".tmp"
-            subprocess.check_call(["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, *srcs])
-            os.replace(tmp, path)
+            cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-o", tmp, *srcs]
+            jobs.append((subprocess.Popen(cmd), cmd, tmp, path))
+    for proc, cmd, tmp, path in jobs:
+        if proc.wait() != 0:
+            raise subprocess.CalledProcessError(proc.returncode, cmd)
+        os.replace(tmp, path)
     return LIB_PATH
 
 
@@ -81,9 +90,23 @@ EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_decode_layer", "moe_decode_s
 
 @lru_cache(maxsize=None)
 def lib():
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() (no fallback exists)")
-    L = ctypes.CDLL(LIB_PATH)
+    """The production library."""
+    return _bind(LIB_PATH)
+
+
+@lru_cache(maxsize=None)
+def delay_lib():
+    """The ordering-stress build: the same entry points plus moe_debug_set_delay."""
+    L = _bind(DELAY_PATH)
+    L.moe_debug_set_delay.argtypes = [ctypes.c_uint64, ctypes.c_int32]
+    L.moe_debug_set_delay.restype = None
+    return L
+
+
+def _bind(path):
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run __graft_entry__.build() (no fallback exists)")
+    L = ctypes.CDLL(path)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     D, Wt = ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights)
     L.moe_workspace_bytes.argtypes = [D, i32, i32]
@@ -135,9 +158,9 @@ def _bytes(t):
     return t.numel() * t.element_size()
 
 
-def _check(status: int) -> None:
+def _check(status: int, library=None) -> None:
     if status != MOE_OK:
-        raise MoeError(status, lib().moe_last_error().decode())
+        raise MoeError(status, (library or lib()).moe_last_error().decode())
 
 
 def moe_status_string(status: int) -> str:
@@ -152,31 +175,34 @@ def moe_workspace_bytes(desc: moe_layer_desc, max_tokens: int, num_layers: int =
     return int(lib().moe_workspace_bytes(ctypes.byref(desc), max_tokens, num_layers))
 
 
-def moe_route(desc, weights, x, B, topk_idx, topk_w, logits, ws, ws_bytes=None, stream=None, check=True):
-    st = lib().moe_route(ctypes.byref(desc), ctypes.byref(weights), _addr(x), B, _addr(topk_idx),
+def moe_route(desc, weights, x, B, topk_idx, topk_w, logits, ws, ws_bytes=None, stream=None, check=True,
+              library=None):
+    st = (library or lib()).moe_route(ctypes.byref(desc), ctypes.byref(weights), _addr(x), B, _addr(topk_idx),
                          _addr(topk_w), _addr(logits), _addr(ws),
                          _bytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
     if check:
-        _check(st)
+        _check(st, library)
     return st
 
 
-def moe_decode_layer(desc, weights, x, y, B, topk_idx, topk_w, ws, ws_bytes=None, stream=None, check=True):
-    st = lib().moe_decode_layer(ctypes.byref(desc), ctypes.byref(weights), _addr(x), _addr(y), B,
+def moe_decode_layer(desc, weights, x, y, B, topk_idx, topk_w, ws, ws_bytes=None, stream=None, check=True,
+                     library=None):
+    st = (library or lib()).moe_decode_layer(ctypes.byref(desc), ctypes.byref(weights), _addr(x), _addr(y), B,
                                 _addr(topk_idx), _addr(topk_w), _addr(ws),
                                 _bytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
     if check:
-        _check(st)
+        _check(st, library)
     return st
 
 
-def moe_decode_stack(desc, layers, x, y, B, topk_idx, topk_w, ws, ws_bytes=None, stream=None, check=True):
+def moe_decode_stack(desc, layers, x, y, B, topk_idx, topk_w, ws, ws_bytes=None, stream=None, check=True,
+                     library=None):
     arr = (moe_layer_weights * len(layers))(*layers)
-    st = lib().moe_decode_stack(ctypes.byref(desc), arr, len(layers), _addr(x), _addr(y), B,
+    st = (library or lib()).moe_decode_stack(ctypes.byref(desc), arr, len(layers), _addr(x), _addr(y), B,
                                 _addr(topk_idx), _addr(topk_w), _addr(ws),
                                 _bytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
     if check:
-        _check(st)
+        _check(st, library)
     return st
 
 
@@ -184,18 +210,19 @@ def moe_unfused_workspace_bytes(desc: moe_layer_desc, max_tokens: int) -> int:
     return lib().moe_unfused_workspace_bytes(ctypes.byref(desc), max_tokens)
 
 
-def moe_decode_layer_unfused(desc, weights, x, y, B, topk_idx, topk_w, ws, ws_bytes=None, stream=None, check=True):
-    st = lib().moe_decode_layer_unfused(ctypes.byref(desc), ctypes.byref(weights), _addr(x), _addr(y), B,
+def moe_decode_layer_unfused(desc, weights, x, y, B, topk_idx, topk_w, ws, ws_bytes=None, stream=None, check=True,
+                             library=None):
+    st = (library or lib()).moe_decode_layer_unfused(ctypes.byref(desc), ctypes.byref(weights), _addr(x), _addr(y), B,
                                         _addr(topk_idx), _addr(topk_w), _addr(ws),
                                         _bytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
     if check:
-        _check(st)
+        _check(st, library)
     return st
 
 
-def moe_set_watchdog_ticks(ticks: int) -> None:
-    lib().moe_set_watchdog_ticks(ticks)
+def moe_set_watchdog_ticks(ticks: int, library=None) -> None:
+    (library or lib()).moe_set_watchdog_ticks(ticks)
 
 
-def moe_check_workspace(ws, ws_bytes=None, stream=None) -> int:
-    return lib().moe_check_workspace(_addr(ws), _bytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
+def moe_check_workspace(ws, ws_bytes=None, stream=None, library=None) -> int:
+    return (library or lib()).moe_check_workspace(_addr(ws), _bytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))

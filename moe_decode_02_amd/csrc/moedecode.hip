@@ -69,6 +69,9 @@
 #include <string.h>
 
 #include "moedecode.h"
+#ifdef MOE_DEBUG_DELAY
+#include "moedecode_debug.h"
+#endif
 
 namespace {
 
@@ -135,6 +138,10 @@ struct Params {
   int rows_per_wg;        // P2 output rows per workgroup (multiple of kRowBlock)
   float eps;
   long long timeout_ticks;  // s_memrealtime ticks (100 MHz) before a barrier wait gives up
+  // ordering-stress build only (MOE_DEBUG_DELAY): seed of the injected delays,
+  // and the workgroup -> work permutation g -> (perm_a * g + perm_c) mod G
+  unsigned long long dbg_seed;
+  int perm_a, perm_c;
   unsigned *ctrl;         // control words, kCtrlStride apart
   float *xhat;            // [B][H] fp32 (general regime)
   void *xa;               // [B][H] act (general regime; == xhat for fp32 activations)
@@ -340,6 +347,41 @@ template <> struct XSrc<true> {
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
 __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
 
+// The work of "workgroup g" (every share of tasks, rows and tiles is keyed
+// by it). The ordering-stress build maps the hardware workgroups onto these
+// shares through a seeded permutation, so that which CU, XCD and launch
+// position takes which share changes between runs; results must not.
+__device__ __forceinline__ int wg_id(KParams p) {
+#ifdef MOE_DEBUG_DELAY
+  return (int)(((long long)p->perm_a * blockIdx.x + p->perm_c) % p->G);
+#else
+  (void)p;
+  return (int)blockIdx.x;
+#endif
+}
+
+// Ordering-stress build: a seeded pause of up to ~55 us for about one call in
+// four, keyed by (seed, workgroup, wave, site, arg), before barrier arrivals,
+// published logits, expert tasks, output units, routing and the combine.
+// Every result must be bit-identical to the undelayed run. Other builds: no code.
+enum : int { DLY_START = 0, DLY_ARRIVE, DLY_PUBLISH, DLY_P1, DLY_P2, DLY_COMBINE, DLY_ROUTE, DLY_STAGE, DLY_CLEAR };
+__device__ __forceinline__ void dbg_delay(KParams p, int site, int arg) {
+#ifdef MOE_DEBUG_DELAY
+  if (p->dbg_seed == 0) return;
+  unsigned long long z = p->dbg_seed ^ ((unsigned long long)site << 56) ^ ((unsigned long long)wg_id(p) << 40) ^
+                         ((unsigned long long)wave_id() << 32) ^ (unsigned)arg;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;  // SplitMix64 output function (Steele, Lea, Flood)
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  if ((z & 3u) == 0) {
+    const int n = 1 + (int)((z >> 8) & 15u);
+    for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(127);
+  }
+#else
+  (void)p; (void)site; (void)arg;
+#endif
+}
+
 // ---------------------------------------------------------------------------
 // DPP cross-lane operations (wave64). After the six steps below lane 63 holds
 // the reduction of the whole wave: quad swaps, half-row and row mirrors give
@@ -516,6 +558,7 @@ template <int D> __device__ __forceinline__ void publish_act(void *p, size_t i, 
 // complete (they are then visible device-wide) replaces the L2 write-back.
 // Readers still acquire at agent scope (L1/L2 invalidate) before reading.
 __device__ void bar_arrive_published(KParams p, SmemHead &sh, int b) {
+  dbg_delay(p, DLY_ARRIVE, b);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   if (lane_id() == 0) {
@@ -529,6 +572,7 @@ __device__ void bar_arrive_published(KParams p, SmemHead &sh, int b) {
 // its own stores to reach the L2 (a workgroup-scope release does not wait for
 // them), so the last wave's L2 write-back covers every wave's stores.
 __device__ void bar_arrive(KParams p, SmemHead &sh, int b) {
+  dbg_delay(p, DLY_ARRIVE, b);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   if (lane_id() == 0) {
@@ -710,7 +754,7 @@ __device__ __attribute__((noinline)) void produce_xhat(KParams p_arg, KLayer lp_
   const KParams p = uni(p_arg);
   const KLayer lp = uni(lp_arg);
   const int H = p->H;
-  for (int t = blockIdx.x; t < p->B; t += p->G) {
+  for (int t = wg_id(p); t < p->B; t += p->G) {
     const int tok[1] = {t};
     rmsnorm_rows<AD, 1>(p, lp, L.head(), tok, [&](int, int h, float v) {
       p->xhat[(size_t)t * H + h] = v;
@@ -777,6 +821,7 @@ __device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, 
       const float v = wave_sum63(acc[0][t]);
       if (t < nt && lane_id() == 63) {
         if (NSR == 1) {
+          dbg_delay(p, DLY_PUBLISH, e);
           if constexpr (XL) publish(lp->lg + (size_t)(t0 + t) * E + e, nonzero_bits(v + bias));
           else lp->lg[(size_t)(t0 + t) * E + e] = v + bias;
         } else {
@@ -786,6 +831,7 @@ __device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, 
     }
   });
   if (NSR > 1 && last_slice(L.head().rcnt, round, NSR)) {
+    dbg_delay(p, DLY_PUBLISH, e);
     const int w0 = wave_id() - s;
     for (int t = lane_id(); t < B; t += 64) {
       float sum = slice_slot(p, L, round, w0)[t];
@@ -1158,6 +1204,7 @@ __device__ __attribute__((noinline)) void build_tables_wave(KParams p_arg, const
 
 template <int AD, int ED, bool XL>
 __device__ __forceinline__ void expert_gu_task(KParams p, KLayer lp, const Lds &L, int u, int j) {
+  dbg_delay(p, DLY_P1, u * 4096 + j);
   const int H = p->H, I = p->I, k = p->k;
   const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   const int *plist = L.at<int>(p->o_plist);
@@ -1281,10 +1328,12 @@ template <bool SMALL> __device__ __forceinline__ int part_cs(KParams p) { return
 
 // Next P2 unit of this wave, handed out through the workgroup's LDS counter
 // `which` (so a wave that starts late takes fewer).
-__device__ __forceinline__ int next_unit(SmemHead &sh, int which) {
+__device__ __forceinline__ int next_unit(KParams p, SmemHead &sh, int which) {
   int u = 0;
   if (lane_id() == 0) u = __hip_atomic_fetch_add(&sh.unit_ctr[which], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  return __builtin_amdgcn_readfirstlane(u);
+  u = __builtin_amdgcn_readfirstlane(u);
+  dbg_delay(p, DLY_P2, which * 65536 + u);
+  return u;
 }
 
 // shared-expert units of rows [pr0, pr1): (row block, column block hf); the
@@ -1296,7 +1345,7 @@ __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Ld
   const int nrb = (pr1 - pr0) / kRowBlock;
   float *part = part_base<SMALL>(p, L);
   const int prb = SMALL ? pr0 : 0;
-  for (int un = next_unit(L.head(), 0); un < nrb * nsh; un = next_unit(L.head(), 0)) {
+  for (int un = next_unit(p, L.head(), 0); un < nrb * nsh; un = next_unit(p, L.head(), 0)) {
     const int hf = un / nrb, rb = un % nrb;
     const int o0 = pr0 + rb * kRowBlock;
     const int kw = min(I, Is - hf * I);  // columns of block hf (the last may be partial)
@@ -1448,6 +1497,7 @@ __device__ __forceinline__ void with_token_tiles(int n, F &&f) {
 // matrices for all of the expert's tokens; h = SiLU(g) * u to hbuf.
 template <int AD, int ED>
 __device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L, int u, int jb) {
+  dbg_delay(p, DLY_P1, u * 4096 + jb);
   const int H = p->H, I = p->I, k = p->k, lane = lane_id();
   const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   const int *pl = L.at<int>(p->o_plist) + ustart[u];
@@ -1578,7 +1628,7 @@ __device__ __attribute__((noinline)) void router_mfma(KParams p_arg, KLayer lp_a
   const int H = p->H, E = p->E, B = p->B, lane = lane_id(), wv = wave_id();
   const int r = lane & 15, kq = lane >> 4;
   const int b0 = router_tile_blk(H, wv), b1 = router_tile_blk(H, wv + 1);
-  for (int tile = blockIdx.x; tile < router_tiles(E); tile += p->G) {
+  for (int tile = wg_id(p); tile < router_tiles(E); tile += p->G) {
     const unsigned wo = (unsigned)((size_t)min(16 * tile + r, E - 1) * H * dsz<RD>()) + (unsigned)(kq * 4 * dsz<RD>());
     const char *wb = (const char *)lp->rw;
     const char *xb = (const char *)p->xhat;
@@ -1680,7 +1730,7 @@ __device__ __attribute__((noinline)) void shared_gu_mfma(KParams p_arg, KLayer l
   const int k0 = shared_tile_k(H, wv), k1 = shared_tile_k(H, wv + 1);
   float *red = L.at<float>(p->o_red);  // [kWaves][16][B]
   const char *xa = (const char *)p->xa + (size_t)k0 * 2;
-  for (int j = shared_tile0(p, blockIdx.x); j < Is / 8; j += shared_tile_step(p)) {
+  for (int j = shared_tile0(p, wg_id(p)); j < Is / 8; j += shared_tile_step(p)) {
     const char *wb = (const char *)lp->sgu + (size_t)k0 * 2;
     const unsigned wo[1] = {(unsigned)((size_t)shared_tile_row(Is, j, r) * H * 2)};  // < 4 GB
     with_token_tiles(B, [&]<int NT>() {
@@ -1726,7 +1776,7 @@ __device__ __forceinline__ void shared_down_mfma(KParams p, KLayer lp, const Lds
   const int r = lane & 15, kq = lane >> 4;
   const int ntile = (pr1 - pr0 + 15) / 16;
   float *part = p->partbuf;
-  for (int un = next_unit(L.head(), 0); un < ntile * nsh; un = next_unit(L.head(), 0)) {
+  for (int un = next_unit(p, L.head(), 0); un < ntile * nsh; un = next_unit(p, L.head(), 0)) {
     const int hf = un / ntile, ti = un % ntile;
     const int o0 = min(pr0 + 16 * ti, pr1 - 16);  // the last tile ends at pr1
     const int lo = pr0 + 16 * ti;                 // rows below lo belong to the previous tile
@@ -1848,7 +1898,7 @@ __device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Ld
   float *part = part_base<SMALL>(p, L);
   const int prb = SMALL ? pr0 : 0;
   const int nu = ub - ua;
-  for (int un = next_unit(L.head(), uc); un < nrb * nu; un = next_unit(L.head(), uc)) {
+  for (int un = next_unit(p, L.head(), uc); un < nrb * nu; un = next_unit(p, L.head(), uc)) {
     const int s = ua + un / nrb, o0 = pr0 + (un % nrb) * kRowBlock;
     expert_down_gemv<AD, ED, SMALL>(p, lp, L, s, o0, part + (size_t)(o0 - prb) * part_rs<SMALL>(p, pstride),
                                     part_rs<SMALL>(p, pstride), part_cs<SMALL>(p));
@@ -1869,7 +1919,7 @@ __device__ __forceinline__ void expert_down_listed(KParams p, KLayer lp, const L
   const int ma = min(ia, nM), mb = min(ib, nM);
   const int nmu = (mb - ma) * (ntile > 0 ? ntile : nrb);
   const int total = nmu + (max(ib, nM) - max(ia, nM)) * nrb;
-  for (int un = next_unit(L.head(), uc); un < total; un = next_unit(L.head(), uc)) {
+  for (int un = next_unit(p, L.head(), uc); un < total; un = next_unit(p, L.head(), uc)) {
     if (un < nmu && ntile > 0) {
       const int ti = un % ntile;
       const int o0 = min(pr0 + 16 * ti, pr1 - 16);  // the last tile ends at pr1
@@ -1895,6 +1945,7 @@ __device__ __forceinline__ void combine(KParams p, KLayer lp, const Lds &L, int 
   const int prb = SMALL ? pr0 : 0;
   const float *sel_w = L.at<float>(p->o_sel_w);
   const int nr = pr1 - pr0, cells = nr * B;
+  dbg_delay(p, DLY_COMBINE, 0);
   for (int c = threadIdx.x; c < cells; c += kThreads) {
     const int ro = c % nr, t = c / nr;  // consecutive threads: consecutive rows (coalesced x, y, partials)
     const int o = pr0 + ro;
@@ -1938,7 +1989,7 @@ __device__ __forceinline__ unsigned prefetch_p0(KParams p, KLayer nl) {
   const int nrt = E * NSR;
   unsigned acc = 0;
   for (int r = 0; r < p->p0r; ++r) {
-    const int tau = p0_task(p, r, blockIdx.x, wave_id());
+    const int tau = p0_task(p, r, wg_id(p), wave_id());
     if (tau < 0 || tau >= p->p0_end) continue;
     if (tau < nrt) {
       const int e = tau / NSR, s = tau % NSR;
@@ -1954,18 +2005,18 @@ __device__ __forceinline__ unsigned prefetch_p0(KParams p, KLayer nl) {
   }
   if (MSH) {
     // this wave's columns of the workgroup's first router tile
-    if ((int)blockIdx.x < router_tiles(E)) {
-      const int tile = blockIdx.x;
+    if (wg_id(p) < router_tiles(E)) {
+      const int tile = wg_id(p);
       const int b0 = router_tile_blk(H, wave_id()), b1 = router_tile_blk(H, wave_id() + 1);
       for (int r = 0; r < 16 && 16 * tile + r < E; ++r)
         acc ^= touch_lines((const char *)nl->rw + ((size_t)(16 * tile + r) * H + (size_t)b0 * 16) * dsz<RD>(),
                            (size_t)(b1 - b0) * 16 * dsz<RD>());
     }
   }
-  if (MSH && shared_tile0(p, blockIdx.x) < Is / 8) {
+  if (MSH && shared_tile0(p, wg_id(p)) < Is / 8) {
     // this wave's columns of the workgroup's first shared MFMA tile
     const int k0 = shared_tile_k(H, wave_id()), k1 = shared_tile_k(H, wave_id() + 1);
-    const int j = shared_tile0(p, blockIdx.x);
+    const int j = shared_tile0(p, wg_id(p));
     for (int r = 0; r < 16; ++r)
       acc ^= touch_lines((const char *)nl->sgu + (size_t)shared_tile_row(Is, j, r) * H * dsz<SD>() +
                              (size_t)k0 * dsz<SD>(),
@@ -1998,7 +2049,7 @@ __device__ __forceinline__ void p0_tasks(KParams p, KLayer lp, const Lds &L, int
   const int nrt = p->E * p->NSR, s0 = p->s0, end = p->p0_end;
   bool routed = false;  // arrived at the router barrier
   for (int r = 0; r < p->p0r; ++r) {
-    const int tau = p0_task(p, r, blockIdx.x, wave_id());
+    const int tau = p0_task(p, r, wg_id(p), wave_id());
     if (tau < 0 || tau >= end) break;
     if (tau >= nrt && !routed) {
       if constexpr (!PUB) bar_arrive(p, sh, b0 + BAR_ROUTER);
@@ -2070,7 +2121,7 @@ __device__ __forceinline__ void p1_cost_range(KParams p, KLayer lp, const Lds &L
 template <int AD, int RD, int ED, int SD>
 __device__ __forceinline__ bool layer_small(KParams p, KLayer lp, const Lds &L, int b0, int W, int NW) {
   SmemHead &sh = L.head();
-  const int G = p->G, g = blockIdx.x;
+  const int G = p->G, g = wg_id(p);
   stage_xhat<AD>(p, lp, L);
 
   // P0
@@ -2082,7 +2133,8 @@ __device__ __forceinline__ bool layer_small(KParams p, KLayer lp, const Lds &L, 
     claimed = __hip_atomic_exchange(&sh.route_claim, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
   claimed = __builtin_amdgcn_readfirstlane(claimed);
   if (claimed) {
-    for (int t = 0; t < p->B; ++t) topk_token<true>(p, lp, L, t, blockIdx.x == 0);
+    dbg_delay(p, DLY_ROUTE, 0);
+    for (int t = 0; t < p->B; ++t) topk_token<true>(p, lp, L, t, g == 0);
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
     build_tables_wave(p, L);
     raise_flag(sh.route_ready);
@@ -2111,6 +2163,7 @@ __device__ __forceinline__ bool layer_small(KParams p, KLayer lp, const Lds &L, 
   sclaim = __builtin_amdgcn_readfirstlane(sclaim);
   if (sclaim) {
     bar_wait(p, sh, b0 + BAR_SHARED);
+    dbg_delay(p, DLY_STAGE, 0);
     stage_shared_h_wave<AD>(p, L);
     raise_flag(sh.shared_ready);
   } else {
@@ -2140,6 +2193,7 @@ __device__ __forceinline__ bool layer_small(KParams p, KLayer lp, const Lds &L, 
   // use of the buffer (the stores complete before the layer barrier or the
   // end of the launch)
   if (wave_id() == 0) {
+    dbg_delay(p, DLY_CLEAR, 0);
     const int n = p->B * p->E;
     for (int i = share_lo(n, g, G) + lane_id(); i < share_lo(n, g + 1, G); i += 64) publish(lp->lg + i, 0.f);
   }
@@ -2160,10 +2214,11 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
   SmemHead &sh = L.head();
   const int tid = threadIdx.x, wv = wave_id();
   const int NW = p->G * kWaves;
-  const int W = blockIdx.x * kWaves + wv;  // global wave id
+  const int W = wg_id(p) * kWaves + wv;  // global wave id of this share
 
   for (int i = tid; i < kMaxBarriers; i += kThreads) sh.bar_cnt[i] = sh.bar_claim[i] = sh.bar_flag[i] = 0;
   if (tid == 0) sh.sink = sh.expired = 0;
+  dbg_delay(p, DLY_START, 0);
 
   unsigned sink = 0;
   bool poisoned = false;  // a wait gave up during this launch (this workgroup's, or one before a barrier it passed)
@@ -2190,7 +2245,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       else bar_arrive(p, sh, b0 + BAR_ROUTER);
       bar_wait(p, sh, b0 + BAR_ROUTER);
       poisoned = err_word(p) != 0;
-      if (blockIdx.x == 0)
+      if (wg_id(p) == 0)
         for (int t = wv; t < p->B; t += kWaves) topk_token<false>(p, lp, L, t, true);
       break;
     }
@@ -2214,7 +2269,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       // falls in its equal share, so all waves finish group 0 first and the
       // down projections of early groups overlap the later gate/up work.
       bar_wait(p, sh, b0 + BAR_ROUTER);
-      for (int t = wv; t < p->B; t += kWaves) topk_token<false>(p, lp, L, t, blockIdx.x == 0);
+      for (int t = wv; t < p->B; t += kWaves) topk_token<false>(p, lp, L, t, wg_id(p) == 0);
       __syncthreads();
       build_tables(p, L);
       classify_slots(p, L);
@@ -2230,7 +2285,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       // P2: this workgroup's output rows, partial sums in global memory; the
       // shared expert's rows first, then each group's routed rows once its
       // barrier has passed
-      const int r0 = blockIdx.x * p->rows_per_wg;
+      const int r0 = wg_id(p) * p->rows_per_wg;
       const int r1 = min(p->H, r0 + p->rows_per_wg);
       bar_wait(p, sh, b0 + BAR_SHARED);
       if (r0 < r1) {
@@ -2264,7 +2319,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
   // after a watchdog stop the routing outputs are not trusted either: the
   // workgroup that wrote them overwrites them with -1 / NaN
   const bool poison_out = __syncthreads_or(poisoned || sh.expired != 0);
-  if (blockIdx.x == 0 && poison_out) {
+  if (wg_id(p) == 0 && poison_out) {
     const int n = p->B * p->k;
     for (int l = 0; l < p->L; ++l) {
       KLayer lp = &p->lp[l];
@@ -2621,6 +2676,14 @@ std::mutex g_dev_mu;
 constexpr long long kDefaultWatchdogTicks = 200000000LL;  // 2 s
 std::atomic<long long> g_watchdog_ticks{kDefaultWatchdogTicks};
 
+#ifdef MOE_DEBUG_DELAY
+// ordering-stress build: delay seed (0 = none) and grid size (0 = one workgroup per CU)
+std::atomic<unsigned long long> g_dbg_seed{0};
+std::atomic<int> g_dbg_grid{0};
+
+int gcd_int(int a, int b) { while (b) { const int t = a % b; a = b; b = t; } return a; }
+#endif
+
 moe_status current_device(int &dev) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_DEVICE, "hipGetDevice failed");
   return MOE_OK;
@@ -2805,6 +2868,23 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   p.nsh = shared_blocks(d);
   p.G = cus;
   if (p.G < 1) return fail(MOE_ERR_DEVICE, "device reports no compute units");
+  p.perm_a = 1;
+  p.perm_c = 0;
+#ifdef MOE_DEBUG_DELAY
+  {
+    const int grid = g_dbg_grid.load(std::memory_order_relaxed);
+    if (grid > 0 && grid < p.G) p.G = grid;  // fewer workgroups than CUs: still all resident
+    const unsigned long long seed = g_dbg_seed.load(std::memory_order_relaxed);
+    p.dbg_seed = seed;
+    if (seed != 0 && p.G > 1) {
+      int a = (int)(((seed >> 17) * 2 + 1) % (unsigned long long)p.G);  // odd start, then the next unit mod G
+      if (a < 1) a = 1;
+      while (gcd_int(a, p.G) != 1) a = a % p.G + 1;
+      p.perm_a = a;
+      p.perm_c = (int)(seed % (unsigned long long)p.G);
+    }
+  }
+#endif
   // the regime: B <= kSmallB keeps x-hat in every workgroup's LDS when it
   // fits; otherwise (or for larger B) the general regime
   bool small = small_regime(B);
@@ -3126,6 +3206,13 @@ const char *moe_status_string(moe_status s) {
 }
 
 const char *moe_last_error(void) { return g_err; }
+
+#ifdef MOE_DEBUG_DELAY
+void moe_debug_set_delay(uint64_t seed, int32_t grid) {
+  g_dbg_seed.store(seed, std::memory_order_relaxed);
+  g_dbg_grid.store(grid < 0 ? 0 : grid, std::memory_order_relaxed);
+}
+#endif
 
 void moe_set_watchdog_ticks(int64_t ticks) {
   g_watchdog_ticks.store(ticks < 0 ? kDefaultWatchdogTicks : (long long)ticks, std::memory_order_relaxed);

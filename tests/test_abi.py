@@ -30,6 +30,20 @@ def test_exports_every_declared_function(lib):
         assert hasattr(lib, n), n
 
 
+def test_stress_build_exports(lib):
+    """The ordering-stress build exports every entry point of moedecode.h plus
+    the call of moedecode_debug.h; the production library does not export it."""
+    md.build(force=False)
+    L = md.delay_lib()
+    for n in header_functions():
+        assert hasattr(L, n), n
+    text = re.sub(r"/\*.*?\*/", "", open(md.HEADER.replace("moedecode.h", "moedecode_debug.h")).read(), flags=re.S)
+    dbg = sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    assert dbg == ["moe_debug_set_delay"] and hasattr(L, dbg[0])
+    with pytest.raises(AttributeError):
+        getattr(lib, "moe_debug_set_delay")
+
+
 def test_status_strings(lib):
     for code, name in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARGUMENT"), (2, "MOE_ERR_UNSUPPORTED"),
                        (3, "MOE_ERR_WORKSPACE_TOO_SMALL"), (4, "MOE_ERR_DEVICE"), (5, "MOE_ERR_TIMEOUT")]:
