@@ -142,6 +142,24 @@ moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights 
                             const void *x, void *y, int32_t B, int32_t *topk_idx, float *topk_w,
                             void *ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as moe_decode_layer, with the library's own workspace instead of a
+ * caller-allocated one, so the call allocates nothing and needs no workspace
+ * argument. That workspace is one 16 MiB device array per GPU, held until the
+ * process ends, zeroed by a small fill kernel on `stream` at the first call on
+ * each device. Shapes whose moe_workspace_bytes(desc, B, 1) exceeds 16 MiB
+ * (at the K3 share, H = 7168, E = 896, k = 16, I = 1024, Is = 2048: batches
+ * above 27) return MOE_ERR_UNSUPPORTED before any launch. Every call on one
+ * GPU shares the array and finds it as the previous call left it: calls that
+ * overlap in time on one GPU (other streams or threads) race and give wrong
+ * results, so enqueue them on one stream. A watchdog stop shows in the
+ * outputs as for moe_decode_layer (NaN rows, -1 / NaN routing); the launch
+ * restores the array itself. Other arguments as for moe_decode_layer. */
+moe_status moe_decode_layer_static(const moe_layer_desc *desc, const moe_layer_weights *weights,
+                                   const void *x, void *y, int32_t B, int32_t *topk_idx, float *topk_w,
+                                   void *stream);
+
 /* L layers of the same shape, each with its own weights (layers: host array of
  * L structs), in one persistent launch: y = layer_{L-1}(... layer_0(x)), each
  * layer's bf16 output feeding the next layer's RMSNorm. The layers stay in one

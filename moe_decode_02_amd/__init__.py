@@ -83,7 +83,7 @@ class moe_layer_weights(ctypes.Structure):
                 ("shared_down", ctypes.c_void_p)]
 
 
-EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_decode_layer", "moe_decode_stack",
+EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_decode_layer", "moe_decode_layer_static", "moe_decode_stack",
            "moe_unfused_workspace_bytes", "moe_decode_layer_unfused",
            "moe_check_workspace", "moe_set_watchdog_ticks", "moe_status_string", "moe_last_error")
 
@@ -115,6 +115,8 @@ def _bind(path):
     L.moe_route.restype = ctypes.c_int
     L.moe_decode_layer.argtypes = [D, Wt, vp, vp, i32, vp, vp, vp, sz, vp]
     L.moe_decode_layer.restype = ctypes.c_int
+    L.moe_decode_layer_static.argtypes = [D, Wt, vp, vp, i32, vp, vp, vp]
+    L.moe_decode_layer_static.restype = ctypes.c_int
     L.moe_decode_stack.argtypes = [D, Wt, i32, vp, vp, i32, vp, vp, vp, sz, vp]
     L.moe_decode_stack.restype = ctypes.c_int
     L.moe_unfused_workspace_bytes.argtypes = [D, i32]
@@ -190,6 +192,14 @@ def moe_decode_layer(desc, weights, x, y, B, topk_idx, topk_w, ws, ws_bytes=None
     st = (library or lib()).moe_decode_layer(ctypes.byref(desc), ctypes.byref(weights), _addr(x), _addr(y), B,
                                 _addr(topk_idx), _addr(topk_w), _addr(ws),
                                 _bytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
+    if check:
+        _check(st, library)
+    return st
+
+
+def moe_decode_layer_static(desc, weights, x, y, B, topk_idx, topk_w, stream=None, check=True, library=None):
+    st = (library or lib()).moe_decode_layer_static(ctypes.byref(desc), ctypes.byref(weights), _addr(x), _addr(y), B,
+                                                    _addr(topk_idx), _addr(topk_w), _stream(stream))
     if check:
         _check(st, library)
     return st

@@ -73,6 +73,13 @@
 #include "moedecode_debug.h"
 #endif
 
+// The library's own workspace for moe_decode_layer_static (callers that
+// cannot allocate device memory): every GPU the library runs on holds one copy
+// until the process ends. Host code never uses this name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -142,6 +149,7 @@ struct Params {
   // and the workgroup -> work permutation g -> (perm_a * g + perm_c) mod G
   unsigned long long dbg_seed;
   int perm_a, perm_c;
+  int self_reset;         // the workspace is the library's static array: the launch also clears a watchdog stop's state
   unsigned *ctrl;         // control words, kCtrlStride apart
   float *xhat;            // [B][H] fp32 (general regime)
   void *xa;               // [B][H] act (general regime; == xhat for fp32 activations)
@@ -2344,12 +2352,34 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
   if (tid == 0) {
     const unsigned old =
         __hip_atomic_fetch_add(ctrl_word(p, CTRL_DONE), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.route_claim = old == (unsigned)p->G - 1u;  // this workgroup is the last out
     if (old == (unsigned)p->G - 1u) {
       for (int b = 0; b < kBarPerLayer * p->L; ++b)
         __hip_atomic_store(ctrl_word(p, CTRL_BAR + b), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ctrl_word(p, CTRL_DONE), 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      if (!p->self_reset)
+        __hip_atomic_store(ctrl_word(p, CTRL_DONE), 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  if (p->self_reset) {
+    // The static workspace has no moe_check_workspace: after a watchdog stop
+    // (already visible as NaN outputs) the last workgroup out clears the
+    // error word and the small-batch logit buffers itself.
+    __syncthreads();
+    if (sh.route_claim) {
+      if (err_word(p) != 0) {
+        for (int i = tid; i < 2 * kSmallB * p->E; i += kThreads) publish(p->rlog + i, 0.f);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(ctrl_word(p, CTRL_ERR), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (tid == 0) __hip_atomic_store(ctrl_word(p, CTRL_DONE), 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// zero n words (the control words and logit buffers of a fresh workspace)
+__global__ void __launch_bounds__(256) zero_words(unsigned *w, unsigned n) {
+  for (unsigned i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) w[i] = 0u;
 }
 
 
@@ -2671,6 +2701,7 @@ struct DevInfo {
 
 DevInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once set up
 
 // every in-kernel wait gives up after this many ticks of the 100 MHz realtime counter
 constexpr long long kDefaultWatchdogTicks = 200000000LL;  // 2 s
@@ -2837,8 +2868,31 @@ moe_status check_weights(const moe_layer_desc *d, const moe_layer_weights *w) {
 
 size_t align16(size_t v) { return (v + 15u) & ~(size_t)15u; }
 
+// The device address of this device's copy of `scratch`; on the first call
+// on a device (with it current) the symbol's address is looked up and a fill
+// kernel on `stream` zeroes its control words and logit buffers.
+moe_status static_workspace(int dev, void *stream, void *&ws) {
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(MOE_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    const unsigned words = (unsigned)((kRlogOffset + kRlogBytes) / sizeof(unsigned));
+    hipLaunchKernelGGL(zero_words, dim3((words + 255u) / 256u), dim3(256), 0, (hipStream_t)stream, (unsigned *)ptr,
+                       words);
+    const hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return fail(MOE_ERR_DEVICE, "clearing the static workspace failed: %s", hipGetErrorString(e2));
+    g_scratch_ptr[dev] = ptr;
+  }
+  ws = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// static_ws: the workspace is the library's `scratch` (ws must be NULL)
 moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int L, const void *x, void *y, int B,
-                  int32_t *idx, float *wts, float *logits, void *ws, size_t ws_bytes, void *stream, bool route_only) {
+                  int32_t *idx, float *wts, float *logits, void *ws, size_t ws_bytes, void *stream, bool route_only,
+                  bool static_ws = false) {
   moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
   if (B < 1 || B > kMaxB) return fail(MOE_ERR_UNSUPPORTED, "batch %d outside 1..64", B);
@@ -2846,7 +2900,8 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   if (!layers) return fail(MOE_ERR_INVALID_ARGUMENT, "weights is NULL");
   for (int l = 0; l < L; ++l)
     if ((st = check_weights(d, &layers[l])) != MOE_OK) return st;
-  if (!x || !ws || (!route_only && !y)) return fail(MOE_ERR_INVALID_ARGUMENT, "x, y or workspace is NULL");
+  if (!x || (!static_ws && !ws) || (!route_only && !y))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "x, y or workspace is NULL");
   if (route_only && (!idx || !wts)) return fail(MOE_ERR_INVALID_ARGUMENT, "topk_idx or topk_w is NULL");
   const void *ptrs[] = {x, y, idx, wts, logits, ws};
   for (const void *q : ptrs)
@@ -2854,13 +2909,23 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   const size_t xbytes = (size_t)B * d->hidden * dsize(d->act);
   if (y && y != x && overlap(x, xbytes, y, xbytes)) return fail(MOE_ERR_INVALID_ARGUMENT, "x and y partially overlap");
   const WsLayout wl = ws_layout(d, B, L);
-  if (ws_bytes < wl.total)
-    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes, wl.total);
-  if (overlap(ws, wl.total, x, xbytes) || (y && overlap(ws, wl.total, y, xbytes)))
-    return fail(MOE_ERR_INVALID_ARGUMENT, "workspace overlaps x or y");
+  if (static_ws) {
+    if (wl.total > kScratchBytes)
+      return fail(MOE_ERR_UNSUPPORTED, "this shape and batch need %zu bytes of workspace; the static workspace holds %zu",
+                  wl.total, kScratchBytes);
+  } else {
+    if (ws_bytes < wl.total)
+      return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes, wl.total);
+    if (overlap(ws, wl.total, x, xbytes) || (y && overlap(ws, wl.total, y, xbytes)))
+      return fail(MOE_ERR_INVALID_ARGUMENT, "workspace overlaps x or y");
+  }
 
   int dev = 0, cus = 0, max_lds = 0;
   if ((st = current_device(dev)) != MOE_OK || (st = device_info(dev, cus, max_lds)) != MOE_OK) return st;
+  if (static_ws) {
+    if ((st = static_workspace(dev, stream, ws)) != MOE_OK) return st;
+    ws_bytes = kScratchBytes;
+  }
   Params p;
   memset(&p, 0, sizeof p);
   p.H = d->hidden; p.E = d->num_experts; p.k = d->top_k; p.I = d->expert_inter; p.Is = d->shared_inter;
@@ -2870,6 +2935,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   if (p.G < 1) return fail(MOE_ERR_DEVICE, "device reports no compute units");
   p.perm_a = 1;
   p.perm_c = 0;
+  p.self_reset = static_ws ? 1 : 0;
 #ifdef MOE_DEBUG_DELAY
   {
     const int grid = g_dbg_grid.load(std::memory_order_relaxed);
@@ -3153,6 +3219,11 @@ moe_status moe_route(const moe_layer_desc *desc, const moe_layer_weights *weight
 moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *weights, const void *x, void *y,
                             int32_t B, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
   return launch(desc, weights, 1, x, y, B, topk_idx, topk_w, nullptr, ws, ws_bytes, stream, false);
+}
+
+moe_status moe_decode_layer_static(const moe_layer_desc *desc, const moe_layer_weights *weights, const void *x,
+                                   void *y, int32_t B, int32_t *topk_idx, float *topk_w, void *stream) {
+  return launch(desc, weights, 1, x, y, B, topk_idx, topk_w, nullptr, nullptr, 0, stream, false, true);
 }
 
 moe_status moe_decode_stack(const moe_layer_desc *desc, const moe_layer_weights *layers, int32_t L, const void *x,
