@@ -95,7 +95,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxL = 8;
 constexpr int kTokGroup = 4;    // tokens whose partial sums a lane holds at once
 constexpr int kRowBlock = 4;    // down-projection rows per unit
-constexpr int kSmallB = 2;      // B <= kSmallB: the small regime (x-hat in every workgroup's LDS)
+constexpr int kSmallB = 4;      // B <= kSmallB (and B * k <= 64): the small regime (x-hat in every workgroup's LDS)
 constexpr int kMaxRounds = 32;  // rounds of P0 slices over the grid's waves
 
 // expert barriers of the small regime: P1's rounds fall into up to kP1Groups
@@ -168,9 +168,13 @@ struct Params {
   int o_cnt, o_start, o_tmask;      // per-expert scratch of the workgroup-wide table build [E]
   int o_mslot, o_gslot;             // general regime: union slots on MFMA tiles / on GEMV [min(E, B*k)]
   int o_cpre;                       // general regime: P1 cost before each listed slot [min(E, B*k) + 1]
-  int o_xf, o_xa;                   // small regime: x-hat fp32 / act [B][H]
+  int o_xf, o_xa;                   // small regime: x-hat fp32 [B][H] (fp32 activations) / act [B][H]
+  int o_x, o_g;                     // small regime, bf16 activations: x [B][H] and gamma [H] as given
+  int rx32;                         // small regime: the router's fp32 x-hat [B][H] is in LDS (o_xf); else formed from o_x, o_g
+  int o_cand;                       // top-k candidates, then the ranked k: [slots][2 * 64] keys, then indices
   int o_hs;                         // small regime: shared h [B][Is] (act)
   int o_slc;                        // slice sums of P0 tasks [round][wave][slw]
+  int o_scnt;                       // slices of a router row / shared pair done: [2][round][slice group] int
   int o_part;                       // small regime: P2 partial sums [rows_per_wg][pstride] fp32
   int o_red;                        // shared MFMA tiles: partial tiles of the waves [kWaves][16][B] fp32
   LayerPtrs lp[kMaxL];
@@ -182,16 +186,13 @@ struct SmemHead {
   int bar_claim[kMaxBarriers];  // one wave polls the global counter
   int bar_flag[kMaxBarriers];   // raised once the barrier is passed
   float red[kWaves * kSmallB];
+  float rstd[kSmallB];             // small regime, bf16 activations: 1 / sqrt(mean(x^2) + eps) of each token
   int scan_tmp[2 * kWaves];
   int nU;
   int route_claim, route_ready;    // small regime: the first free wave does the routing
   int shared_claim, shared_ready;  // small regime: ... and the shared expert's h
   int unit_ctr[2 + kP1Groups];     // P2 units handed out to waves (shared, experts / expert group)
-  int rcnt[kMaxRounds][kWaves];    // slices of a router row / shared pair done, per round and slice group
-  int scnt[kMaxRounds][kWaves];
   int nM, nG;                      // general regime: union slots on MFMA tiles, on GEMV
-  unsigned cand_key[kWaves][2 * 64];  // top-k candidates of each wave (ordered logit bits), then the ranked k
-  int cand_idx[kWaves][2 * 64];
   unsigned sink;
   int expired;                     // a wait of this workgroup gave up at its watchdog during this launch
 };
@@ -339,16 +340,37 @@ __device__ __forceinline__ float late_scale(uint32_t raw) {
 // weight chunk: streamed once, so loaded non-temporal
 __device__ __forceinline__ u32x4 ldw(const char *p) { return __builtin_nontemporal_load((const u32x4 *)p); }
 
-// activation chunk, from global memory (XL = false) or LDS (XL = true)
-template <bool XL> struct XSrc;
-template <> struct XSrc<false> {
+// activation chunk, from global memory (XS = 0), LDS (XS = 1), or, for the
+// router in the small regime with bf16 activations, the fp32 x-hat formed
+// from the token's bf16 x, bf16 gamma (both in LDS) and its fp32 r (XS = 2)
+template <int XS> struct XSrc;
+template <> struct XSrc<0> {
   typedef const char *ptr;
   __device__ static __forceinline__ u32x4 ld(ptr p, size_t off) { return *(const u32x4 *)(p + off); }
 };
-template <> struct XSrc<true> {
+template <> struct XSrc<1> {
   typedef const lds_t *ptr;
   __device__ static __forceinline__ u32x4 ld(ptr p, size_t off) {
     return *(const __attribute__((address_space(3))) u32x4 *)(p + off);
+  }
+};
+template <> struct XSrc<2> {
+  struct ptr {
+    const lds_t *x, *g;  // the token's row of x, and gamma, bf16
+    float r;
+  };
+  // off: byte offset into an fp32 row; 4 elements, each (x * r) * gamma as
+  // the normalisation computes it, so the router sees the same bits
+  __device__ static __forceinline__ u32x4 ld(const ptr &p, size_t off) {
+    const size_t b = off >> 1;
+    const u32x2 xv = *(const __attribute__((address_space(3))) u32x2 *)(p.x + b);
+    const u32x2 gv = *(const __attribute__((address_space(3))) u32x2 *)(p.g + b);
+    u32x4 v;
+    v.x = __float_as_uint(__uint_as_float(xv.x << 16) * p.r * __uint_as_float(gv.x << 16));
+    v.y = __float_as_uint(__uint_as_float(xv.x & 0xFFFF0000u) * p.r * __uint_as_float(gv.x & 0xFFFF0000u));
+    v.z = __float_as_uint(__uint_as_float(xv.y << 16) * p.r * __uint_as_float(gv.y << 16));
+    v.w = __float_as_uint(__uint_as_float(xv.y & 0xFFFF0000u) * p.r * __uint_as_float(gv.y & 0xFFFF0000u));
+    return v;
   }
 };
 
@@ -457,7 +479,7 @@ __device__ __forceinline__ void wave_argmax(float &v, int &i) {
 // the remainder runs chunk by chunk with one. Rows are 16-byte aligned and
 // k0, k1 multiples of EPL. acc[r][t] receives lane partial sums.
 
-template <int WD, int XD, bool XL, int NR, int SEG, int TG>
+template <int WD, int XD, int XL, int NR, int SEG, int TG>
 __device__ __forceinline__ void rows_dot(const char *const (&wrow)[NR], int k0, int k1,
                                          const typename XSrc<XL>::ptr (&xr)[TG], float (&acc)[NR][TG]) {
   constexpr int EPL = epl<WD>(), NX = Chunk<WD, XD>::NX, CH = 64 * EPL;
@@ -682,8 +704,10 @@ __device__ __forceinline__ void act_chunk_vals(const u32x4 &v, float (&f)[8]) {
 }
 
 // RMSNorm of NT tokens (rows x_t of `x`, t = tok[i]) by the whole workgroup:
-// every load is issued before the first use (one round trip); out(t, h, v)
-// receives x-hat. Chunk c of a row is handled by thread c mod 1024.
+// every load is issued before the first use (one round trip). Chunk c of a
+// row is handled by thread c mod 1024; out(i, ch, xv, gv, r) receives token
+// i's chunk ch of x and gamma (16 bytes each) and the token's
+// r = 1 / sqrt(mean(x^2) + eps); x-hat is (x * r) * gamma, elementwise.
 template <int AD, int NT, class Out>
 __device__ __forceinline__ void rmsnorm_rows(KParams p, KLayer lp, SmemHead &sh, const int (&tok)[NT], Out &&out) {
   constexpr int EPC = 16 / dsz<AD>(), NC = act_chunks_max<AD>();
@@ -722,38 +746,124 @@ __device__ __forceinline__ void rmsnorm_rows(KParams p, KLayer lp, SmemHead &sh,
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int ch = tid + c * kThreads;
-      if (ch < nch) {
-        float f[8], g[8];
-        act_chunk_vals<AD>(xv[i][c], f);
-        act_chunk_vals<AD>(gv[c], g);
+      if (ch < nch) out(i, ch, xv[i][c], gv[c], r);
+    }
+  }
+  __syncthreads();
+}
+
+// x-hat values of one chunk: (x * r) * gamma
+template <int AD>
+__device__ __forceinline__ void xhat_chunk(const u32x4 &xv, const u32x4 &gv, float r, float (&v)[8]) {
+  float f[8], g[8];
+  act_chunk_vals<AD>(xv, f);
+  act_chunk_vals<AD>(gv, g);
 #pragma unroll
-        for (int q = 0; q < EPC; ++q) out(i, ch * EPC + q, f[q] * r * g[q]);
+  for (int q = 0; q < 16 / dsz<AD>(); ++q) v[q] = f[q] * r * g[q];
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Small regime: this workgroup normalises every token into its own LDS. fp32
+// activations: x-hat [B][H] (the router's and the FFNs' input). bf16: the
+// FFNs' x-hat [B][H] in bf16, and either the router's fp32 x-hat [B][H]
+// (rx32) or x [B][H] and gamma [H] as given with each token's r, from which
+// the router forms its fp32 input (XSrc<2>). All loads are issued first; each
+// raw x chunk goes straight to its x-hat slot in LDS, so no chunk stays in a
+// register across the workgroup barrier, and after it each thread reads its
+// own chunks back and normalises them in place.
+template <int AD, int NT>
+__device__ __forceinline__ void stage_tokens(KParams p, KLayer lp, const Lds &L) {
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  constexpr int EPC = 16 / dsz<AD>(), NC = act_chunks_max<AD>();
+  constexpr int XSL = AD == DT_F32 ? 4 : 2;  // bytes per element of the x-hat slot
+  SmemHead &sh = L.head();
+  const int H = p->H, tid = threadIdx.x, nch = H / EPC;
+  lds_t *slot = L.raw(AD == DT_F32 ? p->o_xf : p->o_xa);
+  u32x4 xv[NT][NC], gv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = tid + c * kThreads;
+    const int cc = ch < nch ? ch : 0;
+    gv[c] = *(const u32x4 *)((const char *)lp->gamma + (size_t)cc * 16);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) xv[i][c] = *(const u32x4 *)((const char *)lp->x + ((size_t)i * nch + cc) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int ch = tid + c * kThreads;
+      if (ch < nch) {
+        float f[8];
+        act_chunk_vals<AD>(xv[i][c], f);
+#pragma unroll
+        for (int q = 0; q < EPC; ++q) ss = fmaf(f[q], f[q], ss);
+        *(lds_u32x4 *)(slot + ((size_t)i * H + (size_t)ch * EPC) * XSL) = xv[i][c];
+      }
+    }
+    ss = readlane_f(wave_sum63(ss), 63);
+    if (lane_id() == 0) sh.red[i * kWaves + wave_id()] = ss;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    float tot = 0.f;
+    for (int w2 = 0; w2 < kWaves; ++w2) tot += sh.red[i * kWaves + w2];
+    const float r = 1.0f / sqrtf(tot / (float)H + p->eps);
+    if constexpr (AD != DT_F32)
+      if (tid == 0 && !p->rx32) sh.rstd[i] = r;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int ch = tid + c * kThreads;
+      if (ch >= nch) continue;
+      lds_u32x4 *sl = (lds_u32x4 *)(slot + ((size_t)i * H + (size_t)ch * EPC) * XSL);
+      const u32x4 x = *sl;
+      float v[8];
+      xhat_chunk<AD>(x, gv[c], r, v);
+      if constexpr (AD == DT_F32) {
+        *sl = u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+      } else {
+        *sl = u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
+        const size_t off = ((size_t)i * H + (size_t)ch * 8) * 2;
+        if (p->rx32) {
+          lds_u32x4 *xf = (lds_u32x4 *)(L.raw(p->o_xf) + off * 2);
+          xf[0] = u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+          xf[1] = u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])};
+        } else {
+          *(lds_u32x4 *)(L.raw(p->o_x) + off) = x;
+          if (i == 0) *(lds_u32x4 *)(L.raw(p->o_g) + (size_t)ch * 16) = gv[c];
+        }
       }
     }
   }
   __syncthreads();
 }
 
-// Small regime: this workgroup normalises every token into its own LDS:
-// xf [B][H] fp32 (router input) and xa [B][H] act (FFN input).
+// One or two tokens, and three or four, in separate non-inlined functions:
+// the register footprint of the larger batches would otherwise make every
+// call save and restore callee-saved registers through scratch memory.
 template <int AD>
-__device__ __attribute__((noinline)) void stage_xhat(KParams p_arg, KLayer lp_arg, const Lds &L) {
+__device__ __attribute__((noinline)) void stage_xhat12(KParams p_arg, KLayer lp_arg, const Lds &L) {
   const KParams p = uni(p_arg);
   const KLayer lp = uni(lp_arg);
-  const int H = p->H;
-  float *xf = L.at<float>(p->o_xf);
-  lds_t *xa = L.raw(p->o_xa);
-  auto put = [&](int t, int h, float v) {
-    xf[(size_t)t * H + h] = v;
-    if constexpr (AD != DT_F32) store_act_lds<AD>(xa, (size_t)t * H + h, v);
-  };
-  if (p->B == 1) {
-    const int tok[1] = {0};
-    rmsnorm_rows<AD, 1>(p, lp, L.head(), tok, put);
-  } else {
-    const int tok[2] = {0, 1};
-    rmsnorm_rows<AD, 2>(p, lp, L.head(), tok, put);
-  }
+  if (p->B == 1) stage_tokens<AD, 1>(p, lp, L);
+  else stage_tokens<AD, 2>(p, lp, L);
+}
+template <int AD>
+__device__ __attribute__((noinline)) void stage_xhat34(KParams p_arg, KLayer lp_arg, const Lds &L) {
+  const KParams p = uni(p_arg);
+  const KLayer lp = uni(lp_arg);
+  if (p->B == 3) stage_tokens<AD, 3>(p, lp, L);
+  else stage_tokens<AD, 4>(p, lp, L);
+}
+template <int AD>
+__device__ __forceinline__ void stage_xhat(KParams p, KLayer lp, const Lds &L) {
+  if (p->B <= 2) stage_xhat12<AD>(p, lp, L);
+  else stage_xhat34<AD>(p, lp, L);
 }
 
 // General regime: workgroup t normalises token t into global memory.
@@ -762,26 +872,46 @@ __device__ __attribute__((noinline)) void produce_xhat(KParams p_arg, KLayer lp_
   const KParams p = uni(p_arg);
   const KLayer lp = uni(lp_arg);
   const int H = p->H;
+  constexpr int EPC = 16 / dsz<AD>();
   for (int t = wg_id(p); t < p->B; t += p->G) {
     const int tok[1] = {t};
-    rmsnorm_rows<AD, 1>(p, lp, L.head(), tok, [&](int, int h, float v) {
-      p->xhat[(size_t)t * H + h] = v;
-      if constexpr (AD != DT_F32) store_act<AD>(p->xa, (size_t)t * H + h, v);
+    rmsnorm_rows<AD, 1>(p, lp, L.head(), tok, [&](int, int ch, const u32x4 &xv, const u32x4 &gv, float r) {
+      float v[8];
+      xhat_chunk<AD>(xv, gv, r, v);
+#pragma unroll
+      for (int q = 0; q < EPC; ++q) {
+        const size_t h = (size_t)ch * EPC + q;
+        p->xhat[(size_t)t * H + h] = v[q];
+        if constexpr (AD != DT_F32) store_act<AD>(p->xa, (size_t)t * H + h, v[q]);
+      }
     });
   }
 }
 
-// pointer to token t's row of x-hat (fp32 if F32X, else act) in LDS or global memory
-template <bool XL, int AD, bool F32X>
+// pointer to token t's row of the FFNs' x-hat (act dtype) in LDS or global memory
+template <bool XL, int AD>
 __device__ __forceinline__ typename XSrc<XL>::ptr xhat_row(KParams p, const Lds &L, int t) {
-  constexpr int XB = F32X ? 4 : dsz<AD>();
+  constexpr int XB = dsz<AD>();
   if constexpr (XL) {
-    const int off = (F32X || AD == DT_F32) ? p->o_xf : p->o_xa;
+    const int off = AD == DT_F32 ? p->o_xf : p->o_xa;
     return L.raw(off) + (size_t)t * p->H * XB;
   } else {
-    const char *base = (F32X || AD == DT_F32) ? (const char *)p->xhat : (const char *)p->xa;
+    const char *base = AD == DT_F32 ? (const char *)p->xhat : (const char *)p->xa;
     return base + (size_t)t * p->H * XB;
   }
+}
+
+// the router's fp32 input: global x-hat (general regime), LDS x-hat (small
+// regime, fp32 activations), or formed from LDS x, gamma and r (small regime,
+// bf16 activations)
+template <bool XL, int AD> constexpr int router_src() { return !XL ? 0 : AD == DT_F32 ? 1 : 2; }
+
+template <bool XL, int AD>
+__device__ __forceinline__ typename XSrc<router_src<XL, AD>()>::ptr router_row(KParams p, const Lds &L, int t) {
+  constexpr int XS = router_src<XL, AD>();
+  if constexpr (XS == 0) return (const char *)p->xhat + (size_t)t * p->H * 4;
+  else if constexpr (XS == 1) return L.raw(p->o_xf) + (size_t)t * p->H * 4;
+  else return typename XSrc<2>::ptr{L.raw(p->o_x) + (size_t)t * p->H * 2, L.raw(p->o_g), L.head().rstd[t]};
 }
 
 // ---------------------------------------------------------------------------
@@ -798,32 +928,50 @@ __device__ __forceinline__ float *slice_slot(KParams p, const Lds &L, int round,
   return L.at<float>(p->o_slc) + ((size_t)round * kWaves + wave) * p->slw;
 }
 
-__device__ __forceinline__ bool last_slice(int (&cnt)[kMaxRounds][kWaves], int round, int NS) {
+// which = 0: router rows, 1: shared pairs
+__device__ __forceinline__ bool last_slice(KParams p, const Lds &L, int which, int round, int NS) {
   if (NS == 1) return true;
+  int *cnt = L.at<int>(p->o_scnt) + ((size_t)which * p->p0r + round) * kWaves;
   int old = 0;
   if (lane_id() == 0)
-    old = __hip_atomic_fetch_add(&cnt[round][wave_id() / NS], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __hip_atomic_fetch_add(&cnt[wave_id() / NS], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
   return __builtin_amdgcn_readfirstlane(old) == NS - 1;
 }
 
 // router task tau = (row e, slice s) of round `round`: slice sums of all
 // tokens to this wave's LDS slot; the last slice's wave writes the logit rfin[t][e]
 // (published in the small regime)
-template <int RD, bool XL>
+template <int AD, int RD, bool XL>
+__device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, int tau, int round);
+
+// small regime, bf16 activations: the router reads the fp32 x-hat from LDS
+// where it fits (XS = 1), else forms it from x, gamma and r (XS = 2)
+template <int AD, int RD, bool XL>
+__device__ __forceinline__ void router_task_any(KParams p, KLayer lp, const Lds &L, int tau, int round) {
+  if constexpr (router_src<XL, AD>() == 2) {
+    if (p->rx32) router_task<DT_F32, RD, XL>(p, lp, L, tau, round);
+    else router_task<AD, RD, XL>(p, lp, L, tau, round);
+  } else {
+    router_task<AD, RD, XL>(p, lp, L, tau, round);
+  }
+}
+
+template <int AD, int RD, bool XL>
 __device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, int tau, int round) {
+  constexpr int XS = router_src<XL, AD>();
   const int H = p->H, E = p->E, B = p->B, NSR = p->NSR;
   const int e = tau / NSR, s = tau % NSR;
   const int Ks = H / NSR;
   const char *const wrow[1] = {(const char *)lp->rw + (size_t)e * H * dsz<RD>()};
   const float bias = lp->rb ? lp->rb[e] : 0.f;  // added to the finished fp32 dot product
   for_token_groups(B, [&]<int TG>(int t0, int nt) {
-    typename XSrc<XL>::ptr xr[TG];
+    typename XSrc<XS>::ptr xr[TG];
 #pragma unroll
-    for (int t = 0; t < TG; ++t) xr[t] = xhat_row<XL, DT_F32, true>(p, L, t0 + (t < nt ? t : 0));
+    for (int t = 0; t < TG; ++t) xr[t] = router_row<XL, AD>(p, L, t0 + (t < nt ? t : 0));
     float acc[1][TG];
 #pragma unroll
     for (int t = 0; t < TG; ++t) acc[0][t] = 0.f;
-    rows_dot<RD, DT_F32, XL, 1, seg_router<RD, TG>(), TG>(wrow, s * Ks, (s + 1) * Ks, xr, acc);
+    rows_dot<RD, DT_F32, XS, 1, seg_router<RD, TG>(), TG>(wrow, s * Ks, (s + 1) * Ks, xr, acc);
 #pragma unroll
     for (int t = 0; t < TG; ++t) {
       const float v = wave_sum63(acc[0][t]);
@@ -838,7 +986,7 @@ __device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, 
       }
     }
   });
-  if (NSR > 1 && last_slice(L.head().rcnt, round, NSR)) {
+  if (NSR > 1 && last_slice(p, L, 0, round, NSR)) {
     dbg_delay(p, DLY_PUBLISH, e);
     const int w0 = wave_id() - s;
     for (int t = lane_id(); t < B; t += 64) {
@@ -871,7 +1019,7 @@ __device__ __forceinline__ void shared_gu_task(KParams p, KLayer lp, const Lds &
   for_token_groups(B, [&]<int TG>(int t0, int nt) {
     typename XSrc<XL>::ptr xr[TG];
 #pragma unroll
-    for (int t = 0; t < TG; ++t) xr[t] = xhat_row<XL, AD, false>(p, L, t0 + (t < nt ? t : 0));
+    for (int t = 0; t < TG; ++t) xr[t] = xhat_row<XL, AD>(p, L, t0 + (t < nt ? t : 0));
     float acc[2][TG];
 #pragma unroll
     for (int t = 0; t < TG; ++t) acc[0][t] = acc[1][t] = 0.f;
@@ -891,7 +1039,7 @@ __device__ __forceinline__ void shared_gu_task(KParams p, KLayer lp, const Lds &
       }
     }
   });
-  if (NSS > 1 && last_slice(L.head().scnt, round, NSS)) {
+  if (NSS > 1 && last_slice(p, L, 1, round, NSS)) {
     const int w0 = wave_id() - s;
     for (int t = lane_id(); t < B; t += 64) {
       float g = slice_slot(p, L, round, w0)[2 * t], u = slice_slot(p, L, round, w0)[2 * t + 1];
@@ -1068,8 +1216,9 @@ __device__ __attribute__((noinline)) void topk_token(KParams p_arg, KLayer lp_ar
   int myidx = 0;
   float myv = -INFINITY;
   if (total <= kMaxCand) {
-    unsigned *ck = L.head().cand_key[wave_id()];
-    int *ci = L.head().cand_idx[wave_id()];
+    // the small regime's routing wave may be any wave: slot 0 (the only one there)
+    unsigned *ck = L.at<unsigned>(p->o_cand) + (POLL ? 0 : wave_id()) * 4 * kMaxCand;
+    int *ci = (int *)ck + 2 * kMaxCand;
     int pos = pre;
 #pragma unroll
     for (int j = 0; j < PER; ++j)
@@ -1183,7 +1332,7 @@ __device__ __attribute__((noinline)) void build_tables_wave(KParams p_arg, const
   const int *sel_idx = L.at<int>(p->o_sel_idx);
   int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   int *plist = L.at<int>(p->o_plist);
-  unsigned *sorted = L.head().cand_key[wave_id()];
+  unsigned *sorted = L.at<unsigned>(p->o_cand);  // slot 0: the small regime's routing wave
   const bool valid = lane < P;
   const unsigned key = valid ? ((unsigned)sel_idx[lane] << 6) | (unsigned)lane : 0xFFFFFFFFu;
   int rank = 0;
@@ -1235,7 +1384,7 @@ __device__ __forceinline__ void expert_gu_task(KParams p, KLayer lp, const Lds &
 #pragma unroll
     for (int t = 0; t < TG; ++t) {
       slot[t] = pl[t0 + (t < nt ? t : 0)];
-      xr[t] = xhat_row<XL, AD, false>(p, L, slot[t] / k);
+      xr[t] = xhat_row<XL, AD>(p, L, slot[t] / k);
     }
     float acc[2][TG];
 #pragma unroll
@@ -2063,7 +2212,7 @@ __device__ __forceinline__ void p0_tasks(KParams p, KLayer lp, const Lds &L, int
       if constexpr (!PUB) bar_arrive(p, sh, b0 + BAR_ROUTER);
       routed = true;
     }
-    if (tau < nrt) router_task<RD, PUB>(p, lp, L, tau, r);
+    if (tau < nrt) router_task_any<AD, RD, PUB>(p, lp, L, tau, r);
     else if (!MSH && tau >= s0) shared_gu_task<AD, SD, PUB>(p, lp, L, tau - s0, r);
   }
   if constexpr (PUB) {
@@ -2233,7 +2382,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
   for (int l = 0; l < p->L; ++l) {
     KLayer lp = &p->lp[l];
     const int b0 = kBarPerLayer * l;
-    for (int i = tid; i < kMaxRounds * kWaves; i += kThreads) (&sh.rcnt[0][0])[i] = (&sh.scnt[0][0])[i] = 0;
+    for (int i = tid; i < 2 * p->p0r * kWaves; i += kThreads) L.at<int>(p->o_scnt)[i] = 0;
     if (tid == 0) {
       sh.route_claim = sh.route_ready = sh.shared_claim = sh.shared_ready = 0;
       for (int i = 0; i < 2 + kP1Groups; ++i) sh.unit_ctr[i] = 0;
@@ -2248,7 +2397,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
         bar_arrive(p, sh, b0 + BAR_XHAT);
         bar_wait(p, sh, b0 + BAR_XHAT);
       }
-      for (int tau = W, r = 0; tau < p->E * p->NSR; tau += NW, ++r) router_task<RD, SMALL>(p, lp, L, tau, r);
+      for (int tau = W, r = 0; tau < p->E * p->NSR; tau += NW, ++r) router_task_any<AD, RD, SMALL>(p, lp, L, tau, r);
       if constexpr (SMALL) bar_arrive_published(p, sh, b0 + BAR_ROUTER);
       else bar_arrive(p, sh, b0 + BAR_ROUTER);
       bar_wait(p, sh, b0 + BAR_ROUTER);
@@ -2951,9 +3100,11 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     }
   }
 #endif
-  // the regime: B <= kSmallB keeps x-hat in every workgroup's LDS when it
+  // the regime: B <= kSmallB with B * k <= 64 (one wave routes the batch and
+  // builds the gather tables) keeps x-hat in every workgroup's LDS when it
   // fits; otherwise (or for larger B) the general regime
-  bool small = small_regime(B);
+  bool small = small_regime(B) && B * d->top_k <= 64;
+  p.rx32 = d->act == MOE_BF16 ? 1 : 0;  // first try: the router's fp32 x-hat in LDS (bf16 activations)
   size_t lds = 0;
   const size_t lds_cap = (size_t)(max_lds > 0 ? max_lds : 65536);
   for (;;) {
@@ -3010,10 +3161,20 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     p.o_ucnt = (int)o; o = align16(o + (size_t)nslot * 4);
     p.o_ustart = (int)o; o = align16(o + (size_t)nslot * 4);
     p.o_plist = (int)o; o = align16(o + (size_t)P * 4);
+    // top-k candidate slots of 1 KB: one per routing wave
+    // (small regime: the one routing wave; its route-only launch: one wave per token)
+    p.o_cand = (int)o; o = align16(o + (size_t)(small ? (route_only ? B : 1) : kWaves) * 4 * 64 * sizeof(unsigned));
     if (small) {
-      if (P > 64) return fail(MOE_ERR_UNSUPPORTED, "small-batch routing needs batch*top_k <= 64");
-      p.o_xf = (int)o; o = align16(o + (size_t)B * H * 4);
-      p.o_xa = (int)o; o = align16(o + (d->act == MOE_F32 ? 0 : (size_t)B * H * act));
+      if (d->act == MOE_F32) {
+        p.o_xf = (int)o; o = align16(o + (size_t)B * H * 4);
+      } else if (p.rx32) {
+        p.o_xf = (int)o; o = align16(o + (size_t)B * H * 4);
+        p.o_xa = (int)o; o = align16(o + (size_t)B * H * act);
+      } else {
+        p.o_x = (int)o; o = align16(o + (size_t)B * H * act);
+        p.o_xa = (int)o; o = align16(o + (size_t)B * H * act);
+        p.o_g = (int)o; o = align16(o + (size_t)H * act);
+      }
       p.o_hs = (int)o; o = align16(o + (size_t)B * (d->shared_inter > 0 ? d->shared_inter : 1) * act);
     } else {
       p.o_cnt = (int)o; o = align16(o + (size_t)E * 4);
@@ -3025,6 +3186,8 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     }
     p.o_slc = (int)o;
     o = align16(o + (size_t)rounds * kWaves * p.slw * sizeof(float));
+    p.o_scnt = (int)o;
+    o = align16(o + (size_t)2 * p.p0r * kWaves * sizeof(int));
     p.o_red = (int)o;
     if (p.mfma_sh) o = align16(o + (size_t)kWaves * 16 * B * sizeof(float));
     p.o_part = (int)o;
@@ -3035,8 +3198,13 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     p.use_mfma = (!small && d->expert != MOE_F32 && rpw >= 16) ? 1 : 0;
     if (lds <= lds_cap) break;
     if (!small) return fail(MOE_ERR_UNSUPPORTED, "shape needs more LDS than the device's %zu bytes", lds_cap);
-    // x-hat of every token does not fit a workgroup's LDS (from H = 16384 at
-    // B = 2): the general regime keeps it in global memory instead
+    if (p.rx32) {  // the router's fp32 x-hat does not fit: form it from x, gamma and r instead
+      p.rx32 = 0;
+      continue;
+    }
+    // x-hat of every token does not fit a workgroup's LDS (H = 16384 at
+    // B = 2, or the K3 share above B = 4): the general regime keeps it in
+    // global memory instead
     small = false;
   }
 

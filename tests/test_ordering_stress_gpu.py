@@ -88,7 +88,7 @@ def stress(w, layers, x, B, dev):
     return prod
 
 
-@pytest.mark.parametrize("name,B", [("k3_b1", 1), ("k3_b8", 8), ("tiny_f32", 2), ("tiny_f32", 9)])
+@pytest.mark.parametrize("name,B", [("k3_b1", 1), ("k3_b1", 4), ("k3_b8", 8), ("tiny_f32", 2), ("tiny_f32", 9)])
 def test_layer_under_delays(dev, name, B):
     w = synth.WORKLOADS[name]
     Lh = host_layer(w, experts=[])

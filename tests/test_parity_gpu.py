@@ -217,7 +217,7 @@ def test_odd_multiples(dev, expert, router, seed):
     oracle."""
     w = small_workload(name="odd", H=4352, E=24, k=3, I=384, Is=768, act=synth.BF16, router=router,
                        expert=expert, shared=synth.BF16, seed=seed)
-    for B in (1, 2, 9, 40):
+    for B in (1, 2, 3, 4, 9, 40):
         err = full_parity(w, B, dev, poison=True)
         log(f"odd multiples ({expert}) B={B} max rel err {err:.2e}")
 
@@ -231,7 +231,7 @@ def test_widened_envelope(dev, case):
     if case == "h33x128_is_not_multiple_of_i":
         w = small_workload(name="h4224", H=4224, E=24, k=3, I=256, Is=384, act=synth.BF16, router=synth.F32,
                            expert=synth.BF16, shared=synth.BF16, seed=91)
-        batches = (1, 2, 9, 40)
+        batches = (1, 2, 3, 4, 9, 40)
     elif case == "h33x128_fp8":
         w = small_workload(name="h4224f8", H=4224, E=24, k=3, I=256, Is=640, act=synth.BF16, router=synth.BF16,
                            expert=synth.FP8, shared=synth.BF16, seed=92)
@@ -251,6 +251,15 @@ def test_widened_envelope(dev, case):
 def test_k3_b1(dev):
     err = full_parity(synth.WORKLOADS["k3_b1"], 1, dev, poison=True)
     log(f"k3_b1 max rel err {err:.2e}")
+
+
+@pytest.mark.parametrize("B", [2, 3, 4, 5])
+def test_k3_small_batches(dev, B):
+    """The K3 share at B = 2..4 (the small regime: x-hat in every workgroup's
+    LDS, the router's fp32 input formed from bf16 x, gamma and r) and at
+    B = 5 (the general regime), every token vs the oracle."""
+    err = full_parity(synth.WORKLOADS["k3_b1"], B, dev, poison=True)
+    log(f"k3 B={B} max rel err {err:.2e}")
 
 
 def test_k3_b1_all_experts_drawn(dev):
