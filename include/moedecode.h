@@ -150,7 +150,7 @@ moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights 
  * process ends, zeroed by a small fill kernel on `stream` at the first call on
  * each device. Shapes whose moe_workspace_bytes(desc, B, 1) exceeds 16 MiB
  * (at the K3 share, H = 7168, E = 896, k = 16, I = 1024, Is = 2048: batches
- * above 27) return MOE_ERR_UNSUPPORTED before any launch. Every call on one
+ * above 26) return MOE_ERR_UNSUPPORTED before any launch. Every call on one
  * GPU shares the array and finds it as the previous call left it: calls that
  * overlap in time on one GPU (other streams or threads) race and give wrong
  * results, so enqueue them on one stream. A watchdog stop shows in the

@@ -105,8 +105,12 @@ constexpr int kP1Groups = 4;
 enum : int { BAR_XHAT = 0, BAR_ROUTER = 1, BAR_SHARED = 2, BAR_LAYER = 3, BAR_H = 4, kBarPerLayer = 4 + kP1Groups };
 constexpr int kMaxBarriers = kBarPerLayer * kMaxL;
 constexpr int kCtrlStride = 16;  // words: each control word on its own 64-byte line
-enum : int { CTRL_DONE = 0, CTRL_ERR = 1, CTRL_BAR = 2 };
-constexpr size_t kCtrlBytes = (size_t)(CTRL_BAR + kMaxBarriers) * kCtrlStride * sizeof(unsigned);
+// router MFMA tiles (16 experts each) whose K range is split over workgroups:
+// one arrival counter per tile, after the barrier counters
+constexpr int kMaxRTiles = kMaxE / 16;
+constexpr int kMaxRQ = 8;        // most K parts of a router tile
+enum : int { CTRL_DONE = 0, CTRL_ERR = 1, CTRL_BAR = 2, CTRL_RTILE = CTRL_BAR + kMaxBarriers };
+constexpr size_t kCtrlBytes = (size_t)(CTRL_RTILE + kMaxRTiles) * kCtrlStride * sizeof(unsigned);
 // small-regime logit buffers (two layer parities), right after the control words
 constexpr size_t kRlogOffset = (kCtrlBytes + 255u) & ~(size_t)255u;
 constexpr size_t kRlogBytes = (size_t)2 * kSmallB * kMaxE * sizeof(float);
@@ -135,6 +139,7 @@ struct Params {
   int route_only;
   int use_mfma;           // general regime: experts with >= kMfmaMin tokens go through MFMA tiles
   int mfma_sh;            // general regime: the router and the shared expert go through MFMA tiles
+  int rq;                 // K parts of each router MFMA tile, one workgroup each
   int p0_end;             // P0 task indices in [0, p0_end): router slices, then shared slices (VALU)
   int NSR;                // router K-slices
   int NSS;                // shared gate/up K-slices
@@ -160,6 +165,7 @@ struct Params {
   void *hbuf;             // [B*k][I] act
   void *hsbuf;             // [B][Is] act (general regime)
   float *partbuf;          // [pstride][H] P2 partial sums (general regime), column-major
+  float *rpart;            // [rq][B][E] router partial logits of the K parts of the MFMA tiles
   void *xbuf[2];          // [B][H] act, stack intermediates
   // LDS carve-up, byte offsets from the start of dynamic LDS
   int o_sel_idx, o_sel_w;           // routing of each token [B*k]
@@ -537,6 +543,16 @@ template <int WD, int TG> constexpr int seg_gu() { return kLoadsPerStep >= 4 ? k
 // rows of a 4-row down unit handled per pass, and chunks per step
 constexpr int kDownRows = kLoadsPerStep >= 4 ? 4 : kLoadsPerStep >= 2 ? 2 : 1;
 template <int WD, int TG> constexpr int seg_down() { return kLoadsPerStep / kDownRows > 0 ? kLoadsPerStep / kDownRows : 1; }
+// General regime (B > 4): chunks per step of a gate/up pair and of a down
+// pass. Its x-hat rows come from L2, not LDS, so a step waits longer.
+#ifndef MOE_GEN_GU_SEG
+#define MOE_GEN_GU_SEG 1
+#endif
+#ifndef MOE_GEN_DOWN_SEG
+#define MOE_GEN_DOWN_SEG 1
+#endif
+template <int WD, int TG, bool XL> constexpr int seg_gu_r() { return XL ? seg_gu<WD, TG>() : MOE_GEN_GU_SEG; }
+template <int WD, int TG, bool XL> constexpr int seg_down_r() { return XL ? seg_down<WD, TG>() : MOE_GEN_DOWN_SEG; }
 // P0 (router and shared gate/up slices): loads per step
 #ifndef MOE_P0_LOADS_PER_STEP
 #define MOE_P0_LOADS_PER_STEP MOE_LOADS_PER_STEP
@@ -866,7 +882,15 @@ __device__ __forceinline__ void stage_xhat(KParams p, KLayer lp, const Lds &L) {
   else stage_xhat34<AD>(p, lp, L);
 }
 
-// General regime: workgroup t normalises token t into global memory.
+// 16-byte device-coherent store (written through this XCD's L2, visible
+// device-wide once complete), for values published before a barrier that
+// needs no L2 write-back
+__device__ __forceinline__ void publish16(void *q, const u32x4 &v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(q), "v"(v) : "memory");
+}
+
+// General regime: workgroup t normalises token t into global memory, fp32
+// (the router's input) and in the act dtype (the FFNs'), published.
 template <int AD>
 __device__ __attribute__((noinline)) void produce_xhat(KParams p_arg, KLayer lp_arg, const Lds &L) {
   const KParams p = uni(p_arg);
@@ -878,11 +902,12 @@ __device__ __attribute__((noinline)) void produce_xhat(KParams p_arg, KLayer lp_
     rmsnorm_rows<AD, 1>(p, lp, L.head(), tok, [&](int, int ch, const u32x4 &xv, const u32x4 &gv, float r) {
       float v[8];
       xhat_chunk<AD>(xv, gv, r, v);
-#pragma unroll
-      for (int q = 0; q < EPC; ++q) {
-        const size_t h = (size_t)ch * EPC + q;
-        p->xhat[(size_t)t * H + h] = v[q];
-        if constexpr (AD != DT_F32) store_act<AD>(p->xa, (size_t)t * H + h, v[q]);
+      float *xf = p->xhat + (size_t)t * H + (size_t)ch * EPC;
+      publish16(xf, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+      if constexpr (AD != DT_F32) {
+        publish16(xf + 4, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
+        publish16((char *)p->xa + ((size_t)t * H + (size_t)ch * EPC) * 2,
+                  u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])});
       }
     });
   }
@@ -1389,7 +1414,7 @@ __device__ __forceinline__ void expert_gu_task(KParams p, KLayer lp, const Lds &
     float acc[2][TG];
 #pragma unroll
     for (int t = 0; t < TG; ++t) acc[0][t] = acc[1][t] = 0.f;
-    rows_dot<ED, AD, XL, 2, seg_gu<ED, TG>(), TG>(wrow, 0, H, xr, acc);
+    rows_dot<ED, AD, XL, 2, seg_gu_r<ED, TG, XL>(), TG>(wrow, 0, H, xr, acc);
 #pragma unroll
     for (int t = 0; t < TG; ++t) {
       float g = wave_sum63(acc[0][t]), uu = wave_sum63(acc[1][t]);
@@ -1460,7 +1485,7 @@ __device__ __forceinline__ void down_unit(const char *const (&wrow)[kRowBlock], 
 #pragma unroll
       for (int t = 0; t < TG; ++t) acc[r][t] = 0.f;
     }
-    rows_dot<WD, AD, XL, kDownRows, seg_down<WD, TG>(), TG>(wr, 0, K, xr, acc);
+    rows_dot<WD, AD, XL, kDownRows, seg_down_r<WD, TG, XL>(), TG>(wr, 0, K, xr, acc);
 #pragma unroll
     for (int r = 0; r < kDownRows; ++r)
 #pragma unroll
@@ -1738,21 +1763,21 @@ __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &
   });
 }
 
-// P0 on MFMA tiles (general regime from kMfmaSharedMin tokens). Router tile i
-// (16 experts by all tokens over all K columns) goes to workgroup i; the
-// shared gate/up tiles go to the remaining workgroups round-robin, so that a
-// workgroup streams one router tile or up to a few shared tiles. Within a
-// tile the 16 waves split the K columns and sum their partial tiles in LDS in
-// wave order.
+// P0 on MFMA tiles (general regime from kMfmaSharedMin tokens): first a
+// router unit (one K part of a 16-expert tile, for all tokens), then shared
+// gate/up tiles. Within a unit or tile the 16 waves split the K columns and
+// sum their partial tiles in LDS in wave order.
 __device__ __forceinline__ int router_tiles(int E) { return (E + 15) / 16; }
-// first shared tile of workgroup g, and the tile stride
-__device__ __forceinline__ int shared_tile0(KParams p, int g) {
-  const int ntr = router_tiles(p->E);
-  return p->G > ntr ? (g >= ntr ? g - ntr : p->Is / 8) : g;
-}
-__device__ __forceinline__ int shared_tile_step(KParams p) {
-  const int ntr = router_tiles(p->E);
-  return p->G > ntr ? p->G - ntr : p->G;
+// Router units: each 16-expert tile's K range is split into p->rq parts, and
+// unit u = tile * rq + q goes to workgroup u, so the router's bytes spread
+// over nearly every CU (with one CU per whole tile, the router barrier waited
+// for 56 CUs streaming 458 KB each while the rest streamed half of that).
+__device__ __forceinline__ int router_units(KParams p) { return router_tiles(p->E) * p->rq; }
+// first 16-column block of wave w's share of K part q
+__device__ __forceinline__ int router_unit_blk(KParams p, int q, int w) {
+  const int nb = p->H / 16;
+  const int q0 = share_lo(nb, q, p->rq), q1 = share_lo(nb, q + 1, p->rq);
+  return q0 + share_lo(q1 - q0, w, kWaves);
 }
 
 // Router tile: v_mfma_f32_16x16x4_f32 with lane l holding A[l%16][l/16] and
@@ -1760,8 +1785,6 @@ __device__ __forceinline__ int shared_tile_step(KParams p) {
 // block lane l loads columns 4(l/16) .. 4(l/16)+3 of its expert row and of
 // its token row, and MFMA m of the block takes component m: k-slot q then
 // holds column 4q + m on both sides. The logits (with the bias) go to rfin.
-__device__ __forceinline__ int router_tile_blk(int H, int w) { return share_lo(H / 16, w, kWaves); }
-
 __device__ __forceinline__ f32x4 mfma4f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -1782,10 +1805,12 @@ template <int RD>
 __device__ __attribute__((noinline)) void router_mfma(KParams p_arg, KLayer lp_arg, const Lds &L) {
   const KParams p = uni(p_arg);
   const KLayer lp = uni(lp_arg);
-  const int H = p->H, E = p->E, B = p->B, lane = lane_id(), wv = wave_id();
-  const int r = lane & 15, kq = lane >> 4;
-  const int b0 = router_tile_blk(H, wv), b1 = router_tile_blk(H, wv + 1);
-  for (int tile = wg_id(p); tile < router_tiles(E); tile += p->G) {
+  const int H = p->H, E = p->E, B = p->B, lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
+  const int r = lane & 15, kq = lane >> 4, RQ = p->rq;
+  SmemHead &sh = L.head();
+  for (int u = wg_id(p); u < router_units(p); u += p->G) {
+    const int tile = u / RQ, q = u % RQ;
+    const int b0 = router_unit_blk(p, q, wv), b1 = router_unit_blk(p, q, wv + 1);
     const unsigned wo = (unsigned)((size_t)min(16 * tile + r, E - 1) * H * dsz<RD>()) + (unsigned)(kq * 4 * dsz<RD>());
     const char *wb = (const char *)lp->rw;
     const char *xb = (const char *)p->xhat;
@@ -1861,20 +1886,44 @@ __device__ __attribute__((noinline)) void router_mfma(KParams p_arg, KLayer lp_a
       }
     });
     __syncthreads();
-    for (int q = threadIdx.x; q < 16 * B; q += kThreads) {
-      const int i = q / B, t = q % B, e = 16 * tile + i;
+    // this part's sums over the waves (wave order), published
+    float *part = p->rpart + (size_t)q * B * E;
+    for (int idx = tid; idx < 16 * B; idx += kThreads) {
+      const int i = idx / B, t = idx % B, e = 16 * tile + i;
       float sum = 0.f;
       for (int w = 0; w < kWaves; ++w) sum += red[(size_t)(w * 16 + i) * B + t];
-      if (e < E) lp->lg[(size_t)t * E + e] = sum + (lp->rb ? lp->rb[e] : 0.f);
+      if (e < E) publish(part + (size_t)t * E + e, sum);
+    }
+    // the last of the tile's RQ workgroups to arrive sums the parts in part
+    // order (whoever it is, the same sums) and writes the logits with the bias
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned old = __hip_atomic_fetch_add(ctrl_word(p, CTRL_RTILE + tile), 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      sh.route_claim = old == (unsigned)RQ - 1u;
+    }
+    __syncthreads();
+    if (sh.route_claim) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      for (int idx = tid; idx < 16 * B; idx += kThreads) {
+        const int i = idx % 16, t = idx / 16, e = 16 * tile + i;
+        if (e < E) {
+          float sum = 0.f;
+          for (int q2 = 0; q2 < RQ; ++q2) sum += p->rpart[((size_t)q2 * B + t) * E + e];
+          lp->lg[(size_t)t * E + e] = sum + (lp->rb ? lp->rb[e] : 0.f);
+        }
+      }
+      if (tid == 0) __hip_atomic_store(ctrl_word(p, CTRL_RTILE + tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
   }
 }
 
-// Shared expert on MFMA tiles (bf16). Gate/up tile j is one 16-row A
-// operand: gate rows [8j, 8j + 8) over up rows [8j, 8j + 8), so that g and u
-// of one h element land in the same tile; the waves split K in 64-column
-// steps.
+// Shared expert on MFMA tiles (bf16), after the router units. Gate/up tile
+// j is one 16-row A operand: gate rows [8j, 8j + 8) over up rows [8j, 8j + 8),
+// so that g and u of one h element land in the same tile; workgroup g takes
+// tiles g, g + G, ..., and its waves split K in 64-column steps.
 __device__ __forceinline__ int shared_tile_row(int Is, int j, int r) { return r < 8 ? 8 * j + r : Is + 8 * j + r - 8; }
 __device__ __forceinline__ int shared_tile_k(int H, int w) { return share_lo(H / 64, w, kWaves) * 64; }
 
@@ -1887,7 +1936,7 @@ __device__ __attribute__((noinline)) void shared_gu_mfma(KParams p_arg, KLayer l
   const int k0 = shared_tile_k(H, wv), k1 = shared_tile_k(H, wv + 1);
   float *red = L.at<float>(p->o_red);  // [kWaves][16][B]
   const char *xa = (const char *)p->xa + (size_t)k0 * 2;
-  for (int j = shared_tile0(p, wg_id(p)); j < Is / 8; j += shared_tile_step(p)) {
+  for (int j = wg_id(p); j < Is / 8; j += p->G) {
     const char *wb = (const char *)lp->sgu + (size_t)k0 * 2;
     const unsigned wo[1] = {(unsigned)((size_t)shared_tile_row(Is, j, r) * H * 2)};  // < 4 GB
     with_token_tiles(B, [&]<int NT>() {
@@ -1966,8 +2015,17 @@ __device__ __forceinline__ void shared_down_mfma(KParams p, KLayer lp, const Lds
 // P1 cost of a GEMV row pair of an expert with n tokens and of an MFMA tile
 // (16 pairs, ceil(n/16) token tiles), in tenths of a one-token GEMV pair:
 // per-task timings on MI355X at the K3 share (B=64, every wave streaming).
-__device__ __forceinline__ int gemv_pair_cost(int n) { return n <= 1 ? 10 : n == 2 ? 15 : n <= 4 ? 21 : 11 + 4 * n; }
-__device__ __forceinline__ int mfma_tile_cost(int n) { return 190 + 30 * ((n + 15) / 16); }
+#ifndef MOE_COST_G2
+#define MOE_COST_G2 15
+#endif
+#ifndef MOE_COST_M0
+#define MOE_COST_M0 190
+#endif
+#ifndef MOE_COST_M1
+#define MOE_COST_M1 30
+#endif
+__device__ __forceinline__ int gemv_pair_cost(int n) { return n <= 1 ? 10 : n == 2 ? MOE_COST_G2 : n <= 4 ? 21 : 11 + 4 * n; }
+__device__ __forceinline__ int mfma_tile_cost(int n) { return MOE_COST_M0 + MOE_COST_M1 * ((n + 15) / 16); }
 // all of a listed slot's P1 work
 __device__ __forceinline__ int slot_cost(KParams p, bool mfma, int n) {
   return mfma ? (p->I / 16) * mfma_tile_cost(n) : p->I * gemv_pair_cost(n);
@@ -2161,23 +2219,22 @@ __device__ __forceinline__ unsigned prefetch_p0(KParams p, KLayer nl) {
     }
   }
   if (MSH) {
-    // this wave's columns of the workgroup's first router tile
-    if (wg_id(p) < router_tiles(E)) {
-      const int tile = wg_id(p);
-      const int b0 = router_tile_blk(H, wave_id()), b1 = router_tile_blk(H, wave_id() + 1);
+    // this wave's columns of the workgroup's first router unit and shared tile
+    if (wg_id(p) < router_units(p)) {
+      const int tile = wg_id(p) / p->rq, q = wg_id(p) % p->rq;
+      const int b0 = router_unit_blk(p, q, wave_id()), b1 = router_unit_blk(p, q, wave_id() + 1);
       for (int r = 0; r < 16 && 16 * tile + r < E; ++r)
         acc ^= touch_lines((const char *)nl->rw + ((size_t)(16 * tile + r) * H + (size_t)b0 * 16) * dsz<RD>(),
                            (size_t)(b1 - b0) * 16 * dsz<RD>());
     }
-  }
-  if (MSH && shared_tile0(p, wg_id(p)) < Is / 8) {
-    // this wave's columns of the workgroup's first shared MFMA tile
-    const int k0 = shared_tile_k(H, wave_id()), k1 = shared_tile_k(H, wave_id() + 1);
-    const int j = shared_tile0(p, wg_id(p));
-    for (int r = 0; r < 16; ++r)
-      acc ^= touch_lines((const char *)nl->sgu + (size_t)shared_tile_row(Is, j, r) * H * dsz<SD>() +
-                             (size_t)k0 * dsz<SD>(),
-                         (size_t)(k1 - k0) * dsz<SD>());
+    if (wg_id(p) < Is / 8) {
+      const int k0 = shared_tile_k(H, wave_id()), k1 = shared_tile_k(H, wave_id() + 1);
+      const int j = wg_id(p);
+      for (int r = 0; r < 16; ++r)
+        acc ^= touch_lines((const char *)nl->sgu + (size_t)shared_tile_row(Is, j, r) * H * dsz<SD>() +
+                               (size_t)k0 * dsz<SD>(),
+                           (size_t)(k1 - k0) * dsz<SD>());
+    }
   }
   return acc;
 }
@@ -2394,7 +2451,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
         stage_xhat<AD>(p, lp, L);
       } else {
         produce_xhat<AD>(p, lp, L);
-        bar_arrive(p, sh, b0 + BAR_XHAT);
+        bar_arrive_published(p, sh, b0 + BAR_XHAT);
         bar_wait(p, sh, b0 + BAR_XHAT);
       }
       for (int tau = W, r = 0; tau < p->E * p->NSR; tau += NW, ++r) router_task_any<AD, RD, SMALL>(p, lp, L, tau, r);
@@ -2410,9 +2467,9 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
     if constexpr (SMALL) {
       poisoned |= layer_small<AD, RD, ED, SD>(p, lp, L, b0, W, NW);
     } else {
-      // x-hat
+      // x-hat (published: the barrier needs no L2 write-back)
       produce_xhat<AD>(p, lp, L);
-      bar_arrive(p, sh, b0 + BAR_XHAT);
+      bar_arrive_published(p, sh, b0 + BAR_XHAT);
       bar_wait(p, sh, b0 + BAR_XHAT);
 
       // P0: router slices, then shared gate/up
@@ -2505,15 +2562,15 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
     if (old == (unsigned)p->G - 1u) {
       for (int b = 0; b < kBarPerLayer * p->L; ++b)
         __hip_atomic_store(ctrl_word(p, CTRL_BAR + b), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (!p->self_reset)
-        __hip_atomic_store(ctrl_word(p, CTRL_DONE), 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  __syncthreads();
+  if (sh.route_claim && tid == 0 && !p->self_reset)
+    __hip_atomic_store(ctrl_word(p, CTRL_DONE), 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   if (p->self_reset) {
     // The static workspace has no moe_check_workspace: after a watchdog stop
     // (already visible as NaN outputs) the last workgroup out clears the
     // error word and the small-batch logit buffers itself.
-    __syncthreads();
     if (sh.route_claim) {
       if (err_word(p) != 0) {
         for (int i = tid; i < 2 * kSmallB * p->E; i += kThreads) publish(p->rlog + i, 0.f);
@@ -2950,7 +3007,7 @@ bool small_regime(int B) { return B <= kSmallB; }
 int shared_blocks(const moe_layer_desc *d) { return (d->shared_inter + d->expert_inter - 1) / d->expert_inter; }
 
 struct WsLayout {
-  size_t rlog, xhat, xa, rfin, hsh32, hbuf, hsbuf, partbuf, xbuf0, xbuf1, total;
+  size_t rlog, xhat, xa, rfin, hsh32, hbuf, hsbuf, partbuf, rpart, xbuf0, xbuf1, total;
 };
 
 size_t up256(size_t v) { return (v + 255u) & ~(size_t)255u; }
@@ -2969,6 +3026,8 @@ WsLayout ws_layout(const moe_layer_desc *d, int B, int L) {
   w.hsbuf = off; off += up256((size_t)B * is * act);
   const size_t pstride = (size_t)B * d->top_k + (size_t)B * shared_blocks(d);
   w.partbuf = off; off += up256((size_t)d->hidden * pstride * 4);
+  // router partial logits of the MFMA tiles' K parts (batches that use them)
+  w.rpart = off; off += (B >= kMfmaSharedMin) ? up256((size_t)kMaxRQ * B * d->num_experts * 4) : 0;
   w.xbuf0 = off; off += (L > 1) ? up256((size_t)B * d->hidden * act) : 0;
   w.xbuf1 = off; off += (L > 2) ? up256((size_t)B * d->hidden * act) : 0;
   w.total = off;
@@ -3122,6 +3181,11 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
                     ? 1
                     : 0;
     p.NSS = (d->shared_inter > 0 && !p.mfma_sh) ? k_slices(d->hidden, d->shared, 2) : 1;
+    // K parts per router MFMA tile: as many as the grid holds one unit each (at most kMaxRQ)
+    {
+      const int ntr = (d->num_experts + 15) / 16;
+      p.rq = p.mfma_sh ? std::max(1, std::min(kMaxRQ, p.G / ntr)) : 1;
+    }
     // the slices of a row are one workgroup's waves of one round: the shared
     // tasks start at a multiple of the workgroup's wave count, and the rounds
     // must fit the per-round slice counters and LDS slots (else every row is
@@ -3219,6 +3283,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
   p.hbuf = wsb + wl.hbuf;
   p.hsbuf = wsb + wl.hsbuf;
   p.partbuf = (float *)(wsb + wl.partbuf);
+  p.rpart = (float *)(wsb + wl.rpart);
   p.xbuf[0] = wsb + wl.xbuf0;
   p.xbuf[1] = wsb + wl.xbuf1;
   for (int l = 0; l < L; ++l) {

@@ -40,7 +40,7 @@ def both(w, dl, x, B, dev):
     return (to_host(y1), i1.cpu().numpy(), w1.cpu().numpy()), (to_host(y2), i2.cpu().numpy(), w2.cpu().numpy())
 
 
-@pytest.mark.parametrize("name,batches", [("k3_b8", (8, 2, 1)), ("tiny_f32", (9, 3, 1)), ("k3_b1", (27, 5))])
+@pytest.mark.parametrize("name,batches", [("k3_b8", (8, 2, 1)), ("tiny_f32", (9, 3, 1)), ("k3_b1", (26, 5))])
 def test_static_workspace_matches_caller_workspace(dev, name, batches):
     w = synth.WORKLOADS[name]
     dl = DeviceLayer(w, device=dev)
@@ -59,8 +59,8 @@ def test_static_workspace_matches_caller_workspace(dev, name, batches):
 def test_static_workspace_refuses_large_shapes(dev):
     w = synth.WORKLOADS["k3_b64_zipf"]
     d = desc_of(w)
-    assert md.moe_workspace_bytes(d, 27, 1) <= 16 << 20 < md.moe_workspace_bytes(d, 28, 1)
+    assert md.moe_workspace_bytes(d, 26, 1) <= 16 << 20 < md.moe_workspace_bytes(d, 27, 1)
     FAKE = 1 << 40
     wt = md.moe_layer_weights(FAKE, FAKE, None, FAKE, FAKE, None, None, FAKE, FAKE)
-    st = md.moe_decode_layer_static(d, wt, FAKE + (1 << 30), FAKE + (2 << 30), 28, None, None, check=False)
+    st = md.moe_decode_layer_static(d, wt, FAKE + (1 << 30), FAKE + (2 << 30), 27, None, None, check=False)
     assert st == md.MOE_ERR_UNSUPPORTED and "static workspace" in md.moe_last_error()
