@@ -164,11 +164,10 @@ moe_status moe_decode_layer_static(const moe_layer_desc *desc, const moe_layer_w
  * L structs), in one persistent launch: y = layer_{L-1}(... layer_0(x)), each
  * layer's bf16 output feeding the next layer's RMSNorm. The layers stay in one
  * launch (openai-hub.com "Kimi K3 ... 1.68x", section on why decode suits a
- * megakernel), and while a layer's barrier is pending each wave loads the
- * first router and shared gate/up slices it will read in the next layer, the
- * single-GPU form of warming next-step weights while memory would idle
- * (smzdm.com post, section "what changed", bandwidth-stealing prefetch item;
- * aiposthub.com article, section on what the K3 decode path changed).
+ * megakernel), separated by one grid barrier. (Warming the next layer's
+ * weights during that barrier, the single-GPU form of the pages' next-step
+ * prefetch (smzdm.com post, section "what changed", bandwidth-stealing
+ * prefetch item), was measured and left out: it slowed every batch.)
  *   topk_idx [L][B][k] / topk_w [L][B][k]: the routing of every layer, or NULL. */
 moe_status moe_decode_stack(const moe_layer_desc *desc, const moe_layer_weights *layers, int32_t L,
                             const void *x, void *y, int32_t B, int32_t *topk_idx, float *topk_w,

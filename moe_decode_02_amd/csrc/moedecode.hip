@@ -29,9 +29,8 @@
 //           each group's routed down rows once that group's barrier has
 //           passed, overlapping later gate/up work, then combines in a fixed
 //           order with the routing weights and the residual.
-//   stack   Between layers one more barrier; while waiting for it, a
-//           workgroup loads the next layer's router and shared-expert rows
-//           that it will read first, so they come from cache.
+//   stack   Between layers one more barrier (published: the combine writes
+//           the next layer's input with device-coherent stores).
 //
 // Weight rows stream through 16-byte non-temporal loads, whole chunks of 64
 // lanes with no per-lane guard, all loads of a step in flight before the
@@ -199,7 +198,6 @@ struct SmemHead {
   int shared_claim, shared_ready;  // small regime: ... and the shared expert's h
   int unit_ctr[2 + kP1Groups];     // P2 units handed out to waves (shared, experts / expert group)
   int nM, nG;                      // general regime: union slots on MFMA tiles, on GEMV
-  unsigned sink;
   int expired;                     // a wait of this workgroup gave up at its watchdog during this launch
 };
 
@@ -2177,14 +2175,6 @@ __device__ __forceinline__ void combine(KParams p, KLayer lp, const Lds &L, int 
   }
 }
 
-// Bring the lines of [p, p + bytes) into the caches: one 4-byte load per
-// 128-byte line, folded into a value that is never used.
-__device__ __forceinline__ unsigned touch_lines(const char *p, size_t bytes) {
-  unsigned acc = 0;
-  for (size_t off = (size_t)lane_id() * 128; off < bytes; off += 64 * 128) acc ^= *(const unsigned *)(p + off);
-  return acc;
-}
-
 // P0 task of wave wv of workgroup g in round r, or -1. Every round but the
 // last gives each workgroup kWaves consecutive task indices; the last gives
 // each p0w (fewer when the tasks left do not need all waves), so the spare
@@ -2194,49 +2184,6 @@ __device__ __forceinline__ unsigned touch_lines(const char *p, size_t bytes) {
 __device__ __forceinline__ int p0_task(KParams p, int r, int g, int wv) {
   const int w = (r == p->p0r - 1) ? p->p0w : kWaves;
   return wv < w ? r * p->G * kWaves + g * w + wv : -1;
-}
-
-// The weights this wave reads first in the next layer's P0 (its router and
-// shared gate/up slices), loaded while the layer barrier is pending.
-template <int RD, int SD, bool MSH>
-__device__ __forceinline__ unsigned prefetch_p0(KParams p, KLayer nl) {
-  const int H = p->H, NSR = p->NSR, NSS = p->NSS, E = p->E, Is = p->Is;
-  const int nrt = E * NSR;
-  unsigned acc = 0;
-  for (int r = 0; r < p->p0r; ++r) {
-    const int tau = p0_task(p, r, wg_id(p), wave_id());
-    if (tau < 0 || tau >= p->p0_end) continue;
-    if (tau < nrt) {
-      const int e = tau / NSR, s = tau % NSR;
-      const size_t ks = (size_t)(H / NSR) * dsz<RD>();
-      acc ^= touch_lines((const char *)nl->rw + (size_t)e * H * dsz<RD>() + s * ks, ks);
-    } else if (!MSH && tau >= p->s0) {
-      const int j = (tau - p->s0) / NSS, s = (tau - p->s0) % NSS;
-      const size_t ks = (size_t)(H / NSS) * dsz<SD>();
-      const size_t rowb = (size_t)H * dsz<SD>();
-      acc ^= touch_lines((const char *)nl->sgu + (size_t)j * rowb + s * ks, ks);
-      acc ^= touch_lines((const char *)nl->sgu + (size_t)(Is + j) * rowb + s * ks, ks);
-    }
-  }
-  if (MSH) {
-    // this wave's columns of the workgroup's first router unit and shared tile
-    if (wg_id(p) < router_units(p)) {
-      const int tile = wg_id(p) / p->rq, q = wg_id(p) % p->rq;
-      const int b0 = router_unit_blk(p, q, wave_id()), b1 = router_unit_blk(p, q, wave_id() + 1);
-      for (int r = 0; r < 16 && 16 * tile + r < E; ++r)
-        acc ^= touch_lines((const char *)nl->rw + ((size_t)(16 * tile + r) * H + (size_t)b0 * 16) * dsz<RD>(),
-                           (size_t)(b1 - b0) * 16 * dsz<RD>());
-    }
-    if (wg_id(p) < Is / 8) {
-      const int k0 = shared_tile_k(H, wave_id()), k1 = shared_tile_k(H, wave_id() + 1);
-      const int j = wg_id(p);
-      for (int r = 0; r < 16; ++r)
-        acc ^= touch_lines((const char *)nl->sgu + (size_t)shared_tile_row(Is, j, r) * H * dsz<SD>() +
-                               (size_t)k0 * dsz<SD>(),
-                           (size_t)(k1 - k0) * dsz<SD>());
-    }
-  }
-  return acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -2431,10 +2378,9 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
   const int W = wg_id(p) * kWaves + wv;  // global wave id of this share
 
   for (int i = tid; i < kMaxBarriers; i += kThreads) sh.bar_cnt[i] = sh.bar_claim[i] = sh.bar_flag[i] = 0;
-  if (tid == 0) sh.sink = sh.expired = 0;
+  if (tid == 0) sh.expired = 0;
   dbg_delay(p, DLY_START, 0);
 
-  unsigned sink = 0;
   bool poisoned = false;  // a wait gave up during this launch (this workgroup's, or one before a barrier it passed)
   for (int l = 0; l < p->L; ++l) {
     KLayer lp = &p->lp[l];
@@ -2524,11 +2470,9 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       // by the combine) and values published by this layer; its workspace
       // buffers are rewritten before other workgroups read them
       bar_arrive_published(p, sh, b0 + BAR_LAYER);
-      sink ^= prefetch_p0<RD, SD, MSH>(p, &p->lp[l + 1]);
       bar_wait(p, sh, b0 + BAR_LAYER);
     }
   }
-  if (sink == 0x9E3779B9u) sh.sink = sink;  // keeps the prefetch loads; practically never taken
 
   // after a watchdog stop the routing outputs are not trusted either: the
   // workgroup that wrote them overwrites them with -1 / NaN
