@@ -28,6 +28,7 @@ DEV_SO = os.path.join(_HERE, "libsynth_dev.so")
 TABLE_SIZE = 1 << 14
 T_X, T_GAMMA, T_ROUTER, T_EXPERT_GU, T_EXPERT_D, T_SHARED_GU, T_SHARED_D = 1, 2, 3, 4, 5, 6, 7
 T_BIAS_PERM, T_SCALE_GU, T_SCALE_D = 8, 9, 10
+T_SPEC = 11  # draft-token perturbations of the speculative-decoding verify workload
 
 F32, BF16, FP8 = 0, 1, 2
 WEIGHT_SIGMA = 0.02
@@ -191,6 +192,10 @@ class Workload:
     zipf_s: float = 0.0       # router bias = log-Zipf(s) when > 0
     eps: float = 1e-6
     scale_group: int = 128
+    # speculative-decoding verify step: each request contributes its base
+    # token and spec_drafts draft tokens, x_draft = act(x_base + spec_delta * z)
+    spec_drafts: int = 0
+    spec_delta: float = 0.0
 
     @property
     def B(self) -> int:
@@ -212,15 +217,35 @@ WORKLOADS = {
     "k3_stack4_fp8": Workload("k3_stack4_fp8", H=7168, E=896, k=16, I=1024, Is=2048, act=BF16,
                               router=BF16, expert=FP8, shared=BF16, seed=4,
                               batches=(1, 2, 4, 16, 64), layers=4),
+    # the verify step of speculative decoding on the K3 share: R requests of
+    # 1 + 7 tokens (R = 1 and 8), drafts perturbing their request's base token
+    "k3_spec_verify": Workload("k3_spec_verify", H=7168, E=896, k=16, I=1024, Is=2048, act=BF16,
+                               router=F32, expert=BF16, shared=BF16, seed=5, batches=(8, 64),
+                               spec_drafts=7, spec_delta=0.5),
 }
+
+
+def token_row(w: Workload, t: int, attempts=None, layer: int = 0) -> np.ndarray:
+    """Token t of a layer input [H] in the activation dtype (redraw attempts[t]).
+    Verify-step workloads (spec_drafts > 0): token t = r * (1 + drafts) + d is
+    request r's base token (d = 0, an N(0, 1) draw) or a draft, the base plus
+    spec_delta * N(0, 1) in fp32, stored in the activation dtype; a draft's
+    attempt redraws its perturbation, the base's attempt the whole request."""
+    a = 0 if attempts is None else int(attempts[t])
+    if w.spec_drafts <= 0:
+        return fill_host((w.H,), key(w.seed, layer, T_X, t, a), w.act, INPUT_SIGMA)
+    g = 1 + w.spec_drafts
+    t0 = (t // g) * g
+    a0 = 0 if attempts is None else int(attempts[t0])
+    x = fill_host((w.H,), key(w.seed, layer, T_X, t0, a0), F32, INPUT_SIGMA)
+    if t != t0:
+        x = x + fill_host((w.H,), key(w.seed, layer, T_SPEC, t, a), F32, w.spec_delta)
+    return x.astype(np.float32) if w.act == F32 else _bf16_bits_of(x)
 
 
 def x_tokens(w: Workload, B: int, attempts=None, layer: int = 0) -> np.ndarray:
     """Layer input [B][H] in the activation dtype; token t uses redraw attempts[t]."""
-    rows = []
-    for t in range(B):
-        a = 0 if attempts is None else int(attempts[t])
-        rows.append(fill_host((w.H,), key(w.seed, layer, T_X, t, a), w.act, INPUT_SIGMA))
+    rows = [token_row(w, t, attempts, layer) for t in range(B)]
     return np.stack(rows) if rows else np.zeros((0, w.H), dtype=_np_dtype(w.act))
 
 

@@ -70,7 +70,7 @@ def draw_tokens_with_margin(w, B, layers_host, min_margin=1e-3, max_attempts=64,
     for t in toks:
         for a in range(max_attempts):
             attempts[t] = a
-            xt = synth.fill_host((1, w.H), synth.key(w.seed, 0, synth.T_X, t, a), w.act, synth.INPUT_SIGMA)
+            xt = synth.token_row(w, t, attempts)[None, :]
             ok = True
             if len(layers_host) == 1:
                 xhat, _ = oracle.rmsnorm(d, xt[0], layers_host[0].gamma)

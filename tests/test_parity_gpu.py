@@ -90,6 +90,10 @@ def full_parity(w, B, dev, poison=True, random_gamma=False):
     Lh = host_layer(w, experts=[], random_gamma=random_gamma)
     x, _ = draw_tokens_with_margin(w, B, [Lh])
     idx_r, w_r, lg_r = oracle_routes(w, Lh, x)
+    if w.spec_drafts:
+        g = 1 + w.spec_drafts
+        per_req = [len(np.unique(idx_r[r:r + g])) for r in range(0, B, g)]
+        log(f"{w.name} B={B}: distinct experts per request {per_req}, in the batch {len(np.unique(idx_r))}")
     add_experts(w, Lh, idx_r)
     y_ref, idx_o, w_o, _ = oracle_layer_tokens(oracle.desc_of(w), Lh, x)
     assert np.array_equal(idx_o, idx_r)
@@ -278,6 +282,16 @@ def test_k3_b64_zipf(dev):
     w = synth.WORKLOADS["k3_b64_zipf"]
     err = full_parity(w, 64, dev, poison=True)
     log(f"k3_b64_zipf all 64 tokens max rel err {err:.2e}")
+
+
+@pytest.mark.parametrize("B", [8, 64])
+def test_k3_spec_verify(dev, B):
+    """The verify step of speculative decoding: B = R * (1 + 7) tokens, each
+    request's drafts perturbing its base token, so a request's tokens share
+    many experts. Every token vs the oracle."""
+    w = synth.WORKLOADS["k3_spec_verify"]
+    err = full_parity(w, B, dev, poison=True)
+    log(f"k3_spec_verify B={B} max rel err {err:.2e}")
 
 
 @pytest.fixture(scope="module")

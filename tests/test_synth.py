@@ -87,3 +87,29 @@ def test_workload_shapes():
     assert x.shape == (2, 7168) and x.dtype == np.uint16
     t = synth.WORKLOADS["tiny_f32"]
     assert synth.router_w(t).shape == (32, 256) and synth.router_w(t).dtype == np.float32
+
+
+def test_spec_verify_tokens():
+    """Verify-step tokens: request r's base token is an N(0, 1) draw stored in
+    bf16; each of its 7 drafts is bf16(base + 0.5 z) with z drawn under its own
+    key, so a draft correlates with its base (~1/sqrt(1.25)) and requests are
+    independent; a draft's redraw changes only that draft."""
+    w = synth.WORKLOADS["k3_spec_verify"]
+    g = 1 + w.spec_drafts
+    x = synth.x_tokens(w, 2 * g)
+    f = lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    base = synth.fill_host((w.H,), synth.key(w.seed, 0, synth.T_X, 0), synth.F32, 1.0)
+    assert np.array_equal(x[0], synth._bf16_bits_of(base))
+    z = synth.fill_host((w.H,), synth.key(w.seed, 0, synth.T_SPEC, 3), synth.F32, w.spec_delta)
+    assert np.array_equal(x[3], synth._bf16_bits_of(base + z))
+    c_in = np.corrcoef(f(x[0]), f(x[5]))[0, 1]
+    c_out = np.corrcoef(f(x[0]), f(x[g]))[0, 1]
+    assert abs(c_in - 1 / np.sqrt(1 + w.spec_delta ** 2)) < 0.02 and abs(c_out) < 0.05
+    att = np.zeros(2 * g, np.int64)
+    att[3] = 1
+    y = synth.x_tokens(w, 2 * g, att)
+    assert not np.array_equal(y[3], x[3]) and np.array_equal(np.delete(y, 3, 0), np.delete(x, 3, 0))
+    att[:] = 0
+    att[g] = 1  # the second request's base: all its tokens move
+    y = synth.x_tokens(w, 2 * g, att)
+    assert np.array_equal(y[:g], x[:g]) and not any(np.array_equal(y[t], x[t]) for t in range(g, 2 * g))
