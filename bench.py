@@ -15,9 +15,12 @@ workload's seed) and their own token batch; the routed-expert tensor is
 common to them (the routing of different instances picks nearly disjoint
 experts).
 
-With --unfused a step is one call of moe_decode_layer_unfused instead: the
-same layer as eleven kernel launches with every intermediate in device memory,
-the baseline the fused kernel is measured against.
+With --unfused a step is one call of moe_decode_layer_unfused instead (of
+moe_decode_stack_unfused for the stack workload): the same layer as eleven
+kernel launches with every intermediate in device memory, the baseline the
+fused kernel is measured against. --side shared|prefetch|both moves the shared
+expert and / or a next-layer weight prefetch of that path to a second stream
+(moe_decode_stack_unfused's flags).
 
 `value` is tokens per second (B / step time). The roofline object gives the
 weight bytes the step must touch (router + shared + gain + every distinct
@@ -45,6 +48,8 @@ WORKLOAD_NOTES = {
     "k3_b8": "K3-scale layer share at B=8",
     "k3_b64_zipf": "K3-scale layer share at B=64 with log-Zipf(1.1) router bias",
     "k3_stack4_fp8": "4-layer K3-scale stack, fp8 e4m3 experts (bf16 scale per 128 rows), bf16 router/shared",
+    "k3_spec_verify": "K3-scale layer share, speculative-decoding verify step: requests of 1 base + 7 draft tokens "
+                      "(drafts = base + 0.5 N(0,1))",
 }
 
 
@@ -58,19 +63,34 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="k3_b1",
-                    choices=["tiny_f32", "k3_b1", "k3_b8", "k3_b64_zipf", "k3_stack4_fp8"])
+                    choices=["tiny_f32", "k3_b1", "k3_b8", "k3_b64_zipf", "k3_stack4_fp8", "k3_spec_verify"])
     ap.add_argument("--batch", type=int, default=None, help="tokens per step (default: the workload's first)")
     ap.add_argument("--copies", type=int, default=8, help="layer instances the timed loop rotates over")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="time the multi-launch path (moe_decode_layer_unfused) instead of the fused kernel")
+    ap.add_argument("--side", choices=["none", "shared", "prefetch", "both"], default="none",
+                    help="with --unfused: work on a second stream (the shared expert, the next layer's prefetch)")
     return ap.parse_args()
 
 
 def cpu_baseline(w, B, budget_s):
     """The oracle (single-threaded plain C) on tokens of the same workload,
-    until about budget_s seconds of oracle time have run."""
+    until about budget_s seconds of oracle time have run, on one core: the
+    calling thread pins itself to the last core it may use (Linux applies
+    sched_setaffinity(0) to the calling thread only) and restores its
+    affinity afterwards."""
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[-1]
+    os.sched_setaffinity(0, {core})
+    try:
+        return _cpu_baseline_pinned(w, B, budget_s, core, len(allowed))
+    finally:
+        os.sched_setaffinity(0, allowed)
+
+
+def _cpu_baseline_pinned(w, B, budget_s, core, ncores):
     import numpy as np
 
     import oracle
@@ -123,31 +143,44 @@ def cpu_baseline(w, B, budget_s):
         pass
     return {"value": ntok / spent, "unit": "tok/s", "cores": 1, "kind": "oracle",
             "sample": f"{ntok} token(s) of {w.name}, one at a time, {spent:.1f} s of single-threaded oracle time",
-            "s_per_step": B * spent / ntok, "cpu_model": model, "host_cores": os.cpu_count()}
+            "s_per_step": B * spent / ntok, "cpu_model": model, "host_cores": os.cpu_count(),
+            "pinned_core": core, "cores_allowed": ncores}
+
+
+# launch shapes of the streaming probe: (256-thread workgroups per CU, 16-byte
+# loads in flight per lane), i.e. workgroups x loads x 4 KB in flight per CU
+# (as far as the workgroups are resident): "wide" fills every wave slot,
+# "tuned" keeps 32 KB per CU, where a 4 GiB read sweep peaked on MI355X (more
+# in flight lowers the rate)
+PROBE_SHAPES = {"wide": (16, 8), "tuned": (4, 2)}
 
 
 def stream_probe(torch, md, dev, stream, gib=4, reps=5):
-    """HBM read rate of a plain 16-byte streaming kernel over `gib` GiB (the
-    practical ceiling of a weight-streaming step on this GPU)."""
+    """HBM read rate (GB/s) of a plain 16-byte streaming kernel over `gib` GiB
+    for each probe shape: the practical ceiling of a weight-streaming step."""
     n = gib << 30
     buf = torch.empty(n, dtype=torch.uint8, device=dev)
     buf.fill_(1)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
-    grid = torch.cuda.get_device_properties(dev).multi_processor_count * 16
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     lib = md.probe_lib()
-    best = 0.0
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        rc = lib.moe_probe_stream_read(buf.data_ptr(), n, sink.data_ptr(), grid, stream.cuda_stream)
-        b.record(stream)
-        if rc != 0:
-            raise RuntimeError(f"moe_probe_stream_read failed: hip error {rc}")
-        torch.cuda.synchronize()
-        best = max(best, n / (a.elapsed_time(b) * 1e-3) / 1e9)
+    out = {}
+    for name, (wg_per_cu, loads) in PROBE_SHAPES.items():
+        best = 0.0
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = lib.moe_probe_stream_read_u(buf.data_ptr(), n, sink.data_ptr(), cus * wg_per_cu, loads,
+                                             stream.cuda_stream)
+            b.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"moe_probe_stream_read_u failed: hip error {rc}")
+            torch.cuda.synchronize()
+            best = max(best, n / (a.elapsed_time(b) * 1e-3) / 1e9)
+        out[name] = best
     del buf
-    return best
+    return out
 
 
 def calibration_copy(torch, md, dev, stream):
@@ -218,18 +251,19 @@ def main() -> int:
         insts.append(layers)
     xs = []
     for c in range(C):
-        xc = np.stack([synth.fill_host((w.H,), synth.key(w.seed, 100 + c, synth.T_X, t), w.act, synth.INPUT_SIGMA)
-                       for t in range(B)])
-        xs.append(to_device(xc, dev))
+        xs.append(to_device(synth.x_tokens(w, B, layer=100 + c), dev))
     ys = [act_tensor(w, B, dev) for _ in range(C)]
     idx = [torch.zeros((L, B, w.k), dtype=torch.int32, device=dev) for _ in range(C)]
     wts = [torch.zeros((L, B, w.k), dtype=torch.float32, device=dev) for _ in range(C)]
     ws = workspace(d, B, L, dev)
+    flags = {"none": 0, "shared": md.MOE_UF_SHARED_SIDE, "prefetch": md.MOE_UF_PREFETCH_SIDE,
+             "both": md.MOE_UF_SHARED_SIDE | md.MOE_UF_PREFETCH_SIDE}[args.side]
+    if flags and not args.unfused:
+        log("bench: --side applies to the multi-launch path (--unfused)")
+        return 2
+    side = torch.cuda.Stream(device=dev) if flags else None  # default priority
     if args.unfused:
-        if L != 1:
-            log("bench: --unfused times one layer; the workload is a stack")
-            return 2
-        ws_unf = torch.empty(md.moe_unfused_workspace_bytes(d, B), dtype=torch.uint8, device=dev)
+        ws_unf = torch.empty(md.moe_unfused_stack_workspace_bytes(d, B, L), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"bench: inputs ready in {time.time() - t0:.1f} s, {torch.cuda.memory_allocated() / 2**30:.1f} GiB on the GPU")
 
@@ -237,9 +271,12 @@ def main() -> int:
 
     def step(i):
         c = i % C
-        if args.unfused:
+        if args.unfused and L == 1 and not flags:
             md.moe_decode_layer_unfused(d, insts[c][0].weights, xs[c], ys[c], B, idx[c], wts[c], ws_unf,
                                         stream=stream)
+        elif args.unfused:
+            md.moe_decode_stack_unfused(d, [li.weights for li in insts[c]], xs[c], ys[c], B, idx[c], wts[c], ws_unf,
+                                        stream=stream, side_stream=side, flags=flags)
         elif L == 1:
             md.moe_decode_layer(d, insts[c][0].weights, xs[c], ys[c], B, idx[c], wts[c], ws, stream=stream)
         else:
@@ -275,6 +312,7 @@ def main() -> int:
         sel = idx[c].cpu().numpy()
         per_inst[c] = sum(insts[c][l].touched_bytes(sel[l]) for l in range(L))
     nbytes = sum(per_inst[i % C] for i in range(args.steps)) / args.steps
+    distinct = [float(np.mean([len(np.unique(idx[c].cpu().numpy()[l])) for l in range(L)])) for c in per_inst]
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     for c in range(C):
         if not torch.isfinite(ys[c].float()).all():
@@ -297,9 +335,10 @@ def main() -> int:
         f"{nbytes / 1e6:.1f} MB/step -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
 
     calibration_copy(torch, md, dev, stream)
-    probe = stream_probe(torch, md, dev, stream)
-    log(f"bench: streaming-read probe {probe:.0f} GB/s ({probe / HBM_PEAK_GBS:.1%} of 8 TB/s); "
-        f"the step reaches {gbs / probe:.1%} of it")
+    probes = stream_probe(torch, md, dev, stream)
+    probe = max(probes.values())
+    log("bench: streaming-read probe " + ", ".join(f"{k} {v:.0f} GB/s" for k, v in probes.items()) +
+        f"; the step reaches {gbs / probe:.1%} of the best")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -330,13 +369,20 @@ def main() -> int:
         "dtype": {synth.F32: "f32", synth.BF16: "bf16", synth.FP8: "fp8e4m3"}[w.expert],
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {WORKLOAD_NOTES[w.name]}", "batch": B, "layers": L,
-                   "rotated_instances": C, "path": "unfused" if args.unfused else "fused",
-                   "kernel_launches_per_step": (11 if w.Is > 0 else 8) if args.unfused else 1},
+                   "rotated_instances": C,
+                   "path": ("unfused" + ("" if not flags else f", side stream: {args.side}")) if args.unfused
+                   else "fused",
+                   "kernel_launches_per_step": L * (11 if w.Is > 0 else 8) + (L - 1) * bool(flags & 2)
+                   if args.unfused else 1,
+                   "distinct_experts_per_layer": round(float(np.mean(distinct)), 1)},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes, "hbm_bytes_per_launch": hbm_bytes},
         "cpu_baseline": cpu,
-        "stream_probe_GBs": probe,
+        "stream_probe_GBs": {k: round(v, 1) for k, v in probes.items()},
+        "stream_probe_shapes": {k: {"workgroups_per_cu": s[0], "loads_per_lane": s[1],
+                                    "kb_in_flight_per_cu": s[0] * 256 * s[1] * 16 // 1024}
+                                for k, s in PROBE_SHAPES.items()},
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -197,6 +197,47 @@ moe_status moe_decode_layer_unfused(const moe_layer_desc *desc, const moe_layer_
                                     const void *x, void *y, int32_t B, int32_t *topk_idx,
                                     float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
+/* Flags of moe_decode_stack_unfused: the side-stream forms the pages give for
+ * two of the specialised path's changes (smzdm.com post, section "what
+ * changed": the shared expert computed on a second stream beside routing, in
+ * the MoE de-dup item; a side kernel that warms the cache with next-step
+ * weights while HBM is otherwise idle, in the bandwidth-stealing prefetch
+ * item). */
+enum {
+  MOE_UF_SHARED_SIDE = 1,   /* each layer's shared gate/up, SiLU*mul and down on side_stream,
+                               concurrent with its routed path */
+  MOE_UF_PREFETCH_SIDE = 2  /* after layer l's RMSNorm, a kernel on side_stream reads layer l+1's
+                               router, shared gate/up and shared down weights with cache-allocating
+                               loads (nothing for the last layer) */
+};
+
+/* Bytes of workspace moe_decode_stack_unfused needs for up to max_tokens
+ * tokens and num_layers layers of this shape; 0 if desc is invalid or outside
+ * the envelope. At num_layers = 1 it equals moe_unfused_workspace_bytes. */
+size_t moe_unfused_stack_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens,
+                                         int32_t num_layers);
+
+/* L layers (1..8) of the same shape through the multi-launch path of
+ * moe_decode_layer_unfused, each layer's output feeding the next layer's
+ * RMSNorm (between layers it lives in the workspace): the same results as
+ * moe_decode_stack, with every layer's eleven launches enqueued by this call.
+ * flags (0, or MOE_UF_* bits) move work to side_stream; the results do not
+ * depend on them (the same kernels on the same data, bit for bit).
+ *   layers: host array of L weight structs. topk_idx / topk_w: [L][B][k] or
+ *   NULL. ws: moe_unfused_stack_workspace_bytes(desc, B, L) bytes, no zero
+ *   fill. stream, side_stream: hipStream_t of the current device;
+ *   side_stream may be NULL only when flags is 0. Work on side_stream waits
+ *   for `stream` through events and is joined back into `stream` before the
+ *   call's last launch, so waiting for `stream` covers all of it. The
+ *   library keeps two events per device for this and enqueues one such call
+ *   at a time (a mutex). Both streams should have the default priority.
+ * Same validation and status codes as moe_decode_layer_unfused; unknown flag
+ * bits, or flags without a side stream, are MOE_ERR_INVALID_ARGUMENT. */
+moe_status moe_decode_stack_unfused(const moe_layer_desc *desc, const moe_layer_weights *layers,
+                                    int32_t L, const void *x, void *y, int32_t B, int32_t *topk_idx,
+                                    float *topk_w, void *ws, size_t ws_bytes, void *stream,
+                                    void *side_stream, uint32_t flags);
+
 /* Synchronises `stream`, then reads and clears the workspace's error word:
  * MOE_ERR_TIMEOUT if a launch on this workspace stopped at a watchdog (a grid
  * barrier or the small-batch logit wait gave up after the watchdog limit),

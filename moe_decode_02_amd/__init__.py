@@ -26,6 +26,7 @@ HEADER = os.path.join(INCLUDE, "moedecode.h")
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED = 0, 1, 2
 MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE, MOE_ERR_TIMEOUT = 3, 4, 5
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_UF_SHARED_SIDE, MOE_UF_PREFETCH_SIDE = 1, 2
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -62,6 +63,8 @@ def probe_lib():
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     L.moe_probe_stream_read.argtypes = [vp, sz, vp, i32, vp]
     L.moe_probe_stream_read.restype = ctypes.c_int
+    L.moe_probe_stream_read_u.argtypes = [vp, sz, vp, i32, i32, vp]
+    L.moe_probe_stream_read_u.restype = ctypes.c_int
     L.moe_probe_copy.argtypes = [vp, vp, sz, i32, vp]
     L.moe_probe_copy.restype = ctypes.c_int
     return L
@@ -85,6 +88,7 @@ class moe_layer_weights(ctypes.Structure):
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_decode_layer", "moe_decode_layer_static", "moe_decode_stack",
            "moe_unfused_workspace_bytes", "moe_decode_layer_unfused",
+           "moe_unfused_stack_workspace_bytes", "moe_decode_stack_unfused",
            "moe_check_workspace", "moe_set_watchdog_ticks", "moe_status_string", "moe_last_error")
 
 
@@ -123,6 +127,10 @@ def _bind(path):
     L.moe_unfused_workspace_bytes.restype = sz
     L.moe_decode_layer_unfused.argtypes = [D, Wt, vp, vp, i32, vp, vp, vp, sz, vp]
     L.moe_decode_layer_unfused.restype = ctypes.c_int
+    L.moe_unfused_stack_workspace_bytes.argtypes = [D, i32, i32]
+    L.moe_unfused_stack_workspace_bytes.restype = sz
+    L.moe_decode_stack_unfused.argtypes = [D, Wt, i32, vp, vp, i32, vp, vp, vp, sz, vp, vp, ctypes.c_uint32]
+    L.moe_decode_stack_unfused.restype = ctypes.c_int
     L.moe_check_workspace.argtypes = [vp, sz, vp]
     L.moe_check_workspace.restype = ctypes.c_int
     L.moe_set_watchdog_ticks.argtypes = [ctypes.c_int64]
@@ -225,6 +233,22 @@ def moe_decode_layer_unfused(desc, weights, x, y, B, topk_idx, topk_w, ws, ws_by
     st = (library or lib()).moe_decode_layer_unfused(ctypes.byref(desc), ctypes.byref(weights), _addr(x), _addr(y), B,
                                         _addr(topk_idx), _addr(topk_w), _addr(ws),
                                         _bytes(ws) if ws_bytes is None else ws_bytes, _stream(stream))
+    if check:
+        _check(st, library)
+    return st
+
+
+def moe_unfused_stack_workspace_bytes(desc: moe_layer_desc, max_tokens: int, num_layers: int) -> int:
+    return lib().moe_unfused_stack_workspace_bytes(ctypes.byref(desc), max_tokens, num_layers)
+
+
+def moe_decode_stack_unfused(desc, layers, x, y, B, topk_idx, topk_w, ws, ws_bytes=None, stream=None,
+                             side_stream=None, flags=0, check=True, library=None):
+    arr = (moe_layer_weights * len(layers))(*layers)
+    st = (library or lib()).moe_decode_stack_unfused(ctypes.byref(desc), arr, len(layers), _addr(x), _addr(y), B,
+                                                     _addr(topk_idx), _addr(topk_w), _addr(ws),
+                                                     _bytes(ws) if ws_bytes is None else ws_bytes, _stream(stream),
+                                                     _stream(side_stream), flags)
     if check:
         _check(st, library)
     return st

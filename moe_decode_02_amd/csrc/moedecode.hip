@@ -197,6 +197,7 @@ struct SmemHead {
   int route_claim, route_ready;    // small regime: the first free wave does the routing
   int shared_claim, shared_ready;  // small regime: ... and the shared expert's h
   int unit_ctr[2 + kP1Groups];     // P2 units handed out to waves (shared, experts / expert group)
+  int p1_ctr[kP1Groups];           // general regime: P1 tasks of the workgroup's share handed out, per group
   int nM, nG;                      // general regime: union slots on MFMA tiles, on GEMV
   int expired;                     // a wait of this workgroup gave up at its watchdog during this launch
 };
@@ -2229,6 +2230,10 @@ __device__ __forceinline__ void p0_tasks(KParams p, KLayer lp, const Lds &L, int
   }
 }
 
+#ifndef MOE_P1_CLAIM
+#define MOE_P1_CLAIM 1
+#endif
+
 // General regime: the first listed slot of P1 group gi of nG: the first slot
 // whose cost prefix reaches gi/nG of the total (gi = nG gives nL).
 __device__ __forceinline__ int group_first_slot(const int *cpre, int nL, int gi, int nG) {
@@ -2240,6 +2245,53 @@ __device__ __forceinline__ int group_first_slot(const int *cpre, int nL, int gi,
     if (cpre[m] < target) a = m + 1; else z = m;
   }
   return a;
+}
+
+// General regime, P1 tasks numbered in listed order: the I/16 MFMA tiles of
+// each MFMA slot, then the I row pairs of each GEMV slot. First task of
+// listed slot i:
+__device__ __forceinline__ int p1_task_base(KParams p, int nM, int i) {
+  const int nb = p->I / 16;
+  return i <= nM ? i * nb : nM * nb + (i - nM) * p->I;
+}
+
+// The first task of listed slots [ia, ib) whose starting cost is >= c
+// (p1_task_base(ib) if none).
+__device__ __forceinline__ int p1_task_at_cost(KParams p, const Lds &L, int ia, int ib, int c) {
+  const int nM = L.head().nM;
+  const int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
+  const int *ucnt = L.at<int>(p->o_ucnt), *cpre = L.at<int>(p->o_cpre);
+  if (ia >= ib || c >= cpre[ib]) return p1_task_base(p, nM, ib);
+  int a = ia, z = ib;  // the last i in [ia, ib) with cpre[i] <= c
+  while (z - a > 1) {
+    const int m = (a + z) >> 1;
+    if (cpre[m] <= c) a = m; else z = m;
+  }
+  if (c <= cpre[a]) return p1_task_base(p, nM, a);
+  const bool mf = a < nM;
+  const int slot = mf ? mslot[a] : gslot[a - nM];
+  const int uc = mf ? mfma_tile_cost(ucnt[slot]) : gemv_pair_cost(ucnt[slot]);
+  // j <= the slot's task count, since c < cpre[a + 1]
+  return p1_task_base(p, nM, a) + (c - cpre[a] + uc - 1) / uc;
+}
+
+// General regime: the P1 tasks [t0, t1) of this workgroup's cost share of
+// one group, handed out to its waves one at a time through the group's LDS
+// counter, so that waves that drew long tasks (MFMA tiles) take fewer and the
+// workgroup's waves finish together.
+template <int AD, int ED>
+__device__ __forceinline__ void p1_claimed(KParams p, KLayer lp, const Lds &L, int t0, int t1, int gi) {
+  SmemHead &sh = L.head();
+  const int I = p->I, nb = I / 16, nM = sh.nM, mt = nM * nb;
+  const int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
+  for (;;) {
+    int q = 0;
+    if (lane_id() == 0) q = __hip_atomic_fetch_add(&sh.p1_ctr[gi], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int t = t0 + __builtin_amdgcn_readfirstlane(q);
+    if (t >= t1) break;
+    if (t < mt) mfma_gu_task<AD, ED>(p, lp, L, mslot[t / nb], t % nb);
+    else expert_gu_task<AD, ED, false>(p, lp, L, gslot[(t - mt) / I], (t - mt) % I);
+  }
 }
 
 // General regime: the P1 tasks of listed slots [ia, ib) whose starting cost
@@ -2389,6 +2441,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
     if (tid == 0) {
       sh.route_claim = sh.route_ready = sh.shared_claim = sh.shared_ready = 0;
       for (int i = 0; i < 2 + kP1Groups; ++i) sh.unit_ctr[i] = 0;
+      for (int i = 0; i < kP1Groups; ++i) sh.p1_ctr[i] = 0;
     }
     __syncthreads();
 
@@ -2438,7 +2491,15 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       for (int gi = 0; gi < nGr; ++gi) {
         const int ia = group_first_slot(cpre, nL, gi, nGr), ib = group_first_slot(cpre, nL, gi + 1, nGr);
         const int Clo = cpre[ia], Chi = cpre[ib];
+#if MOE_P1_CLAIM
+        {
+          const int g = wg_id(p), lo = Clo + share_lo(Chi - Clo, g * kWaves, NW);
+          const int hi = Clo + share_lo(Chi - Clo, (g + 1) * kWaves, NW);
+          p1_claimed<AD, ED>(p, lp, L, p1_task_at_cost(p, L, ia, ib, lo), p1_task_at_cost(p, L, ia, ib, hi), gi);
+        }
+#else
         p1_cost_range<AD, ED>(p, lp, L, ia, ib, Clo + share_lo(Chi - Clo, W, NW), Clo + share_lo(Chi - Clo, W + 1, NW));
+#endif
         bar_arrive(p, sh, b0 + BAR_H + gi);
       }
 
@@ -2815,6 +2876,37 @@ __global__ void __launch_bounds__(kUfThreads) uf_combine(const void *x, const fl
   }
 }
 
+// Side-stream prefetch of the next layer's dense weights (router, shared
+// gate/up, shared down): ordinary (cache-allocating) 16-byte loads over each
+// range, two in flight per lane, so that the lines are in the memory-side
+// cache when the next layer streams them. The loaded words are folded into
+// one value that is stored only if it equals a constant, which keeps the
+// loads without writing anything in practice.
+struct UfPrefetch {
+  const u32x4 *p[3];
+  size_t n16[3];
+  unsigned *sink;
+};
+
+__global__ void __launch_bounds__(kUfThreads) uf_prefetch(UfPrefetch a) {
+  const size_t stride = (size_t)gridDim.x * kUfThreads;
+  unsigned acc = 0;
+  for (int r = 0; r < 3; ++r) {
+    const u32x4 *q = a.p[r];
+    const size_t n = a.n16[r];
+    size_t i = (size_t)blockIdx.x * kUfThreads + threadIdx.x;
+    for (; i + stride < n; i += 2 * stride) {
+      const u32x4 v0 = q[i], v1 = q[i + stride];
+      acc ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
+    }
+    if (i < n) {
+      const u32x4 v = q[i];
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+  }
+  if (acc == 0x9E3779B9u) a.sink[0] = acc;
+}
+
 // ---------------------------------------------------------------------------
 // host runtime
 
@@ -2847,6 +2939,7 @@ struct DevInfo {
   int max_lds = 0;
   int nk = 0;
   KernelReady ready[kMaxKernels];
+  hipEvent_t fork = nullptr, join = nullptr;  // cross-stream ordering of the side-stream variants
 };
 
 DevInfo g_dev[kMaxDevices];
@@ -3256,10 +3349,11 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
 
 // workspace of the multi-launch path
 struct UfLayout {
-  size_t xf, xa, lg, idx, w, nu, ulist, ustart, plist, gu, h, d, sgu, hs, ds, total;
+  size_t xf, xa, lg, idx, w, nu, ulist, ustart, plist, gu, h, d, sgu, hs, ds, sink, xbuf0, xbuf1, total;
 };
 
-UfLayout uf_layout(const moe_layer_desc *d, int B) {
+// L > 1: the layer outputs between layers alternate between two [B][H] buffers
+UfLayout uf_layout(const moe_layer_desc *d, int B, int L = 1) {
   UfLayout u{};
   const size_t act = (size_t)dsize(d->act), H = (size_t)d->hidden, P = (size_t)B * d->top_k;
   const size_t I = (size_t)d->expert_inter, Is = (size_t)d->shared_inter;
@@ -3281,15 +3375,38 @@ UfLayout uf_layout(const moe_layer_desc *d, int B) {
   u.sgu = take((size_t)B * 2 * Is * 4);
   u.hs = take((size_t)B * Is * act);
   u.ds = take((size_t)B * H * 4);
+  u.sink = take(4);
+  if (L > 1) {
+    u.xbuf0 = take((size_t)B * H * act);
+    u.xbuf1 = take((size_t)B * H * act);
+  }
   u.total = off;
   return u;
 }
 
 unsigned uf_blocks(size_t n) { return (unsigned)std::min<size_t>((n + kUfThreads - 1) / kUfThreads, 8192); }
 
+#ifndef MOE_UF_PREFETCH_BLOCKS
+#define MOE_UF_PREFETCH_BLOCKS 64  // workgroups of the side-stream prefetch (a quarter of the CUs)
+#endif
+
+// Work of a layer on the side stream of the multi-launch path.
+struct UfSide {
+  hipStream_t ss = nullptr;      // the side stream
+  hipEvent_t fork = nullptr;     // recorded on the main stream after the RMSNorm; ss waits for it
+  hipEvent_t join = nullptr;     // recorded on ss after the shared expert; the main stream waits before the combine
+  bool shared = false;           // the shared expert's three launches run on ss
+  const UfPrefetch *pf = nullptr;  // a prefetch launched on ss after them, or none
+};
+
+// The eleven launches of one layer on stream st; the shared expert and a
+// prefetch of other weights optionally on a side stream (UfSide), concurrent
+// with the routed path. Returns the first error of the event calls (launch
+// errors are read with hipGetLastError).
 template <int AD, int RD, int ED, int SD>
-void uf_launch_all(const moe_layer_desc *d, const moe_layer_weights *wt, const void *x, void *y, int B,
-                   int32_t *idx, float *wts, unsigned char *ws, const UfLayout &u, hipStream_t st) {
+hipError_t uf_launch_all(const moe_layer_desc *d, const moe_layer_weights *wt, const void *x, void *y, int B,
+                   int32_t *idx, float *wts, unsigned char *ws, const UfLayout &u, hipStream_t st,
+                   const UfSide &sd = UfSide{}) {
   const int H = d->hidden, E = d->num_experts, k = d->top_k, I = d->expert_inter, Is = d->shared_inter;
   const int P = B * k;
   float *xf = (float *)(ws + u.xf);
@@ -3300,6 +3417,30 @@ void uf_launch_all(const moe_layer_desc *d, const moe_layer_weights *wt, const v
   const dim3 blk(kUfThreads);
   // 1. RMSNorm
   hipLaunchKernelGGL(uf_rmsnorm<AD>, dim3(B), dim3(kThreads), 0, st, x, wt->rms_gamma, H, d->rms_eps, xf, xa);
+  // 8.-10. shared expert: gate/up, SiLU * mul, down
+  auto shared_expert = [&](hipStream_t s) {
+    UfGemv a{};
+    a.w = (const char *)wt->shared_gate_up; a.R = 2 * Is; a.K = H; a.x = (const char *)xa; a.x_div = 1; a.nx = B;
+    a.out = sgu;
+    hipLaunchKernelGGL((uf_gemv<SD, AD, 1>), dim3((2 * Is + kUfRows - 1) / kUfRows, B), blk, 0, s, a);
+    hipLaunchKernelGGL(uf_silu_mul<AD>, dim3(uf_blocks((size_t)B * Is)), blk, 0, s, (const float *)sgu, Is, B, hs);
+    a = UfGemv{};
+    a.w = (const char *)wt->shared_down; a.R = H; a.K = Is; a.x = (const char *)hs; a.x_div = 1; a.nx = B;
+    a.out = ds;
+    hipLaunchKernelGGL((uf_gemv<SD, AD, 1>), dim3((H + kUfRows - 1) / kUfRows, B), blk, 0, s, a);
+  };
+  const bool side = sd.shared && Is > 0;
+  hipError_t er = hipSuccess;
+  auto keep = [&](hipError_t e) { if (er == hipSuccess) er = e; };
+  if (side || sd.pf) {
+    keep(hipEventRecord(sd.fork, st));
+    keep(hipStreamWaitEvent(sd.ss, sd.fork, 0));
+    if (side) {
+      shared_expert(sd.ss);
+      keep(hipEventRecord(sd.join, sd.ss));
+    }
+    if (sd.pf) hipLaunchKernelGGL(uf_prefetch, dim3(MOE_UF_PREFETCH_BLOCKS), dim3(kUfThreads), 0, sd.ss, *sd.pf);
+  }
   // 2. router: one weight row per wave for up to 4 tokens
   UfGemv a{};
   a.w = (const char *)wt->router_w; a.R = E; a.K = H; a.x = (const char *)xf; a.x_div = 1; a.nx = B;
@@ -3327,51 +3468,109 @@ void uf_launch_all(const moe_layer_desc *d, const moe_layer_weights *wt, const v
   g.R = H; g.K = I; g.x = (const char *)h; g.x_div = 1;
   g.scale = (const uint16_t *)wt->expert_down_scale; g.out = dd;
   hipLaunchKernelGGL((uf_group_gemv<ED, AD>), dim3((H + kUfRows - 1) / kUfRows, nslot), blk, 0, st, g);
-  if (Is > 0) {
-    // 8.-10. shared expert: gate/up, SiLU * mul, down
-    a = UfGemv{};
-    a.w = (const char *)wt->shared_gate_up; a.R = 2 * Is; a.K = H; a.x = (const char *)xa; a.x_div = 1; a.nx = B;
-    a.out = sgu;
-    hipLaunchKernelGGL((uf_gemv<SD, AD, 1>), dim3((2 * Is + kUfRows - 1) / kUfRows, B), blk, 0, st, a);
-    hipLaunchKernelGGL(uf_silu_mul<AD>, dim3(uf_blocks((size_t)B * Is)), blk, 0, st, (const float *)sgu, Is, B, hs);
-    a = UfGemv{};
-    a.w = (const char *)wt->shared_down; a.R = H; a.K = Is; a.x = (const char *)hs; a.x_div = 1; a.nx = B;
-    a.out = ds;
-    hipLaunchKernelGGL((uf_gemv<SD, AD, 1>), dim3((H + kUfRows - 1) / kUfRows, B), blk, 0, st, a);
-  }
+  if (side) keep(hipStreamWaitEvent(st, sd.join, 0));
+  else if (Is > 0) shared_expert(st);
   // 11. weighted combine + residual
   hipLaunchKernelGGL(uf_combine<AD>, dim3(uf_blocks((size_t)B * H)), blk, 0, st, x, Is > 0 ? (const float *)ds : nullptr,
                      (const float *)dd, (const float *)wts, H, k, B, y);
+  return er;
 }
 
-moe_status launch_unfused(const moe_layer_desc *d, const moe_layer_weights *wt, const void *x, void *y, int B,
-                          int32_t *idx, float *wts, void *ws, size_t ws_bytes, void *stream) {
+// Dense weights of a layer that the side-stream prefetch reads: router, shared gate/up, shared down.
+UfPrefetch uf_prefetch_args(const moe_layer_desc *d, const moe_layer_weights *wt, unsigned *sink) {
+  const size_t H = (size_t)d->hidden, Is = (size_t)d->shared_inter;
+  UfPrefetch a{};
+  a.p[0] = (const u32x4 *)wt->router_w;
+  a.n16[0] = (size_t)d->num_experts * H * dsize(d->router) / 16;
+  a.p[1] = (const u32x4 *)wt->shared_gate_up;
+  a.n16[1] = Is > 0 ? 2 * Is * H * dsize(d->shared) / 16 : 0;
+  a.p[2] = (const u32x4 *)wt->shared_down;
+  a.n16[2] = Is > 0 ? H * Is * dsize(d->shared) / 16 : 0;
+  a.sink = sink;
+  return a;
+}
+
+// L layers through the multi-launch path: layer l reads x (l = 0) or the
+// previous layer's output in the workspace and writes y (l = L - 1) or the
+// other workspace buffer. flags: MOE_UF_SHARED_SIDE puts each layer's shared
+// expert on `side`; MOE_UF_PREFETCH_SIDE launches on `side`, once layer l's
+// RMSNorm is done (and after its shared expert if that is there too), a
+// prefetch of layer l + 1's router and shared weights.
+// Work on `side` is joined back into `stream` before the call's last launch
+// ends, so `stream` alone orders everything the call enqueued.
+moe_status launch_unfused(const moe_layer_desc *d, const moe_layer_weights *layers, int L, const void *x, void *y,
+                          int B, int32_t *idx, float *wts, void *ws, size_t ws_bytes, void *stream, void *side,
+                          unsigned flags) {
   moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
   if (B < 1 || B > kMaxB) return fail(MOE_ERR_UNSUPPORTED, "batch %d outside 1..64", B);
-  if ((st = check_weights(d, wt)) != MOE_OK) return st;
+  if (!layers) return fail(MOE_ERR_INVALID_ARGUMENT, "layers is NULL");
+  if (L < 1 || L > kMaxL) return fail(MOE_ERR_UNSUPPORTED, "%d layers outside 1..%d", L, kMaxL);
+  if (flags & ~(unsigned)(MOE_UF_SHARED_SIDE | MOE_UF_PREFETCH_SIDE))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", flags);
+  if (flags && !side) return fail(MOE_ERR_INVALID_ARGUMENT, "side-stream flags need a side stream");
+  for (int l = 0; l < L; ++l)
+    if ((st = check_weights(d, &layers[l])) != MOE_OK) return st;
   if (!x || !y || !ws) return fail(MOE_ERR_INVALID_ARGUMENT, "x, y or workspace is NULL");
   const void *ptrs[] = {x, y, idx, wts, ws};
   for (const void *q : ptrs)
     if (q && !aligned16(q)) return fail(MOE_ERR_INVALID_ARGUMENT, "pointer %p is not 16-byte aligned", q);
   const size_t xbytes = (size_t)B * d->hidden * dsize(d->act);
   if (y != x && overlap(x, xbytes, y, xbytes)) return fail(MOE_ERR_INVALID_ARGUMENT, "x and y partially overlap");
-  const UfLayout u = uf_layout(d, B);
+  const UfLayout u = uf_layout(d, B, L);
   if (ws_bytes < u.total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes, u.total);
   if (overlap(ws, u.total, x, xbytes) || overlap(ws, u.total, y, xbytes))
     return fail(MOE_ERR_INVALID_ARGUMENT, "workspace overlaps x or y");
   unsigned char *wsb = (unsigned char *)ws;
-  if (!idx) idx = (int32_t *)(wsb + u.idx);
-  if (!wts) wts = (float *)(wsb + u.w);
-  const hipStream_t s = (hipStream_t)stream;
-  if (d->act == MOE_F32) {
-    uf_launch_all<DT_F32, DT_F32, DT_F32, DT_F32>(d, wt, x, y, B, idx, wts, wsb, u, s);
-  } else if (d->expert == MOE_BF16) {
-    if (d->router == MOE_F32) uf_launch_all<DT_BF16, DT_F32, DT_BF16, DT_BF16>(d, wt, x, y, B, idx, wts, wsb, u, s);
-    else uf_launch_all<DT_BF16, DT_BF16, DT_BF16, DT_BF16>(d, wt, x, y, B, idx, wts, wsb, u, s);
-  } else {
-    if (d->router == MOE_F32) uf_launch_all<DT_BF16, DT_F32, DT_FP8, DT_BF16>(d, wt, x, y, B, idx, wts, wsb, u, s);
-    else uf_launch_all<DT_BF16, DT_BF16, DT_FP8, DT_BF16>(d, wt, x, y, B, idx, wts, wsb, u, s);
+  const int P = B * d->top_k;
+  const hipStream_t s = (hipStream_t)stream, ss = (hipStream_t)side;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::unique_lock<std::mutex> order;  // one call at a time records and waits on the device's two events
+  if (flags) {
+    int dev = 0;
+    if ((st = current_device(dev)) != MOE_OK) return st;
+    std::unique_lock<std::mutex> lock(g_dev_mu);
+    DevInfo &di = g_dev[dev];
+    if (!di.fork && hipEventCreateWithFlags(&di.fork, hipEventDisableTiming) != hipSuccess)
+      return fail(MOE_ERR_DEVICE, "hipEventCreateWithFlags failed");
+    if (!di.join && hipEventCreateWithFlags(&di.join, hipEventDisableTiming) != hipSuccess)
+      return fail(MOE_ERR_DEVICE, "hipEventCreateWithFlags failed");
+    fork = di.fork;
+    join = di.join;
+    order = std::move(lock);
+  }
+  for (int l = 0; l < L; ++l) {
+    const moe_layer_weights *wt = &layers[l];
+    const void *xl = l == 0 ? x : (const void *)(wsb + ((l - 1) % 2 ? u.xbuf1 : u.xbuf0));
+    void *yl = l == L - 1 ? y : (void *)(wsb + (l % 2 ? u.xbuf1 : u.xbuf0));
+    int32_t *il = idx ? idx + (size_t)l * P : (int32_t *)(wsb + u.idx);
+    float *wl = wts ? wts + (size_t)l * P : (float *)(wsb + u.w);
+    UfSide sd;
+    UfPrefetch pf;
+    sd.ss = ss;
+    sd.fork = fork;
+    sd.join = join;
+    sd.shared = (flags & MOE_UF_SHARED_SIDE) != 0;
+    if ((flags & MOE_UF_PREFETCH_SIDE) && l + 1 < L) {
+      pf = uf_prefetch_args(d, &layers[l + 1], (unsigned *)(wsb + u.sink));
+      sd.pf = &pf;
+    }
+    hipError_t er;
+    if (d->act == MOE_F32) {
+      er = uf_launch_all<DT_F32, DT_F32, DT_F32, DT_F32>(d, wt, xl, yl, B, il, wl, wsb, u, s, sd);
+    } else if (d->expert == MOE_BF16) {
+      if (d->router == MOE_F32) er = uf_launch_all<DT_BF16, DT_F32, DT_BF16, DT_BF16>(d, wt, xl, yl, B, il, wl, wsb, u, s, sd);
+      else er = uf_launch_all<DT_BF16, DT_BF16, DT_BF16, DT_BF16>(d, wt, xl, yl, B, il, wl, wsb, u, s, sd);
+    } else {
+      if (d->router == MOE_F32) er = uf_launch_all<DT_BF16, DT_F32, DT_FP8, DT_BF16>(d, wt, xl, yl, B, il, wl, wsb, u, s, sd);
+      else er = uf_launch_all<DT_BF16, DT_BF16, DT_FP8, DT_BF16>(d, wt, xl, yl, B, il, wl, wsb, u, s, sd);
+    }
+    if (er != hipSuccess) return fail(MOE_ERR_DEVICE, "stream ordering failed: %s", hipGetErrorString(er));
+  }
+  if (flags) {
+    hipError_t er = hipEventRecord(join, ss);
+    if (er == hipSuccess) er = hipStreamWaitEvent(s, join, 0);
+    if (er != hipSuccess) return fail(MOE_ERR_DEVICE, "stream ordering failed: %s", hipGetErrorString(er));
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
@@ -3435,10 +3634,22 @@ size_t moe_unfused_workspace_bytes(const moe_layer_desc *desc, int32_t max_token
   return uf_layout(desc, max_tokens).total;
 }
 
+size_t moe_unfused_stack_workspace_bytes(const moe_layer_desc *desc, int32_t max_tokens, int32_t num_layers) {
+  if (check_desc(desc) != MOE_OK) return 0;
+  if (max_tokens < 1 || max_tokens > kMaxB || num_layers < 1 || num_layers > kMaxL) return 0;
+  return uf_layout(desc, max_tokens, num_layers).total;
+}
+
 moe_status moe_decode_layer_unfused(const moe_layer_desc *desc, const moe_layer_weights *weights, const void *x,
                                     void *y, int32_t B, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                                     void *stream) {
-  return launch_unfused(desc, weights, x, y, B, topk_idx, topk_w, ws, ws_bytes, stream);
+  return launch_unfused(desc, weights, 1, x, y, B, topk_idx, topk_w, ws, ws_bytes, stream, nullptr, 0);
+}
+
+moe_status moe_decode_stack_unfused(const moe_layer_desc *desc, const moe_layer_weights *layers, int32_t L,
+                                    const void *x, void *y, int32_t B, int32_t *topk_idx, float *topk_w, void *ws,
+                                    size_t ws_bytes, void *stream, void *side_stream, uint32_t flags) {
+  return launch_unfused(desc, layers, L, x, y, B, topk_idx, topk_w, ws, ws_bytes, stream, side_stream, flags);
 }
 
 const char *moe_status_string(moe_status s) {

@@ -27,6 +27,12 @@ not the decode path).
     the decode kernel (for example LDS bank conflicts against LDS
     instructions, or L2 hits against misses).
 
+`python -m moe_decode_02_amd.profiling unfused <fetch_dir> <write_dir> <out.txt> <command...>`
+    the same two runs for the multi-launch path: per kernel of that path
+    (the `uf_` kernels), dispatches and HBM bytes read and written per
+    dispatch, and the totals per layer (the dispatches of its combine kernel
+    count the layers), scaled by the copy kernel as above.
+
 `<command...>` is the profiled command line, copied into the summary.
 """
 from __future__ import annotations
@@ -42,6 +48,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(HERE, "csrc", "moedecode.hip")
 DECODE_KERNEL = "::moe_kernel<"
 COPY_KERNEL = "::copy_kernel("
+UNFUSED_KERNEL = "::uf_"
+UNFUSED_LAYER_END = "::uf_combine<"
 # bytes the benchmark's calibration copy reads (and writes)
 COPY_BYTES = 1 << 30
 
@@ -128,6 +136,33 @@ def write_traffic(fetch_dir: str, write_dir: str, out_txt: str, command: str) ->
         f.write("\n".join(lines) + "\n")
 
 
+def write_unfused_traffic(fetch_dir: str, write_dir: str, out_txt: str, command: str) -> None:
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+    cf, cw = _pick(fetch, COPY_KERNEL), _pick(write, COPY_KERNEL)
+    fetch_scale = COPY_BYTES / (statistics.mean(cf) * 1024.0)
+    write_scale = COPY_BYTES / (statistics.mean(cw) * 1024.0)
+    layers = len(_pick(fetch, UNFUSED_LAYER_END))
+    lines = ["# HBM traffic of the multi-launch path from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE",
+             f"# command: {command}",
+             f"# copy calibration: fetch_scale {fetch_scale:.4f}, write_scale {write_scale:.4f}",
+             f"kernel_source_sha256 = {kernel_source_sha()}",
+             f"layers = {layers}",
+             f"{'kernel':60s} {'calls':>6s} {'read_MB_per_call':>17s} {'write_MB_per_call':>18s}"]
+    tr = tw = 0.0
+    for name in sorted(k for k in fetch if UNFUSED_KERNEL in k):
+        fv, wv = fetch[name], write.get(name, [0.0])
+        rb = statistics.mean(fv) * 1024.0 * fetch_scale
+        wb = statistics.mean(wv) * 1024.0 * write_scale
+        tr += sum(fv) * 1024.0 * fetch_scale
+        tw += sum(wv) * 1024.0 * write_scale
+        short = name if len(name) <= 60 else name[:57] + "..."
+        lines.append(f"{short:60s} {len(fv):6d} {rb / 1e6:17.3f} {wb / 1e6:18.3f}")
+    lines += [f"hbm_read_bytes_per_layer = {tr / layers:.0f}", f"hbm_write_bytes_per_layer = {tw / layers:.0f}"]
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def read_traffic(path: str):
     """HBM bytes per launch from a traffic summary, or None when the summary is
     missing or was taken on a different kernel source."""
@@ -196,6 +231,9 @@ def main(argv) -> int:
         return 0
     if len(argv) >= 4 and argv[1] == "counters":
         write_counters(argv[2], argv[3], " ".join(argv[4:]))
+        return 0
+    if len(argv) >= 5 and argv[1] == "unfused":
+        write_unfused_traffic(argv[2], argv[3], argv[4], " ".join(argv[5:]))
         return 0
     if len(argv) >= 5 and argv[1] == "mfma":
         write_mfma(argv[2], argv[3], argv[4], " ".join(argv[5:]))

@@ -153,3 +153,30 @@ def test_unfused_workspace_bytes(lib):
     # at least the fp32 gate/up and down outputs of every (token, expert) pair
     assert n64 >= 64 * 16 * (2 * 1024 + 7168) * 4 > n1 > 0
     assert md.moe_unfused_workspace_bytes(d, 0) == 0 and md.moe_unfused_workspace_bytes(d, 65) == 0
+
+
+def test_unfused_stack_workspace_and_argument_errors(lib):
+    """moe_decode_stack_unfused: workspace size, layer count, flag and side-stream
+    checks, all returned before any HIP call."""
+    d = desc_of(synth.WORKLOADS["k3_b1"])
+    wt = _weights()
+    one = md.moe_unfused_stack_workspace_bytes(d, 8, 1)
+    assert one == md.moe_unfused_workspace_bytes(d, 8)
+    four = md.moe_unfused_stack_workspace_bytes(d, 8, 4)
+    assert four >= one + 2 * 8 * 7168 * 2  # two bf16 [B][H] buffers between layers
+    assert md.moe_unfused_stack_workspace_bytes(d, 8, 0) == 0 and md.moe_unfused_stack_workspace_bytes(d, 8, 9) == 0
+    x, ws = FAKE + (1 << 30), FAKE + (3 << 30)
+    side = FAKE + (5 << 30)  # never used: every case fails validation first
+
+    def call(layers, wsb, side_stream, flags):
+        return md.moe_decode_stack_unfused(d, layers, x, x, 8, None, None, ws, wsb, side_stream=side_stream,
+                                           flags=flags, check=False)
+
+    assert call([wt] * 9, four, None, 0) == md.MOE_ERR_UNSUPPORTED
+    assert call([wt] * 4, one, None, 0) == md.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert call([wt] * 4, four, None, md.MOE_UF_SHARED_SIDE) == md.MOE_ERR_INVALID_ARGUMENT
+    assert call([wt] * 4, four, None, md.MOE_UF_PREFETCH_SIDE) == md.MOE_ERR_INVALID_ARGUMENT
+    assert call([wt] * 4, four, side, 4) == md.MOE_ERR_INVALID_ARGUMENT
+    assert "flags" in md.moe_last_error()
+    assert lib.moe_decode_stack_unfused(ctypes.byref(d), None, 1, x, x, 8, None, None, ws, four, None, None, 0) == \
+        md.MOE_ERR_INVALID_ARGUMENT

@@ -10,8 +10,8 @@ import torch
 import moe_decode_02_amd as md
 import oracle
 import synth
-from helpers import (add_experts, draw_tokens_with_margin, host_layer, max_rel_err, oracle_layer_tokens,
-                     small_workload, to_f64)
+from helpers import (add_experts, draw_tokens_with_margin, drop_experts, host_layer, margin, max_rel_err,
+                     oracle_layer_tokens, oracle_logits_tokens, pmap, small_workload, to_f64, valid_selection)
 from synth.device import DeviceLayer, act_tensor, desc_of, to_device, to_host
 
 pytestmark = pytest.mark.gpu
@@ -102,3 +102,89 @@ def test_unfused_k3_b1(dev):
 
 def test_unfused_k3_b8(dev):
     parity(synth.WORKLOADS["k3_b8"], 8, dev)
+
+
+def _unfused_chain(w, dls, x, B, dev):
+    """The layers one call of moe_decode_layer_unfused at a time, on one stream:
+    (input of each layer, output, idx [L][B][k], w [L][B][k])."""
+    ins, idxs, ws_ = [x], [], []
+    for dl in dls:
+        got = unfused_layer(w, dl, ins[-1], B, dev)
+        ins.append(got["y"])
+        idxs.append(got["idx"])
+        ws_.append(got["w"])
+    return ins[:-1], ins[-1], np.stack(idxs), np.stack(ws_)
+
+
+def _unfused_stack(w, dls, x, B, dev, flags, side):
+    d = desc_of(w)
+    L = len(dls)
+    xd = to_device(x, dev)
+    yd = act_tensor(w, B, dev)
+    idx = torch.full((L, B, w.k), -1, dtype=torch.int32, device=dev)
+    wts = torch.zeros((L, B, w.k), dtype=torch.float32, device=dev)
+    ws = torch.empty(md.moe_unfused_stack_workspace_bytes(d, B, L), dtype=torch.uint8, device=dev)
+    ws.fill_(0xA5)
+    md.moe_decode_stack_unfused(d, [dl.weights for dl in dls], xd, yd, B, idx, wts, ws,
+                                stream=torch.cuda.current_stream(dev), side_stream=side, flags=flags)
+    torch.cuda.synchronize()
+    return to_host(yd), idx.cpu().numpy(), wts.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,B,layers,check_oracle", [("tiny_f32", 3, 3, True), ("k3_stack4_fp8", 2, 4, True),
+                                                          ("k3_stack4_fp8", 16, 4, False)])
+def test_unfused_stack_side_streams(dev, name, B, layers, check_oracle):
+    """moe_decode_stack_unfused, with the shared expert and / or the next
+    layer's prefetch on a second stream (every flag set, each run twice), is
+    bit-identical to the same layers chained through moe_decode_layer_unfused
+    on one stream: the same kernels on the same data, ordered by events. Each
+    layer of the chain is checked against the oracle teacher-forced (the
+    oracle's layer l on the GPU's input of layer l), every token, with the
+    fused stack's bar: routing bit-exact where the margin is >= 1e-3, else a
+    valid near-tie selection checked on the oracle evaluated on it."""
+    w = synth.WORKLOADS[name]
+    log(f"gpu unfused stack: {name} B={B} layers={layers}")
+    dls = [DeviceLayer(w, layer=l, device=dev) for l in range(layers)]
+    hosts = [host_layer(w, experts=[], layer=l) for l in range(layers)]
+    x, _ = draw_tokens_with_margin(w, B, [hosts[0]])
+    ins, y0, i0, w0 = _unfused_chain(w, dls, x, B, dev)
+    assert np.all(np.isfinite(to_f64(y0, w.act)))
+    side = torch.cuda.Stream(device=dev)  # default priority, as the header asks
+    for flags in (0, md.MOE_UF_SHARED_SIDE, md.MOE_UF_PREFETCH_SIDE, md.MOE_UF_SHARED_SIDE | md.MOE_UF_PREFETCH_SIDE):
+        for rep in range(2):
+            y, i, ww = _unfused_stack(w, dls, x, B, dev, flags, side if flags else None)
+            assert np.array_equal(i, i0), (flags, rep)
+            assert np.array_equal(ww.view(np.uint32), w0.view(np.uint32)), (flags, rep)
+            assert np.array_equal(y, y0), (flags, rep)
+    log(f"  flags 0..3, twice each: bit-identical to the chained single-stream layers")
+    if check_oracle:
+        d = oracle.desc_of(w)
+        tol = TOL[w.act]
+        for l in range(layers):
+            Lh = hosts[l]
+            lg = oracle_logits_tokens(d, Lh, ins[l])
+            add_experts(w, Lh, np.concatenate([i0[l].ravel(),
+                                               np.stack([oracle.route(d, lg[t])[0] for t in range(B)]).ravel()]),
+                        layer=l)
+
+            def check(t):
+                xt = np.ascontiguousarray(ins[l][t])
+                if margin(lg[t], w.k) >= 1e-3:
+                    yr, ir, wr, _ = oracle.layer(d, Lh, xt[None, :])
+                    yr, wr = yr[0], wr[0]
+                    assert np.array_equal(i0[l, t], ir[0]), (t, l)
+                else:
+                    assert valid_selection(lg[t], i0[l, t], w.k, 4e-4), (t, l)
+                    yr, wr, _ = oracle.layer_given(d, Lh, xt, i0[l, t])
+                assert np.allclose(w0[l, t], wr, rtol=1e-4, atol=1e-6), (t, l)
+                out = ins[l + 1][t] if l + 1 < layers else y0[t]
+                err = max_rel_err(to_f64(out, w.act), to_f64(yr, w.act))
+                assert err <= tol, (t, l, err)
+                return err
+
+            errs = pmap(check, range(B))
+            log(f"  layer {l} teacher-forced: max rel err {max(errs):.2e}")
+            drop_experts(Lh)
+    del dls
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
