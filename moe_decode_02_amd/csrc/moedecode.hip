@@ -1720,23 +1720,25 @@ __device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L,
   });
 }
 
-// P2 MFMA tile: rows [o0, o0 + 16) of union slot s's down matrix for all of
-// the expert's tokens; rows >= lo go to the partial sums (rows below lo were
-// written by the previous tile of the same workgroup).
+// P2 MFMA tile: rows [o0, min(o0 + 16, hi)) of union slot s's down matrix for
+// all of the expert's tokens, into the partial sums. Lanes of rows at or past
+// hi (the workgroup's end) load row hi - 1 again, whose lines the same
+// instruction fetches anyway, and their results are dropped: a partial tile
+// reads no bytes beyond its rows.
 template <int AD, int ED>
-__device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &L, int s, int o0, int lo, float *part) {
+__device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &L, int s, int o0, int hi, float *part) {
   const int H = p->H, I = p->I, lane = lane_id();
   const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   const int *pl = L.at<int>(p->o_plist) + ustart[s];
   const int e = ulist[s], n = ucnt[s];
   const int r = lane & 15, kq = lane >> 4;
   const char *wbase = (const char *)lp->ed + (size_t)e * H * I * dsz<ED>();  // < 4 GB: 32-bit offsets
-  const unsigned wo[1] = {(unsigned)((size_t)(o0 + r) * I * dsz<ED>())};
+  const unsigned wo[1] = {(unsigned)((size_t)min(o0 + r, hi - 1) * I * dsz<ED>())};
   // scales of the lane's output rows o0 + 4 kq + i, applied after the tile
   uint32_t sraw[4] = {0x3F80u, 0x3F80u, 0x3F80u, 0x3F80u};
   if constexpr (ED == DT_FP8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sraw[i] = lp->eds[(size_t)e * (H / 128) + (o0 + 4 * kq + i) / 128];
+    for (int i = 0; i < 4; ++i) sraw[i] = lp->eds[(size_t)e * (H / 128) + min(o0 + 4 * kq + i, hi - 1) / 128];
   }
   with_token_tiles(n, [&]<int NT>() {
     unsigned xo[NT];
@@ -1751,7 +1753,7 @@ __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &
       const int o = o0 + 4 * kq + i;
       float sc = 1.f;
       if constexpr (ED == DT_FP8) sc = late_scale(sraw[i]);
-      if (o >= lo) {
+      if (o < hi) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const int c = 16 * t + r;
@@ -1982,12 +1984,11 @@ __device__ __forceinline__ void shared_down_mfma(KParams p, KLayer lp, const Lds
   const int ntile = (pr1 - pr0 + 15) / 16;
   float *part = p->partbuf;
   for (int un = next_unit(p, L.head(), 0); un < ntile * nsh; un = next_unit(p, L.head(), 0)) {
-    const int hf = un / ntile, ti = un % ntile;
-    const int o0 = min(pr0 + 16 * ti, pr1 - 16);  // the last tile ends at pr1
-    const int lo = pr0 + 16 * ti;                 // rows below lo belong to the previous tile
+    const int hf = un / ntile, o0 = pr0 + 16 * (un % ntile);
     const char *wb = (const char *)lp->sd + (size_t)hf * I * 2;
     const char *xb = (const char *)p->hsbuf + (size_t)hf * I * 2;
-    const unsigned wo[1] = {(unsigned)((size_t)(o0 + r) * Is * 2)};
+    // lanes of rows past pr1 load row pr1 - 1 again (no extra bytes); their results are dropped
+    const unsigned wo[1] = {(unsigned)((size_t)min(o0 + r, pr1 - 1) * Is * 2)};
     with_token_tiles(B, [&]<int NT>() {
       unsigned xo[NT];
 #pragma unroll
@@ -1999,7 +2000,7 @@ __device__ __forceinline__ void shared_down_mfma(KParams p, KLayer lp, const Lds
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int o = o0 + 4 * kq + i;
-        if (o >= lo) {
+        if (o < pr1) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             const int c = 16 * t + r;
@@ -2135,10 +2136,7 @@ __device__ __forceinline__ void expert_down_listed(KParams p, KLayer lp, const L
   const int total = nmu + (max(ib, nM) - max(ia, nM)) * nrb;
   for (int un = next_unit(p, L.head(), uc); un < total; un = next_unit(p, L.head(), uc)) {
     if (un < nmu && ntile > 0) {
-      const int ti = un % ntile;
-      const int o0 = min(pr0 + 16 * ti, pr1 - 16);  // the last tile ends at pr1
-      const int lo = pr0 + 16 * ti;                 // rows below lo belong to the previous tile
-      mfma_down_tile<AD, ED>(p, lp, L, mslot[ma + un / ntile], o0, lo, part);
+      mfma_down_tile<AD, ED>(p, lp, L, mslot[ma + un / ntile], pr0 + 16 * (un % ntile), pr1, part);
     } else {
       const int s = un < nmu ? mslot[ma + un / nrb] : gslot[max(ia, nM) - nM + (un - nmu) / nrb];
       const int o0 = pr0 + ((un < nmu ? un : un - nmu) % nrb) * kRowBlock;
@@ -3210,9 +3208,8 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     p.rows_per_wg = rpw;
     p.NSR = k_slices(d->hidden, d->router, 4);
     // general regime, bf16: the router and the shared expert on MFMA tiles
-    // from kMfmaSharedMin tokens. The shared down tiles are 16 rows that end at
-    // the workgroup's last row, so every workgroup must own at least 16 rows
-    // (with fewer, the first workgroup's tile would start at a negative row).
+    // from kMfmaSharedMin tokens, when every workgroup owns at least 16 output
+    // rows (a 16-row down tile over fewer rows would leave most lanes idle).
     p.mfma_sh = (!small && !route_only && d->act == MOE_BF16 && d->shared_inter > 0 && B >= kMfmaSharedMin &&
                  rpw >= 16)
                     ? 1
