@@ -1664,6 +1664,55 @@ __device__ __forceinline__ void mfma_rows(const char *wbase, const unsigned (&wo
   }
 }
 
+// fp8 weights: the same product with two 64-column steps per wait (K a
+// multiple of 128). An fp8 step moves half the weight bytes of a bf16 step,
+// so one step per wait leaves a gate/up tile waiting on latency; the MFMAs
+// run in the same order as mfma_rows, so the results are identical.
+template <int NR, int NT>
+__device__ __forceinline__ void mfma_rows_fp8x2(const char *wbase, const unsigned (&woff)[NR], int K,
+                                                const char *xbase, const unsigned (&xoff)[NT],
+                                                f32x4 (&acc)[NR][NT]) {
+  const unsigned kq = (unsigned)lane_id() >> 4;
+  for (int k0 = 0; k0 < K; k0 += 128) {
+    u32x4 w[2 * NR][1], x[2 * NT][2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const unsigned c = (unsigned)k0 + 64u * (unsigned)st + kq * 16u;  // the lane's 16 columns
+#pragma unroll
+      for (int r = 0; r < NR; ++r) w[st * NR + r][0] = ld16_nt(wbase, woff[r] + c);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        x[st * NT + t][0] = ld16(xbase, xoff[t] + c * 2u);
+        x[st * NT + t][1] = ld16(xbase, xoff[t] + (c + 8u) * 2u);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    mfma_wait(w);
+    mfma_wait(x);
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const u32x4 wr = w[st * NR + r][0];
+        const u32x4 lo = fp8x8_to_bf16(wr.x, wr.y), hi = fp8x8_to_bf16(wr.z, wr.w);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          acc[r][t] = mfma16(lo, x[st * NT + t][0], acc[r][t]);
+          acc[r][t] = mfma16(hi, x[st * NT + t][1], acc[r][t]);
+        }
+      }
+  }
+}
+
+// P1 gate/up product: fp8 weights and up to 2 token tiles (more would not
+// fit the registers twice) take two steps per wait
+template <int WD, int NR, int NT>
+__device__ __forceinline__ void mfma_rows_gu(const char *wbase, const unsigned (&woff)[NR], int K, const char *xbase,
+                                             const unsigned (&xoff)[NT], f32x4 (&acc)[NR][NT]) {
+  if constexpr (WD == DT_FP8 && NT <= 2) mfma_rows_fp8x2<NR, NT>(wbase, woff, K, xbase, xoff, acc);
+  else mfma_rows<WD, NR, NT>(wbase, woff, K, xbase, xoff, acc);
+}
+
 // Run f.template operator()<NT>() with NT = ceil(n / 16) token tiles (1..4).
 template <class F>
 __device__ __forceinline__ void with_token_tiles(int n, F &&f) {
@@ -1705,7 +1754,7 @@ __device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L,
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_rows<ED, 2, NT>(uni(gu), wo, H, (const char *)p->xa, xo, acc);
+    mfma_rows_gu<ED, 2, NT>(uni(gu), wo, H, (const char *)p->xa, xo, acc);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int c = 16 * t + r;
@@ -2228,10 +2277,6 @@ __device__ __forceinline__ void p0_tasks(KParams p, KLayer lp, const Lds &L, int
   }
 }
 
-#ifndef MOE_P1_CLAIM
-#define MOE_P1_CLAIM 1
-#endif
-
 // General regime: the first listed slot of P1 group gi of nG: the first slot
 // whose cost prefix reaches gi/nG of the total (gi = nG gives nL).
 __device__ __forceinline__ int group_first_slot(const int *cpre, int nL, int gi, int nG) {
@@ -2289,34 +2334,6 @@ __device__ __forceinline__ void p1_claimed(KParams p, KLayer lp, const Lds &L, i
     if (t >= t1) break;
     if (t < mt) mfma_gu_task<AD, ED>(p, lp, L, mslot[t / nb], t % nb);
     else expert_gu_task<AD, ED, false>(p, lp, L, gslot[(t - mt) / I], (t - mt) % I);
-  }
-}
-
-// General regime: the P1 tasks of listed slots [ia, ib) whose starting cost
-// falls in [lo, hi).
-template <int AD, int ED>
-__device__ __forceinline__ void p1_cost_range(KParams p, KLayer lp, const Lds &L, int ia, int ib, int lo, int hi) {
-  const int I = p->I, nb = I / 16, nM = L.head().nM;
-  const int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
-  const int *ucnt = L.at<int>(p->o_ucnt), *cpre = L.at<int>(p->o_cpre);
-  // the listed slot holding cost lo: the last i in [ia, ib) with cpre[i] <= lo
-  int a = ia, z = ib;
-  while (z - a > 1) {
-    const int m = (a + z) >> 1;
-    if (cpre[m] <= lo) a = m; else z = m;
-  }
-  for (int i = a; i < ib && cpre[i] < hi; ++i) {
-    const bool mf = i < nM;
-    const int slot = mf ? mslot[i] : gslot[i - nM];
-    const int uc = mf ? mfma_tile_cost(ucnt[slot]) : gemv_pair_cost(ucnt[slot]);
-    const int nt = mf ? nb : I;
-    // tasks j of this slot with cpre[i] + j*uc in [lo, hi)
-    const int j0 = lo > cpre[i] ? (lo - cpre[i] + uc - 1) / uc : 0;
-    const int j1 = min(nt, (hi - cpre[i] + uc - 1) / uc);
-    for (int j = j0; j < j1; ++j) {
-      if (mf) mfma_gu_task<AD, ED>(p, lp, L, slot, j);
-      else expert_gu_task<AD, ED, false>(p, lp, L, slot, j);
-    }
   }
 }
 
@@ -2489,15 +2506,11 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       for (int gi = 0; gi < nGr; ++gi) {
         const int ia = group_first_slot(cpre, nL, gi, nGr), ib = group_first_slot(cpre, nL, gi + 1, nGr);
         const int Clo = cpre[ia], Chi = cpre[ib];
-#if MOE_P1_CLAIM
         {
           const int g = wg_id(p), lo = Clo + share_lo(Chi - Clo, g * kWaves, NW);
           const int hi = Clo + share_lo(Chi - Clo, (g + 1) * kWaves, NW);
           p1_claimed<AD, ED>(p, lp, L, p1_task_at_cost(p, L, ia, ib, lo), p1_task_at_cost(p, L, ia, ib, hi), gi);
         }
-#else
-        p1_cost_range<AD, ED>(p, lp, L, ia, ib, Clo + share_lo(Chi - Clo, W, NW), Clo + share_lo(Chi - Clo, W + 1, NW));
-#endif
         bar_arrive(p, sh, b0 + BAR_H + gi);
       }
 
