@@ -2169,6 +2169,10 @@ __device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Ld
   }
 }
 
+#ifndef MOE_P2_SPREAD
+#define MOE_P2_SPREAD 1
+#endif
+
 // General regime: routed-expert units of rows [pr0, pr1) for listed slots
 // [ia, ib) (MFMA slots first, then GEMV slots), handed out through unit
 // counter uc: MFMA down tiles of 16 rows for the MFMA slots (GEMV units when
@@ -2183,7 +2187,18 @@ __device__ __forceinline__ void expert_down_listed(KParams p, KLayer lp, const L
   const int ma = min(ia, nM), mb = min(ib, nM);
   const int nmu = (mb - ma) * (ntile > 0 ? ntile : nrb);
   const int total = nmu + (max(ib, nM) - max(ia, nM)) * nrb;
-  for (int un = next_unit(p, L.head(), uc); un < total; un = next_unit(p, L.head(), uc)) {
+  for (int u0 = next_unit(p, L.head(), uc); u0 < total; u0 = next_unit(p, L.head(), uc)) {
+#if MOE_P2_SPREAD
+    // MFMA units spread evenly over the claim order: unit j of nmu sits at
+    // position floor(j * total / nmu), the GEMV units fill the rest in order
+    int un;
+    {
+      const int j = (int)(((long long)u0 * nmu + total - 1) / total);  // MFMA positions before u0
+      un = (j < nmu && (int)((long long)j * total / nmu) == u0) ? j : nmu + (u0 - j);
+    }
+#else
+    const int un = u0;
+#endif
     if (un < nmu && ntile > 0) {
       mfma_down_tile<AD, ED>(p, lp, L, mslot[ma + un / ntile], pr0 + 16 * (un % ntile), pr1, part);
     } else {
