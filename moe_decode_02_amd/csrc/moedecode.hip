@@ -108,8 +108,15 @@ constexpr int kCtrlStride = 16;  // words: each control word on its own 64-byte 
 // one arrival counter per tile, after the barrier counters
 constexpr int kMaxRTiles = kMaxE / 16;
 constexpr int kMaxRQ = 8;        // most K parts of a router tile
-enum : int { CTRL_DONE = 0, CTRL_ERR = 1, CTRL_BAR = 2, CTRL_RTILE = CTRL_BAR + kMaxBarriers };
-constexpr size_t kCtrlBytes = (size_t)(CTRL_RTILE + kMaxRTiles) * kCtrlStride * sizeof(unsigned);
+constexpr int kMaxStealG = 512;  // general regime: workgroups whose P1 tail others may take (larger grids: none)
+enum : int {
+  CTRL_DONE = 0,
+  CTRL_ERR = 1,
+  CTRL_BAR = 2,
+  CTRL_RTILE = CTRL_BAR + kMaxBarriers,
+  CTRL_P1 = CTRL_RTILE + kMaxRTiles,  // [workgroup][P1 group]: tasks taken from the shared tail of its share
+};
+constexpr size_t kCtrlBytes = (size_t)(CTRL_P1 + kMaxStealG * 4) * kCtrlStride * sizeof(unsigned);
 // small-regime logit buffers (two layer parities), right after the control words
 constexpr size_t kRlogOffset = (kCtrlBytes + 255u) & ~(size_t)255u;
 constexpr size_t kRlogBytes = (size_t)2 * kSmallB * kMaxE * sizeof(float);
@@ -139,6 +146,7 @@ struct Params {
   int use_mfma;           // general regime: experts with >= kMfmaMin tokens go through MFMA tiles
   int mfma_sh;            // general regime: the router and the shared expert go through MFMA tiles
   int rq;                 // K parts of each router MFMA tile, one workgroup each
+  int steal;              // general regime: P1 share tails taken through CTRL_P1 counters
   int p0_end;             // P0 task indices in [0, p0_end): router slices, then shared slices (VALU)
   int NSR;                // router K-slices
   int NSS;                // shared gate/up K-slices
@@ -2352,6 +2360,53 @@ __device__ __forceinline__ void p1_claimed(KParams p, KLayer lp, const Lds &L, i
   }
 }
 
+// General regime: the last part of every workgroup's share of a P1 group is
+// taken through a counter in the workspace (CTRL_P1), so that a workgroup
+// done with its own tasks takes the remaining tail tasks of others: first
+// its own tail, then the tails of up to MOE_P1_STEAL workgroups g + 8, g + 16,
+// ... (the same XCD when the grid is a multiple of 8). A task's result does
+// not depend on which wave runs it. Each workgroup zeroes its counters at the
+// start of every layer.
+#ifndef MOE_P1_STEAL
+#define MOE_P1_STEAL 4
+#endif
+#ifndef MOE_P1_TAIL_DIV
+#define MOE_P1_TAIL_DIV 4  // a quarter of each share is in its tail
+#endif
+__device__ __forceinline__ void p1_share(KParams p, const Lds &L, int ia, int ib, int Clo, int Chi, int v, int &t0,
+                                         int &tm, int &t1) {
+  const int NW = p->G * kWaves;
+  t0 = p1_task_at_cost(p, L, ia, ib, Clo + share_lo(Chi - Clo, v * kWaves, NW));
+  t1 = p1_task_at_cost(p, L, ia, ib, Clo + share_lo(Chi - Clo, (v + 1) * kWaves, NW));
+  tm = t1 - (t1 - t0) / MOE_P1_TAIL_DIV;
+}
+template <int AD, int ED>
+__device__ __forceinline__ void p1_stealing(KParams p, KLayer lp, const Lds &L, int ia, int ib, int Clo, int Chi,
+                                            int gi) {
+  SmemHead &sh = L.head();
+  const int I = p->I, nb = I / 16, nM = sh.nM, mt = nM * nb, G = p->G, g = wg_id(p);
+  const int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
+  int t0, tm, t1;
+  p1_share(p, L, ia, ib, Clo, Chi, g, t0, tm, t1);
+  p1_claimed<AD, ED>(p, lp, L, t0, tm, gi);  // the private part, through LDS
+  for (int hop = 0; hop <= MOE_P1_STEAL && hop < G; ++hop) {
+    const int v = (g + 8 * hop) % G;
+    if (hop > 0) {
+      if (v == g) break;
+      p1_share(p, L, ia, ib, Clo, Chi, v, t0, tm, t1);
+    }
+    unsigned *ctr = ctrl_word(p, CTRL_P1 + v * kP1Groups + gi);
+    for (;;) {
+      int q = 0;
+      if (lane_id() == 0) q = (int)__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int t = tm + __builtin_amdgcn_readfirstlane(q);
+      if (t >= t1) break;
+      if (t < mt) mfma_gu_task<AD, ED>(p, lp, L, mslot[t / nb], t % nb);
+      else expert_gu_task<AD, ED, false>(p, lp, L, gslot[(t - mt) / I], (t - mt) % I);
+    }
+  }
+}
+
 // One layer at B <= 2. P0: router slices, then shared gate/up slices, dealt
 // round-robin over all waves of the grid (every slice is ~7 KB, so the waves
 // finish together). The first wave of each workgroup to run out of P0 work
@@ -2497,6 +2552,14 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       poisoned |= layer_small<AD, RD, ED, SD>(p, lp, L, b0, W, NW);
     } else {
       // x-hat (published: the barrier needs no L2 write-back)
+      // this workgroup's P1 tail counters start at zero: reset before it
+      // arrives at the x-hat barrier, so before any wave takes a P1 task (all
+      // wait for the router barrier first); the previous layer's and launch's
+      // takes ended before their barriers or launch end (or the outputs are
+      // already poisoned by a watchdog stop)
+      if (p->steal && threadIdx.x < kP1Groups)
+        __hip_atomic_store(ctrl_word(p, CTRL_P1 + wg_id(p) * kP1Groups + (int)threadIdx.x), 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       produce_xhat<AD>(p, lp, L);
       bar_arrive_published(p, sh, b0 + BAR_XHAT);
       bar_wait(p, sh, b0 + BAR_XHAT);
@@ -2521,7 +2584,9 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       for (int gi = 0; gi < nGr; ++gi) {
         const int ia = group_first_slot(cpre, nL, gi, nGr), ib = group_first_slot(cpre, nL, gi + 1, nGr);
         const int Clo = cpre[ia], Chi = cpre[ib];
-        {
+        if (p->steal) {
+          p1_stealing<AD, ED>(p, lp, L, ia, ib, Clo, Chi, gi);
+        } else {
           const int g = wg_id(p), lo = Clo + share_lo(Chi - Clo, g * kWaves, NW);
           const int hi = Clo + share_lo(Chi - Clo, (g + 1) * kWaves, NW);
           p1_claimed<AD, ED>(p, lp, L, p1_task_at_cost(p, L, ia, ib, lo), p1_task_at_cost(p, L, ia, ib, hi), gi);
@@ -2542,6 +2607,12 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       unsigned gerr = 0;
       for (int gi = 0; gi < nGr; ++gi) {
         bar_wait(p, sh, b0 + BAR_H + gi);
+        // every take of this group ended before its barrier: back to zero, so
+        // that the workspace is left as found (the layer start zeroes them
+        // again, which covers a watchdog stop)
+        if (p->steal && threadIdx.x == 0)
+          __hip_atomic_store(ctrl_word(p, CTRL_P1 + wg_id(p) * kP1Groups + gi), 0u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
         if (gi == nGr - 1) gerr = err_word(p);  // latency hidden by the last group's down rows
         const int ia = group_first_slot(cpre, nL, gi, nGr), ib = group_first_slot(cpre, nL, gi + 1, nGr);
         if (r0 < r1) expert_down_listed<AD, ED>(p, lp, L, r0, r1, ia, ib, 2 + gi);
@@ -3248,6 +3319,9 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
       const int ntr = (d->num_experts + 15) / 16;
       p.rq = p.mfma_sh ? std::max(1, std::min(kMaxRQ, p.G / ntr)) : 1;
     }
+    // P1 tail stealing: bf16 experts (fp8 tasks are half as long, and the
+    // workspace atomics measured a little slower there)
+    p.steal = (!small && !route_only && MOE_P1_STEAL > 0 && p.G <= kMaxStealG && d->expert == MOE_BF16) ? 1 : 0;
     // the slices of a row are one workgroup's waves of one round: the shared
     // tasks start at a multiple of the workgroup's wave count, and the rounds
     // must fit the per-round slice counters and LDS slots (else every row is
