@@ -1805,17 +1805,21 @@ __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     mfma_rows<ED, 1, NT>(uni(wbase), wo, I, (const char *)p->hbuf, xo, acc);
+    // the lane's 4 rows o0 + 4 kq .. + 3 are all below hi or all at or past
+    // it (hi - o0 is a multiple of 4): one 16-byte store per token column
+    // (column-major partial sums, 16-byte aligned: H and o0 are multiples of 4)
+    if (o0 + 4 * kq < hi) {
+      float sc[4] = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (ED == DT_FP8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int o = o0 + 4 * kq + i;
-      float sc = 1.f;
-      if constexpr (ED == DT_FP8) sc = late_scale(sraw[i]);
-      if (o < hi) {
+        for (int i = 0; i < 4; ++i) sc[i] = late_scale(sraw[i]);
+      }
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int c = 16 * t + r;
-          if (c < n) part[(size_t)pl[c] * H + o] = acc[0][t][i] * sc;  // column-major
-        }
+      for (int t = 0; t < NT; ++t) {
+        const int c = 16 * t + r;
+        if (c < n)
+          *(f32x4 *)(part + (size_t)pl[c] * H + o0 + 4 * kq) =
+              f32x4{acc[0][t][0] * sc[0], acc[0][t][1] * sc[1], acc[0][t][2] * sc[2], acc[0][t][3] * sc[3]};
       }
     }
   });
@@ -2054,15 +2058,12 @@ __device__ __forceinline__ void shared_down_mfma(KParams p, KLayer lp, const Lds
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
       mfma_rows<DT_BF16, 1, NT>(uni(wb), wo, min(I, Is - hf * I), uni(xb), xo, acc);
+      // as in mfma_down_tile: the lane's 4 rows are all valid or all past pr1
+      if (o0 + 4 * kq < pr1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int o = o0 + 4 * kq + i;
-        if (o < pr1) {
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const int c = 16 * t + r;
-            if (c < B) part[(size_t)(P + c * nsh + hf) * H + o] = acc[0][t][i];  // column-major
-          }
+        for (int t = 0; t < NT; ++t) {
+          const int c = 16 * t + r;
+          if (c < B) *(f32x4 *)(part + (size_t)(P + c * nsh + hf) * H + o0 + 4 * kq) = acc[0][t];  // column-major
         }
       }
     });
