@@ -1777,12 +1777,16 @@ __device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L,
   });
 }
 
-// P2 MFMA tile: rows [o0, min(o0 + 16, hi)) of union slot s's down matrix for
-// all of the expert's tokens, into the partial sums. Lanes of rows at or past
-// hi (the workgroup's end) load row hi - 1 again, whose lines the same
-// instruction fetches anyway, and their results are dropped: a partial tile
-// reads no bytes beyond its rows.
-template <int AD, int ED>
+// P2 MFMA tile: rows [o0, min(o0 + 16 NR, hi)) of union slot s's down matrix
+// for all of the expert's tokens (NR row tiles of 16 rows), into the partial
+// sums. Lanes of rows at or past hi (the workgroup's end) load row hi - 1
+// again, whose lines the same instruction fetches anyway, and their results
+// are dropped: a partial tile reads no bytes beyond its rows. Two row tiles
+// read the tokens' h once for 32 rows.
+#ifndef MOE_P2_TILE_NR
+#define MOE_P2_TILE_NR 2
+#endif
+template <int AD, int ED, int NR>
 __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &L, int s, int o0, int hi, float *part) {
   const int H = p->H, I = p->I, lane = lane_id();
   const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
@@ -1790,36 +1794,48 @@ __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &
   const int e = ulist[s], n = ucnt[s];
   const int r = lane & 15, kq = lane >> 4;
   const char *wbase = (const char *)lp->ed + (size_t)e * H * I * dsz<ED>();  // < 4 GB: 32-bit offsets
-  const unsigned wo[1] = {(unsigned)((size_t)min(o0 + r, hi - 1) * I * dsz<ED>())};
-  // scales of the lane's output rows o0 + 4 kq + i, applied after the tile
-  uint32_t sraw[4] = {0x3F80u, 0x3F80u, 0x3F80u, 0x3F80u};
-  if constexpr (ED == DT_FP8) {
+  unsigned wo[NR];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sraw[i] = lp->eds[(size_t)e * (H / 128) + min(o0 + 4 * kq + i, hi - 1) / 128];
-  }
+  for (int q = 0; q < NR; ++q) wo[q] = (unsigned)((size_t)min(o0 + 16 * q + r, hi - 1) * I * dsz<ED>());
+  // scales of the lane's output rows o0 + 16 q + 4 kq + i, applied after the tile
+  uint32_t sraw[NR][4];
+#pragma unroll
+  for (int q = 0; q < NR; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sraw[q][i] = 0x3F80u;
+      if constexpr (ED == DT_FP8)
+        sraw[q][i] = lp->eds[(size_t)e * (H / 128) + min(o0 + 16 * q + 4 * kq + i, hi - 1) / 128];
+    }
   with_token_tiles(n, [&]<int NT>() {
     unsigned xo[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) xo[t] = (unsigned)pl[min(16 * t + r, n - 1)] * (unsigned)I * 2u;
-    f32x4 acc[1][NT];
+    f32x4 acc[NR][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_rows<ED, 1, NT>(uni(wbase), wo, I, (const char *)p->hbuf, xo, acc);
-    // the lane's 4 rows o0 + 4 kq .. + 3 are all below hi or all at or past
-    // it (hi - o0 is a multiple of 4): one 16-byte store per token column
+    for (int q = 0; q < NR; ++q)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mfma_rows<ED, NR, NT>(uni(wbase), wo, I, (const char *)p->hbuf, xo, acc);
+    // the lane's 4 rows o0 + 16 q + 4 kq .. + 3 are all below hi or all at or
+    // past it (hi - o0 is a multiple of 4): one 16-byte store per token column
     // (column-major partial sums, 16-byte aligned: H and o0 are multiples of 4)
-    if (o0 + 4 * kq < hi) {
-      float sc[4] = {1.f, 1.f, 1.f, 1.f};
-      if constexpr (ED == DT_FP8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[i] = late_scale(sraw[i]);
-      }
+    for (int q = 0; q < NR; ++q) {
+      const int ob = o0 + 16 * q + 4 * kq;
+      if (ob < hi) {
+        float sc[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (ED == DT_FP8) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int c = 16 * t + r;
-        if (c < n)
-          *(f32x4 *)(part + (size_t)pl[c] * H + o0 + 4 * kq) =
-              f32x4{acc[0][t][0] * sc[0], acc[0][t][1] * sc[1], acc[0][t][2] * sc[2], acc[0][t][3] * sc[3]};
+          for (int i = 0; i < 4; ++i) sc[i] = late_scale(sraw[q][i]);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int c = 16 * t + r;
+          if (c < n)
+            *(f32x4 *)(part + (size_t)pl[c] * H + ob) =
+                f32x4{acc[q][t][0] * sc[0], acc[q][t][1] * sc[1], acc[q][t][2] * sc[2], acc[q][t][3] * sc[3]};
+        }
       }
     }
   });
@@ -2192,7 +2208,8 @@ __device__ __forceinline__ void expert_down_listed(KParams p, KLayer lp, const L
   const int nrb = (pr1 - pr0) / kRowBlock, nM = L.head().nM;
   float *part = p->partbuf;
   const int *mslot = L.at<int>(p->o_mslot), *gslot = L.at<int>(p->o_gslot);
-  const int ntile = (pr1 - pr0) >= 16 ? (pr1 - pr0 + 15) / 16 : 0;
+  constexpr int TR = 16 * MOE_P2_TILE_NR;  // rows of a down tile
+  const int ntile = (pr1 - pr0) >= 16 ? (pr1 - pr0 + TR - 1) / TR : 0;
   const int ma = min(ia, nM), mb = min(ib, nM);
   const int nmu = (mb - ma) * (ntile > 0 ? ntile : nrb);
   const int total = nmu + (max(ib, nM) - max(ia, nM)) * nrb;
@@ -2209,7 +2226,7 @@ __device__ __forceinline__ void expert_down_listed(KParams p, KLayer lp, const L
     const int un = u0;
 #endif
     if (un < nmu && ntile > 0) {
-      mfma_down_tile<AD, ED>(p, lp, L, mslot[ma + un / ntile], pr0 + 16 * (un % ntile), pr1, part);
+      mfma_down_tile<AD, ED, MOE_P2_TILE_NR>(p, lp, L, mslot[ma + un / ntile], pr0 + TR * (un % ntile), pr1, part);
     } else {
       const int s = un < nmu ? mslot[ma + un / nrb] : gslot[max(ia, nM) - nM + (un - nmu) / nrb];
       const int o0 = pr0 + ((un < nmu ? un : un - nmu) % nrb) * kRowBlock;
