@@ -70,3 +70,25 @@ def test_counter_means_of_the_decode_kernel(tmp_path):
     text = out.read_text()
     assert "TCC_HIT_sum = 20   (dispatches 2)" in text
     assert "TCC_MISS_sum = 5   (dispatches 1)" in text
+
+
+def test_unfused_traffic_per_layer(tmp_path):
+    """The multi-launch path's summary sums every uf_ kernel's calibrated bytes
+    and divides by the layers (dispatches of its combine kernel)."""
+    kib = profiling.COPY_BYTES / 1024
+    gemv = "void (anonymous namespace)::uf_gemv<1, 1, 1>((anonymous namespace)::UfGemv)"
+    comb = "void (anonymous namespace)::uf_combine<1>(void const*, float const*, ...)"
+    pref = "(anonymous namespace)::uf_prefetch((anonymous namespace)::UfPrefetch)"
+    write_counters(tmp_path / "f", [(COPY, "FETCH_SIZE", kib / 2), (gemv, "FETCH_SIZE", 100.0),
+                                    (gemv, "FETCH_SIZE", 300.0), (comb, "FETCH_SIZE", 10.0),
+                                    (comb, "FETCH_SIZE", 10.0), (pref, "FETCH_SIZE", 50.0),
+                                    (DECODE, "FETCH_SIZE", 1e9)])
+    write_counters(tmp_path / "w", [(COPY, "WRITE_SIZE", kib), (gemv, "WRITE_SIZE", 4.0),
+                                    (gemv, "WRITE_SIZE", 4.0), (comb, "WRITE_SIZE", 2.0), (comb, "WRITE_SIZE", 2.0)])
+    out = tmp_path / "u.txt"
+    profiling.write_unfused_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(out), "cmd")
+    kv = dict(ln.split(" = ") for ln in out.read_text().splitlines() if " = " in ln and not ln.startswith("#"))
+    assert int(kv["layers"]) == 2
+    # reads: (100 + 300 + 10 + 10 + 50) KiB x 2 (FETCH_SIZE counts half) over 2 layers; the decode kernel is not counted
+    assert float(kv["hbm_read_bytes_per_layer"]) == pytest.approx(470 * 1024 * 2 / 2, rel=1e-6)
+    assert float(kv["hbm_write_bytes_per_layer"]) == pytest.approx(12 * 1024 / 2, rel=1e-6)
