@@ -389,6 +389,15 @@ template <> struct XSrc<2> {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
 __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
+// The lane index computed where it is used (volatile, so the compiler neither
+// hoists nor merges it): after a long MFMA loop a lane-derived value kept
+// from before the loop can be spilled, and each reload's wait then also
+// waits for every store in flight.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 
 // The work of "workgroup g" (every share of tasks, rows and tiles is keyed
 // by it). The ordering-stress build maps the hardware workgroups onto these
@@ -437,6 +446,7 @@ constexpr int DPP_ROW_MIRROR = 0x140;
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;
 constexpr int DPP_ROW_BCAST15 = 0x142;
 constexpr int DPP_ROW_BCAST31 = 0x143;
+constexpr int DPP_ROW_ROR8 = 0x128;    // row_ror:8 (lane s of a 16-lane row reads lane (s + 8) % 16)
 
 template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_f(float old, float v) {
@@ -1611,97 +1621,141 @@ __device__ __forceinline__ void mfma_wait(u32x4 (&a)[A][B2]) {
     for (int j = 0; j < B2; ++j) asm volatile("" : "+v"(a[i][j]));
 }
 
-// acc[row tile r][token tile t] += W rows x activation rows over K columns.
-// Lane l: weight row l%16 of each tile, token column l%16, K group l/16.
-// Addresses are a uniform base plus a per-lane 32-bit byte offset (woff[r]:
-// the lane's row of tile r, xoff[t]: the lane's token row of tile t). Each
-// iteration covers 64 columns and issues every load of the iteration (4 KB
-// of weights per wave for a gate/up pair at bf16) before one wait (bf16: two
-// K groups of 8 per lane; fp8: 16 codes per lane feeding two MFMAs, with the
-// activation columns in the same order).
-template <int WD, int NR, int NT>
-__device__ __forceinline__ void mfma_rows(const char *wbase, const unsigned (&woff)[NR], int K, const char *xbase,
-                                          const unsigned (&xoff)[NT], f32x4 (&acc)[NR][NT]) {
-  const unsigned kq = (unsigned)lane_id() >> 4;
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    constexpr int WH = WD == DT_FP8 ? 1 : 2;
-    u32x4 w[NR][WH], x[NT][2];
-    if constexpr (WD == DT_FP8) {
-      const unsigned c = (unsigned)k0 + kq * 16u;  // the lane's 16 columns
+// Whole-line loads. An MFMA operand gives each lane one row (l%16) and
+// 16 bytes of it, so a 16-byte load in operand order reads 64 bytes of each
+// of 16 rows and every 128-byte line is split over two instructions; such
+// loads stream at ~5.4 TB/s where whole-line loads of the same bytes reach
+// ~6.9 (a read-rate probe on MI355X). The tiles therefore load lines: X, rows
+// 0-7 of a 16-row tile, and Y, rows 8-15, each lane reading chunk c(l) of row
+// l%8 (8 lanes cover a row's 128 bytes), and a rotation by 8 lanes within each
+// 16-lane row (DPP row_ror:8) hands lane (kq = l/16, s = l%16) the chunks of
+// row s that operand order gives it: with c(l) = kq + 4((l>>3)&1), chunks kq
+// (a) and 4 + kq (b); with c(l) = 2kq + ((l>>3)&1), chunks 2kq and 2kq + 1.
+// The MFMAs see the same operands as with operand-order loads, so the results
+// do not change.
+// (lane-derived offsets are computed per task from lane_here(): kept from
+// the start of the kernel, they are what the register allocator spills)
+__device__ __forceinline__ int line_row(int h) { return 8 * h + (lane_here() & 7); }  // the lane's row of half h
+__device__ __forceinline__ unsigned line_chunk4() {
+  const int l = lane_here();
+  return (unsigned)((l >> 4) + 4 * ((l >> 3) & 1));
+}
+__device__ __forceinline__ unsigned line_chunk2() {
+  const int l = lane_here();
+  return (unsigned)(2 * (l >> 4) + ((l >> 3) & 1));
+}
+#ifndef MOE_XLINES
+#define MOE_XLINES 1
+#endif
+constexpr int kXH = MOE_XLINES ? 2 : 1;  // activation offsets per token tile
+// the lane's activation row of half h of a token tile (operand order: l%16)
+__device__ __forceinline__ int x_row(int h) { return MOE_XLINES ? line_row(h) : (lane_here() & 15); }
+// in place: X becomes operand a, Y operand b
+__device__ __forceinline__ void lines_to_operands(u32x4 &X, u32x4 &Y) {
+  const bool lo = (lane_id() & 8) == 0;
 #pragma unroll
-      for (int r = 0; r < NR; ++r) w[r][0] = ld16_nt(wbase, woff[r] + c);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        x[t][0] = ld16(xbase, xoff[t] + c * 2u);
-        x[t][1] = ld16(xbase, xoff[t] + (c + 8u) * 2u);
-      }
-    } else {
-      const unsigned c0 = (unsigned)k0 + kq * 8u, c1 = c0 + 32u;  // K groups of this and the next 32 columns
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        w[r][0] = ld16_nt(wbase, woff[r] + c0 * 2u);
-        w[r][1] = ld16_nt(wbase, woff[r] + c1 * 2u);
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        x[t][0] = ld16(xbase, xoff[t] + c0 * 2u);
-        x[t][1] = ld16(xbase, xoff[t] + c1 * 2u);
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    mfma_wait(w);
-    mfma_wait(x);
-    if constexpr (WD == DT_FP8) {
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const u32x4 lo = fp8x8_to_bf16(w[r][0].x, w[r][0].y), hi = fp8x8_to_bf16(w[r][0].z, w[r][0].w);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          acc[r][t] = mfma16(lo, x[t][0], acc[r][t]);
-          acc[r][t] = mfma16(hi, x[t][1], acc[r][t]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-#pragma unroll
-          for (int t = 0; t < NT; ++t) acc[r][t] = mfma16(w[r][h], x[t][h], acc[r][t]);
-    }
+  for (int d = 0; d < 4; ++d) {
+    const unsigned xr = (unsigned)__builtin_amdgcn_mov_dpp((int)X[d], DPP_ROW_ROR8, 0xF, 0xF, false);
+    const unsigned yr = (unsigned)__builtin_amdgcn_mov_dpp((int)Y[d], DPP_ROW_ROR8, 0xF, 0xF, false);
+    X[d] = lo ? X[d] : yr;
+    Y[d] = lo ? xr : Y[d];
   }
 }
 
-// fp8 weights: the same product with two 64-column steps per wait (K a
-// multiple of 128). An fp8 step moves half the weight bytes of a bf16 step,
-// so one step per wait leaves a gate/up tile waiting on latency; the MFMAs
-// run in the same order as mfma_rows, so the results are identical.
+// acc[row tile r][token tile t] += W rows x activation rows over K columns
+// (bf16 weights). Addresses are a uniform base plus a per-lane 32-bit byte
+// offset: woff[r][h] is the lane's row line_row(h) of row tile r, xoff[t][h]
+// its token row x_row(h) of token tile t. Each iteration covers 64 columns,
+// one 128-byte line of every row, and issues every load of the iteration
+// (4 KB of weights per wave for a gate/up pair) before one wait; operand
+// chunks kq and 4 + kq feed the two MFMAs of a row tile.
 template <int NR, int NT>
-__device__ __forceinline__ void mfma_rows_fp8x2(const char *wbase, const unsigned (&woff)[NR], int K,
-                                                const char *xbase, const unsigned (&xoff)[NT],
-                                                f32x4 (&acc)[NR][NT]) {
-  const unsigned kq = (unsigned)lane_id() >> 4;
-  for (int k0 = 0; k0 < K; k0 += 128) {
-    u32x4 w[2 * NR][1], x[2 * NT][2];
+__device__ __forceinline__ void mfma_rows(const char *wbase, const unsigned (&woff)[NR][2], int K, const char *xbase,
+                                          const unsigned (&xoff)[NT][kXH], f32x4 (&acc)[NR][NT]) {
+  const unsigned ch = line_chunk4() * 16u;                          // the lane's chunk of each row's line
+  const unsigned xq = MOE_XLINES ? ch : ((unsigned)lane_here() >> 4) * 16u;  // operand order: chunk kq
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    u32x4 w[NR][2], x[NT][2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const unsigned c = (unsigned)k0 + 64u * (unsigned)st + kq * 16u;  // the lane's 16 columns
+    for (int r = 0; r < NR; ++r) {
+      w[r][0] = ld16_nt(wbase, woff[r][0] + (unsigned)k0 * 2u + ch);
+      w[r][1] = ld16_nt(wbase, woff[r][1] + (unsigned)k0 * 2u + ch);
+    }
 #pragma unroll
-      for (int r = 0; r < NR; ++r) w[st * NR + r][0] = ld16_nt(wbase, woff[r] + c);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        x[st * NT + t][0] = ld16(xbase, xoff[t] + c * 2u);
-        x[st * NT + t][1] = ld16(xbase, xoff[t] + (c + 8u) * 2u);
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (MOE_XLINES) {
+        x[t][0] = ld16(xbase, xoff[t][0] + (unsigned)k0 * 2u + xq);
+        x[t][1] = ld16(xbase, xoff[t][kXH - 1] + (unsigned)k0 * 2u + xq);
+      } else {  // chunks kq and 4 + kq of the token's line
+        x[t][0] = ld16(xbase, xoff[t][0] + (unsigned)k0 * 2u + xq);
+        x[t][1] = ld16(xbase, xoff[t][0] + (unsigned)k0 * 2u + xq + 64u);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     mfma_wait(w);
     mfma_wait(x);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) lines_to_operands(w[r][0], w[r][1]);
+    if constexpr (MOE_XLINES)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) lines_to_operands(x[t][0], x[t][1]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[r][t] = mfma16(w[r][h], x[t][h], acc[r][t]);
+  }
+}
+
+// fp8 weights (up to 2 token tiles): the same product with two 64-column
+// steps per wait (K a multiple of 128), so that a row's 128 codes are one
+// line: chunks kq and 4 + kq feed steps 0 and 1, and the activation's
+// 32-byte pieces of the two steps (chunks 2kq and 2kq + 1 of each step's
+// line) are loaded the same way. A lane's 16 codes are converted exactly to
+// bf16 and feed two MFMAs. An fp8 step moves half the weight bytes of a
+// bf16 step, so one step per wait would leave a tile waiting on latency.
+// The MFMAs run step by step, so the results do not depend on how many
+// steps share a wait.
+template <int NR, int NT>
+__device__ __forceinline__ void mfma_rows_fp8x2(const char *wbase, const unsigned (&woff)[NR][2], int K,
+                                                const char *xbase, const unsigned (&xoff)[NT][kXH],
+                                                f32x4 (&acc)[NR][NT]) {
+  const unsigned wc = line_chunk4() * 16u, xc = line_chunk2() * 16u;
+  for (int k0 = 0; k0 < K; k0 += 128) {
+    u32x4 w[NR][2], x[2 * NT][2];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      w[r][0] = ld16_nt(wbase, woff[r][0] + (unsigned)k0 + wc);
+      w[r][1] = ld16_nt(wbase, woff[r][1] + (unsigned)k0 + wc);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if constexpr (MOE_XLINES) {
+          const unsigned cb = ((unsigned)k0 + 64u * (unsigned)st) * 2u + xc;
+          x[st * NT + t][0] = ld16(xbase, xoff[t][0] + cb);
+          x[st * NT + t][1] = ld16(xbase, xoff[t][kXH - 1] + cb);
+        } else {
+          const unsigned c = (unsigned)k0 + 64u * (unsigned)st + ((unsigned)lane_here() >> 4) * 16u;
+          x[st * NT + t][0] = ld16(xbase, xoff[t][0] + c * 2u);
+          x[st * NT + t][1] = ld16(xbase, xoff[t][0] + (c + 8u) * 2u);
+        }
+      }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    mfma_wait(w);
+    mfma_wait(x);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) lines_to_operands(w[r][0], w[r][1]);
+    if constexpr (MOE_XLINES)
+#pragma unroll
+      for (int i = 0; i < 2 * NT; ++i) lines_to_operands(x[i][0], x[i][1]);
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const u32x4 wr = w[st * NR + r][0];
+        const u32x4 wr = w[r][st];
         const u32x4 lo = fp8x8_to_bf16(wr.x, wr.y), hi = fp8x8_to_bf16(wr.z, wr.w);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -1712,13 +1766,69 @@ __device__ __forceinline__ void mfma_rows_fp8x2(const char *wbase, const unsigne
   }
 }
 
-// P1 gate/up product: fp8 weights and up to 2 token tiles (more would not
-// fit the registers twice) take two steps per wait
+// fp8 weights and 3 or 4 token tiles: a row's 128 codes are loaded as one
+// line, as in mfma_rows_fp8x2, but the activations of the two 64-column
+// steps are loaded one step at a time, in operand order (lane l: token row
+// l%16, its 16 columns as two 16-byte pieces), so that the tile fits the
+// registers without spilling inside the loop; the second step's
+// activation loads (L2) are issued after the first step's MFMAs. Same MFMA
+// order, so the same results.
+template <int NR, int NT>
+__device__ __forceinline__ void mfma_rows_fp8_split(const char *wbase, const unsigned (&woff)[NR][2], int K,
+                                                    const char *xbase, const unsigned (&xoff)[NT][kXH],
+                                                    f32x4 (&acc)[NR][NT]) {
+  const unsigned wc = line_chunk4() * 16u, xc = ((unsigned)lane_here() >> 4) * 32u;
+  const bool hs = (lane_here() & 8) != 0;
+  unsigned xs[NT];  // the lane's token row l%16 of each token tile
+#pragma unroll
+  for (int t = 0; t < NT; ++t) xs[t] = hs ? xoff[t][kXH - 1] : xoff[t][0];
+  for (int k0 = 0; k0 < K; k0 += 128) {
+    u32x4 w[NR][2];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      w[r][0] = ld16_nt(wbase, woff[r][0] + (unsigned)k0 + wc);
+      w[r][1] = ld16_nt(wbase, woff[r][1] + (unsigned)k0 + wc);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      u32x4 x[NT][2];
+      const unsigned cb = ((unsigned)k0 + 64u * (unsigned)st) * 2u + xc;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        x[t][0] = ld16(xbase, xs[t] + cb);
+        x[t][1] = ld16(xbase, xs[t] + cb + 16u);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (st == 0) {
+        mfma_wait(w);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) lines_to_operands(w[r][0], w[r][1]);
+      }
+      mfma_wait(x);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const u32x4 wr = w[r][st];
+        const u32x4 lo = fp8x8_to_bf16(wr.x, wr.y), hi = fp8x8_to_bf16(wr.z, wr.w);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          acc[r][t] = mfma16(lo, x[t][0], acc[r][t]);
+          acc[r][t] = mfma16(hi, x[t][1], acc[r][t]);
+        }
+      }
+    }
+  }
+}
+
+// The expert tiles' product: bf16 weights one 64-column step per wait, fp8
+// weights two (one line per row), with both steps' activations loaded
+// together up to 2 token tiles
 template <int WD, int NR, int NT>
-__device__ __forceinline__ void mfma_rows_gu(const char *wbase, const unsigned (&woff)[NR], int K, const char *xbase,
-                                             const unsigned (&xoff)[NT], f32x4 (&acc)[NR][NT]) {
-  if constexpr (WD == DT_FP8 && NT <= 2) mfma_rows_fp8x2<NR, NT>(wbase, woff, K, xbase, xoff, acc);
-  else mfma_rows<WD, NR, NT>(wbase, woff, K, xbase, xoff, acc);
+__device__ __forceinline__ void mfma_rows_expert(const char *wbase, const unsigned (&woff)[NR][2], int K,
+                                                 const char *xbase, const unsigned (&xoff)[NT][kXH],
+                                                 f32x4 (&acc)[NR][NT]) {
+  if constexpr (WD != DT_FP8) mfma_rows<NR, NT>(wbase, woff, K, xbase, xoff, acc);
+  else if constexpr (NT <= 2) mfma_rows_fp8x2<NR, NT>(wbase, woff, K, xbase, xoff, acc);
+  else mfma_rows_fp8_split<NR, NT>(wbase, woff, K, xbase, xoff, acc);
 }
 
 // Run f.template operator()<NT>() with NT = ceil(n / 16) token tiles (1..4).
@@ -1740,29 +1850,36 @@ __device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L,
   const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   const int *pl = L.at<int>(p->o_plist) + ustart[u];
   const int e = ulist[u], n = ucnt[u];
-  const int r = lane & 15, kq = lane >> 4;
   const size_t rowb = (size_t)H * dsz<ED>();
   const char *gu = (const char *)lp->egu + (size_t)e * 2 * I * rowb;  // < 4 GB: 32-bit offsets
-  const unsigned wo[2] = {(unsigned)((16 * jb + r) * rowb), (unsigned)((I + 16 * jb + r) * rowb)};
+  unsigned wo[2][2];  // gate and up rows 16 jb + line_row(h)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    wo[0][h] = (unsigned)((16 * jb + line_row(h)) * rowb);
+    wo[1][h] = (unsigned)((I + 16 * jb + line_row(h)) * rowb);
+  }
   uint32_t graw = 0x3F80u, uraw = 0x3F80u;
   if constexpr (ED == DT_FP8) {
     const uint16_t *sc = lp->egus + (size_t)e * (2 * I / 128);
-    graw = sc[(16 * jb) / 128];
-    uraw = sc[(I + 16 * jb) / 128];
+    graw = uni((uint32_t)sc[(16 * jb) / 128]);  // uniform: kept in scalar registers
+    uraw = uni((uint32_t)sc[(I + 16 * jb) / 128]);
   }
   with_token_tiles(n, [&]<int NT>() {
-    unsigned xo[NT];
+    unsigned xo[NT][kXH];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int c = min(16 * t + r, n - 1);  // columns past n repeat a valid token; discarded
-      xo[t] = (unsigned)(pl[c] / k) * (unsigned)H * 2u;
-    }
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int h = 0; h < kXH; ++h) {
+        const int c = min(16 * t + x_row(h), n - 1);  // columns past n repeat a valid token; discarded
+        xo[t][h] = (unsigned)(pl[c] / k) * (unsigned)H * 2u;
+      }
     f32x4 acc[2][NT];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_rows_gu<ED, 2, NT>(uni(gu), wo, H, (const char *)p->xa, xo, acc);
+    mfma_rows_expert<ED, 2, NT>(uni(gu), wo, H, (const char *)p->xa, xo, acc);
+    const int r = lane_here() & 15, kq = lane_here() >> 4;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int c = 16 * t + r;
@@ -1780,8 +1897,8 @@ __device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L,
 // P2 MFMA tile: rows [o0, min(o0 + 16 NR, hi)) of union slot s's down matrix
 // for all of the expert's tokens (NR row tiles of 16 rows), into the partial
 // sums. Lanes of rows at or past hi (the workgroup's end) load row hi - 1
-// again, whose lines the same instruction fetches anyway, and their results
-// are dropped: a partial tile reads no bytes beyond its rows. Two row tiles
+// again, whose lines a load of the same step fetches anyway, and their
+// results are dropped: a partial tile reads no bytes beyond its rows. Two row tiles
 // read the tokens' h once for 32 rows.
 #ifndef MOE_P2_TILE_NR
 #define MOE_P2_TILE_NR 2
@@ -1792,31 +1909,34 @@ __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &
   const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   const int *pl = L.at<int>(p->o_plist) + ustart[s];
   const int e = ulist[s], n = ucnt[s];
-  const int r = lane & 15, kq = lane >> 4;
+  const int kq0 = lane >> 4;
   const char *wbase = (const char *)lp->ed + (size_t)e * H * I * dsz<ED>();  // < 4 GB: 32-bit offsets
-  unsigned wo[NR];
-#pragma unroll
-  for (int q = 0; q < NR; ++q) wo[q] = (unsigned)((size_t)min(o0 + 16 * q + r, hi - 1) * I * dsz<ED>());
-  // scales of the lane's output rows o0 + 16 q + 4 kq + i, applied after the tile
-  uint32_t sraw[NR][4];
+  unsigned wo[NR][2];
 #pragma unroll
   for (int q = 0; q < NR; ++q)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sraw[q][i] = 0x3F80u;
-      if constexpr (ED == DT_FP8)
-        sraw[q][i] = lp->eds[(size_t)e * (H / 128) + min(o0 + 16 * q + 4 * kq + i, hi - 1) / 128];
-    }
-  with_token_tiles(n, [&]<int NT>() {
-    unsigned xo[NT];
+    for (int h = 0; h < 2; ++h) wo[q][h] = (unsigned)((size_t)min(o0 + 16 * q + line_row(h), hi - 1) * I * dsz<ED>());
+  // scale of the lane's output rows o0 + 16 q + 4 kq .. + 3 (one 128-row
+  // group: the 4 rows start at a multiple of 4), applied after the tile
+  uint32_t sraw[NR];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) xo[t] = (unsigned)pl[min(16 * t + r, n - 1)] * (unsigned)I * 2u;
+  for (int q = 0; q < NR; ++q) {
+    sraw[q] = 0x3F80u;
+    if constexpr (ED == DT_FP8) sraw[q] = lp->eds[(size_t)e * (H / 128) + min(o0 + 16 * q + 4 * kq0, hi - 1) / 128];
+  }
+  with_token_tiles(n, [&]<int NT>() {
+    unsigned xo[NT][kXH];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int h = 0; h < kXH; ++h) xo[t][h] = (unsigned)pl[min(16 * t + x_row(h), n - 1)] * (unsigned)I * 2u;
     f32x4 acc[NR][NT];
 #pragma unroll
     for (int q = 0; q < NR; ++q)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_rows<ED, NR, NT>(uni(wbase), wo, I, (const char *)p->hbuf, xo, acc);
+    mfma_rows_expert<ED, NR, NT>(uni(wbase), wo, I, (const char *)p->hbuf, xo, acc);
+    const int r = lane_here() & 15, kq = lane_here() >> 4;
     // the lane's 4 rows o0 + 16 q + 4 kq .. + 3 are all below hi or all at or
     // past it (hi - o0 is a multiple of 4): one 16-byte store per token column
     // (column-major partial sums, 16-byte aligned: H and o0 are multiples of 4)
@@ -1824,17 +1944,13 @@ __device__ __forceinline__ void mfma_down_tile(KParams p, KLayer lp, const Lds &
     for (int q = 0; q < NR; ++q) {
       const int ob = o0 + 16 * q + 4 * kq;
       if (ob < hi) {
-        float sc[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (ED == DT_FP8) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sc[i] = late_scale(sraw[q][i]);
-        }
+        const float sc = ED == DT_FP8 ? late_scale(sraw[q]) : 1.f;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const int c = 16 * t + r;
           if (c < n)
             *(f32x4 *)(part + (size_t)pl[c] * H + ob) =
-                f32x4{acc[q][t][0] * sc[0], acc[q][t][1] * sc[1], acc[q][t][2] * sc[2], acc[q][t][3] * sc[3]};
+                f32x4{acc[q][t][0] * sc, acc[q][t][1] * sc, acc[q][t][2] * sc, acc[q][t][3] * sc};
         }
       }
     }
@@ -2009,22 +2125,25 @@ template <int AD>
 __device__ __attribute__((noinline)) void shared_gu_mfma(KParams p_arg, KLayer lp_arg, const Lds &L) {
   const KParams p = uni(p_arg);
   const KLayer lp = uni(lp_arg);
-  const int H = p->H, Is = p->Is, B = p->B, lane = lane_id(), wv = wave_id();
-  const int r = lane & 15, kq = lane >> 4;
+  const int H = p->H, Is = p->Is, B = p->B, wv = wave_id();
   const int k0 = shared_tile_k(H, wv), k1 = shared_tile_k(H, wv + 1);
   float *red = L.at<float>(p->o_red);  // [kWaves][16][B]
   const char *xa = (const char *)p->xa + (size_t)k0 * 2;
   for (int j = wg_id(p); j < Is / 8; j += p->G) {
     const char *wb = (const char *)lp->sgu + (size_t)k0 * 2;
-    const unsigned wo[1] = {(unsigned)((size_t)shared_tile_row(Is, j, r) * H * 2)};  // < 4 GB
+    const unsigned wo[1][2] = {{(unsigned)((size_t)shared_tile_row(Is, j, line_row(0)) * H * 2),  // < 4 GB
+                                (unsigned)((size_t)shared_tile_row(Is, j, line_row(1)) * H * 2)}};
     with_token_tiles(B, [&]<int NT>() {
-      unsigned xo[NT];
+      unsigned xo[NT][kXH];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) xo[t] = (unsigned)min(16 * t + r, B - 1) * (unsigned)H * 2u;
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int h = 0; h < kXH; ++h) xo[t][h] = (unsigned)min(16 * t + x_row(h), B - 1) * (unsigned)H * 2u;
       f32x4 acc[1][NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mfma_rows<DT_BF16, 1, NT>(uni(wb), wo, k1 - k0, uni(xa), xo, acc);
+      mfma_rows<1, NT>(uni(wb), wo, k1 - k0, uni(xa), xo, acc);
+      const int r = lane_here() & 15, kq = lane_here() >> 4;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int c = 16 * t + r;
@@ -2055,9 +2174,8 @@ __device__ __attribute__((noinline)) void shared_gu_mfma(KParams p_arg, KLayer l
 // owns at least 16 rows).
 template <int AD>
 __device__ __forceinline__ void shared_down_mfma(KParams p, KLayer lp, const Lds &L, int pr0, int pr1) {
-  const int H = p->H, I = p->I, Is = p->Is, B = p->B, lane = lane_id();
+  const int H = p->H, I = p->I, Is = p->Is, B = p->B;
   const int nsh = p->nsh, P = B * p->k;
-  const int r = lane & 15, kq = lane >> 4;
   const int ntile = (pr1 - pr0 + 15) / 16;
   float *part = p->partbuf;
   for (int un = next_unit(p, L.head(), 0); un < ntile * nsh; un = next_unit(p, L.head(), 0)) {
@@ -2065,15 +2183,19 @@ __device__ __forceinline__ void shared_down_mfma(KParams p, KLayer lp, const Lds
     const char *wb = (const char *)lp->sd + (size_t)hf * I * 2;
     const char *xb = (const char *)p->hsbuf + (size_t)hf * I * 2;
     // lanes of rows past pr1 load row pr1 - 1 again (no extra bytes); their results are dropped
-    const unsigned wo[1] = {(unsigned)((size_t)min(o0 + r, pr1 - 1) * Is * 2)};
+    const unsigned wo[1][2] = {{(unsigned)((size_t)min(o0 + line_row(0), pr1 - 1) * Is * 2),
+                                (unsigned)((size_t)min(o0 + line_row(1), pr1 - 1) * Is * 2)}};
     with_token_tiles(B, [&]<int NT>() {
-      unsigned xo[NT];
+      unsigned xo[NT][kXH];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) xo[t] = (unsigned)min(16 * t + r, B - 1) * (unsigned)Is * 2u;
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int h = 0; h < kXH; ++h) xo[t][h] = (unsigned)min(16 * t + x_row(h), B - 1) * (unsigned)Is * 2u;
       f32x4 acc[1][NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mfma_rows<DT_BF16, 1, NT>(uni(wb), wo, min(I, Is - hf * I), uni(xb), xo, acc);
+      mfma_rows<1, NT>(uni(wb), wo, min(I, Is - hf * I), uni(xb), xo, acc);
+      const int r = lane_here() & 15, kq = lane_here() >> 4;
       // as in mfma_down_tile: the lane's 4 rows are all valid or all past pr1
       if (o0 + 4 * kq < pr1) {
 #pragma unroll
