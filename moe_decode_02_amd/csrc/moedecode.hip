@@ -143,7 +143,7 @@ struct Params {
   int H, E, k, I, Is, B, L;
   int nsh;                // shared down: column blocks of width <= I (ceil(Is / I)), each a partial-sum column
   int route_only;
-  int use_mfma;           // general regime: experts with >= kMfmaMin tokens go through MFMA tiles
+  int mfma_min;           // general regime: experts with >= mfma_min tokens go through MFMA tiles (0: none)
   int mfma_sh;            // general regime: the router and the shared expert go through MFMA tiles
   int rq;                 // K parts of each router MFMA tile, one workgroup each
   int steal;              // general regime: P1 share tails taken through CTRL_P1 counters
@@ -1579,7 +1579,7 @@ __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Ld
 // permutation on both sides.
 
 #ifndef MOE_MFMA_MIN
-#define MOE_MFMA_MIN 3
+#define MOE_MFMA_MIN 2
 #endif
 #ifndef MOE_MFMA_SHARED_MIN
 #define MOE_MFMA_SHARED_MIN 8
@@ -2210,15 +2210,18 @@ __device__ __forceinline__ void shared_down_mfma(KParams p, KLayer lp, const Lds
 
 // P1 cost of a GEMV row pair of an expert with n tokens and of an MFMA tile
 // (16 pairs, ceil(n/16) token tiles), in tenths of a one-token GEMV pair:
-// per-task timings on MI355X at the K3 share (B=64, every wave streaming).
+// per-task timings on MI355X at the K3 share (B=64, every wave streaming)
+// for the GEMV pairs; the MFMA tile's from step times over a range of
+// values (with whole-line loads a tile costs less than the timings of
+// operand-order loads gave).
 #ifndef MOE_COST_G2
 #define MOE_COST_G2 15
 #endif
 #ifndef MOE_COST_M0
-#define MOE_COST_M0 190
+#define MOE_COST_M0 150
 #endif
 #ifndef MOE_COST_M1
-#define MOE_COST_M1 30
+#define MOE_COST_M1 24
 #endif
 __device__ __forceinline__ int gemv_pair_cost(int n) { return n <= 1 ? 10 : n == 2 ? MOE_COST_G2 : n <= 4 ? 21 : 11 + 4 * n; }
 __device__ __forceinline__ int mfma_tile_cost(int n) { return MOE_COST_M0 + MOE_COST_M1 * ((n + 15) / 16); }
@@ -2227,7 +2230,7 @@ __device__ __forceinline__ int slot_cost(KParams p, bool mfma, int n) {
   return mfma ? (p->I / 16) * mfma_tile_cost(n) : p->I * gemv_pair_cost(n);
 }
 
-// Union slots split by token count: MFMA tiles (n >= kMfmaMin) and GEMV.
+// Union slots split by token count: MFMA tiles (n >= mfma_min) and GEMV.
 __device__ __attribute__((noinline)) void classify_slots(KParams p_arg, const Lds &L) {
   const KParams p = uni(p_arg);
   SmemHead &sh = L.head();
@@ -2239,7 +2242,7 @@ __device__ __attribute__((noinline)) void classify_slots(KParams p_arg, const Ld
     for (int u0 = 0; u0 < nU; u0 += 64) {
       const int u = u0 + lane;
       const bool valid = u < nU;
-      const bool m = valid && p->use_mfma && ucnt[u] >= kMfmaMin;
+      const bool m = valid && p->mfma_min > 0 && ucnt[u] >= p->mfma_min;
       const unsigned long long bm = __ballot(m), bg = __ballot(valid && !m);
       const unsigned long long below = (1ull << lane) - 1ull;
       if (m) mslot[nm + __popcll(bm & below)] = u;
@@ -3535,7 +3538,7 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     // its rows); general regime: they go to the workspace
     const size_t per_row = (size_t)(P + B * nsh) * sizeof(float);
     lds = small ? o + (size_t)rpw * per_row : o;
-    p.use_mfma = (!small && d->expert != MOE_F32 && rpw >= 16) ? 1 : 0;
+    p.mfma_min = (!small && d->expert != MOE_F32 && rpw >= 16) ? kMfmaMin : 0;
     if (lds <= lds_cap) break;
     if (!small) return fail(MOE_ERR_UNSUPPORTED, "shape needs more LDS than the device's %zu bytes", lds_cap);
     if (p.rx32) {  // the router's fp32 x-hat does not fit: form it from x, gamma and r instead
