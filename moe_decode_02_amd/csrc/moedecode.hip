@@ -100,7 +100,10 @@ constexpr int kMaxRounds = 32;  // rounds of P0 slices over the grid's waves
 // expert barriers of the small regime: P1's rounds fall into up to kP1Groups
 // groups, each with a barrier, so the down projections of the experts done in
 // early groups run while later groups are still being computed
-constexpr int kP1Groups = 4;
+#ifndef MOE_P1_GROUPS
+#define MOE_P1_GROUPS 4
+#endif
+constexpr int kP1Groups = MOE_P1_GROUPS;
 enum : int { BAR_XHAT = 0, BAR_ROUTER = 1, BAR_SHARED = 2, BAR_LAYER = 3, BAR_H = 4, kBarPerLayer = 4 + kP1Groups };
 constexpr int kMaxBarriers = kBarPerLayer * kMaxL;
 constexpr int kCtrlStride = 16;  // words: each control word on its own 64-byte line
@@ -116,7 +119,7 @@ enum : int {
   CTRL_RTILE = CTRL_BAR + kMaxBarriers,
   CTRL_P1 = CTRL_RTILE + kMaxRTiles,  // [workgroup][P1 group]: tasks taken from the shared tail of its share
 };
-constexpr size_t kCtrlBytes = (size_t)(CTRL_P1 + kMaxStealG * 4) * kCtrlStride * sizeof(unsigned);
+constexpr size_t kCtrlBytes = (size_t)(CTRL_P1 + kMaxStealG * kP1Groups) * kCtrlStride * sizeof(unsigned);
 // small-regime logit buffers (two layer parities), right after the control words
 constexpr size_t kRlogOffset = (kCtrlBytes + 255u) & ~(size_t)255u;
 constexpr size_t kRlogBytes = (size_t)2 * kSmallB * kMaxE * sizeof(float);
@@ -147,6 +150,7 @@ struct Params {
   int mfma_sh;            // general regime: the router and the shared expert go through MFMA tiles
   int rq;                 // K parts of each router MFMA tile, one workgroup each
   int steal;              // general regime: P1 share tails taken through CTRL_P1 counters
+  int p1_groups;          // general regime: P1 groups (each closed by a barrier), at most kP1Groups
   int p0_end;             // P0 task indices in [0, p0_end): router slices, then shared slices (VALU)
   int NSR;                // router K-slices
   int NSS;                // shared gate/up K-slices
@@ -2722,7 +2726,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
       __syncthreads();
       build_tables(p, L);
       classify_slots(p, L);
-      const int nL = sh.nM + sh.nG, nGr = min(kP1Groups, nL);
+      const int nL = sh.nM + sh.nG, nGr = min(p->p1_groups, nL);
       const int *cpre = L.at<int>(p->o_cpre);
       for (int gi = 0; gi < nGr; ++gi) {
         const int ia = group_first_slot(cpre, nL, gi, nGr), ib = group_first_slot(cpre, nL, gi + 1, nGr);
@@ -3462,6 +3466,9 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
       const int ntr = (d->num_experts + 15) / 16;
       p.rq = p.mfma_sh ? std::max(1, std::min(kMaxRQ, p.G / ntr)) : 1;
     }
+    // general regime: a workgroup's P2 rows follow its P1 tasks, so extra
+    // groups mostly add barrier waits; 2 measured best up to 16 tokens, 3 above
+    p.p1_groups = std::min(kP1Groups, B <= 16 ? 2 : 3);
     // P1 tail stealing: bf16 experts (fp8 tasks are half as long, and the
     // workspace atomics measured a little slower there)
     p.steal = (!small && !route_only && MOE_P1_STEAL > 0 && p.G <= kMaxStealG && d->expert == MOE_BF16) ? 1 : 0;
