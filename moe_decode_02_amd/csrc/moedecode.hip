@@ -572,6 +572,10 @@ template <int WD, int TG> constexpr int seg_down() { return kLoadsPerStep / kDow
 #ifndef MOE_GEN_DOWN_SEG
 #define MOE_GEN_DOWN_SEG 1
 #endif
+#ifndef MOE_GEN_DOWN_ROWS_FP8
+#define MOE_GEN_DOWN_ROWS_FP8 4
+#endif
+
 template <int WD, int TG, bool XL> constexpr int seg_gu_r() { return XL ? seg_gu<WD, TG>() : MOE_GEN_GU_SEG; }
 template <int WD, int TG, bool XL> constexpr int seg_down_r() { return XL ? seg_down<WD, TG>() : MOE_GEN_DOWN_SEG; }
 // P0 (router and shared gate/up slices): loads per step
@@ -1492,23 +1496,23 @@ __device__ __forceinline__ void stage_shared_h_wave(KParams p, const Lds &L) {
 // the bf16 scale word sraw, common to the unit's rows) to
 // prow[(o0 + r - o0) * rs + col[t] * cs] (rs, cs: row and column strides of
 // the partial-sum buffer).
-template <int WD, int AD, bool XL, int TG>
+template <int WD, int AD, bool XL, int TG, int DR = kDownRows>
 __device__ __forceinline__ void down_unit(const char *const (&wrow)[kRowBlock], int K,
                                           const typename XSrc<XL>::ptr (&xr)[TG], uint32_t sraw,
                                           float *prow, int rs, int cs, const int (&col)[TG], int nt) {
 #pragma unroll
-  for (int r0 = 0; r0 < kRowBlock; r0 += kDownRows) {
-    const char *wr[kDownRows];
-    float acc[kDownRows][TG];
+  for (int r0 = 0; r0 < kRowBlock; r0 += DR) {
+    const char *wr[DR];
+    float acc[DR][TG];
 #pragma unroll
-    for (int r = 0; r < kDownRows; ++r) {
+    for (int r = 0; r < DR; ++r) {
       wr[r] = wrow[r0 + r];
 #pragma unroll
       for (int t = 0; t < TG; ++t) acc[r][t] = 0.f;
     }
-    rows_dot<WD, AD, XL, kDownRows, seg_down_r<WD, TG, XL>(), TG>(wr, 0, K, xr, acc);
+    rows_dot<WD, AD, XL, DR, seg_down_r<WD, TG, XL>(), TG>(wr, 0, K, xr, acc);
 #pragma unroll
-    for (int r = 0; r < kDownRows; ++r)
+    for (int r = 0; r < DR; ++r)
 #pragma unroll
       for (int t = 0; t < TG; ++t) {
         float v = wave_sum63(acc[r][t]);
@@ -1585,6 +1589,7 @@ __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Ld
 #ifndef MOE_MFMA_MIN
 #define MOE_MFMA_MIN 2
 #endif
+
 #ifndef MOE_MFMA_SHARED_MIN
 #define MOE_MFMA_SHARED_MIN 8
 #endif
@@ -2300,7 +2305,8 @@ __device__ __forceinline__ void expert_down_gemv(KParams p, KLayer lp, const Lds
       col[t] = pl[t0 + (t < nt ? t : 0)];
       xr[t] = (const char *)p->hbuf + (size_t)col[t] * I * dsz<AD>();
     }
-    down_unit<ED, AD, false, TG>(wrow, I, xr, sraw, prow, rs, cs, col, nt);
+    // fp8 rows are half as long: all 4 rows of the unit in one pass
+    down_unit<ED, AD, false, TG, ED == DT_FP8 ? MOE_GEN_DOWN_ROWS_FP8 : kDownRows>(wrow, I, xr, sraw, prow, rs, cs, col, nt);
   });
 }
 
