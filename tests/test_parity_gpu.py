@@ -164,6 +164,24 @@ def test_mfma_tiles_every_token(dev, expert, router, seed):
     log(f"mfma tiles ({expert}) max rel err {err:.2e}")
 
 
+@pytest.mark.parametrize("expert,seed", [(synth.BF16, 45), (synth.FP8, 47)])
+def test_mfma_tiles_three_and_four_token_tiles(dev, expert, seed):
+    """B=64 over 8 experts (top-4) with a Zipf router bias: experts get ~14
+    to ~60 tokens, so gate/up and down tiles run with 1 to 4 token tiles
+    (fp8 with 3-4: the product that loads the second step's activations
+    after the first step's MFMAs). Every token vs the oracle."""
+    w = small_workload(name="mfma_many", H=4096, E=8, k=4, I=256, Is=256, act=synth.BF16, router=synth.F32,
+                       expert=expert, shared=synth.BF16, seed=seed, zipf_s=1.1)
+    Lh = host_layer(w, experts=[])
+    x, _ = draw_tokens_with_margin(w, 64, [Lh])
+    idx_r, _, _ = oracle_routes(w, Lh, x)
+    counts = np.bincount(idx_r.ravel(), minlength=w.E)
+    log(f"mfma many-token test: expert token counts {sorted(counts.tolist(), reverse=True)}")
+    assert np.sum((counts > 32) & (counts <= 48)) >= 1 and np.sum(counts > 48) >= 1  # 3 and 4 token tiles
+    err = full_parity(w, 64, dev, poison=True)
+    log(f"3-4 token tiles ({expert}) max rel err {err:.2e}")
+
+
 @pytest.mark.parametrize("B,expert,seed", [(5, synth.BF16, 51), (7, synth.FP8, 53), (12, synth.BF16, 56)])
 def test_mfma_partial_token_tiles(dev, B, expert, seed):
     """Small batches over 8 experts (top-4): experts get 1 to ~10 tokens, so
