@@ -573,9 +573,8 @@ template <int WD, int TG> constexpr int seg_down() { return kLoadsPerStep / kDow
 #define MOE_GEN_DOWN_SEG 1
 #endif
 #ifndef MOE_GEN_DOWN_ROWS_FP8
-#define MOE_GEN_DOWN_ROWS_FP8 4
+#define MOE_GEN_DOWN_ROWS_FP8 4  // fp8 down units: rows per pass (all 4: one 4 KB step)
 #endif
-
 template <int WD, int TG, bool XL> constexpr int seg_gu_r() { return XL ? seg_gu<WD, TG>() : MOE_GEN_GU_SEG; }
 template <int WD, int TG, bool XL> constexpr int seg_down_r() { return XL ? seg_down<WD, TG>() : MOE_GEN_DOWN_SEG; }
 // P0 (router and shared gate/up slices): loads per step
@@ -1246,7 +1245,7 @@ __device__ __attribute__((noinline)) void topk_token(KParams p_arg, KLayer lp_ar
   unsigned thr = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const unsigned c = thr | (1u << bit);
-    if (__popcll(__ballot(omax >= c)) >= k) thr = c;
+    if (__popcll(__ballot(omax >= c)) >= (unsigned)k) thr = c;
   }
   // thr >= the key of -inf > 0: at least k lanes hold an expert
   int nc = 0;
@@ -1530,7 +1529,7 @@ __device__ __forceinline__ float *part_base(KParams p, const Lds &L) {
   if constexpr (SMALL) return L.at<float>(p->o_part);
   else return p->partbuf;
 }
-template <bool SMALL> __device__ __forceinline__ int part_rs(KParams p, int pstride) { return SMALL ? pstride : 1; }
+template <bool SMALL> __device__ __forceinline__ int part_rs(KParams, int pstride) { return SMALL ? pstride : 1; }
 template <bool SMALL> __device__ __forceinline__ int part_cs(KParams p) { return SMALL ? 1 : p->H; }
 
 // Next P2 unit of this wave, handed out through the workgroup's LDS counter
@@ -1589,7 +1588,6 @@ __device__ __forceinline__ void shared_down_units(KParams p, KLayer lp, const Ld
 #ifndef MOE_MFMA_MIN
 #define MOE_MFMA_MIN 2
 #endif
-
 #ifndef MOE_MFMA_SHARED_MIN
 #define MOE_MFMA_SHARED_MIN 8
 #endif
@@ -1653,12 +1651,8 @@ __device__ __forceinline__ unsigned line_chunk2() {
   const int l = lane_here();
   return (unsigned)(2 * (l >> 4) + ((l >> 3) & 1));
 }
-#ifndef MOE_XLINES
-#define MOE_XLINES 1
-#endif
-constexpr int kXH = MOE_XLINES ? 2 : 1;  // activation offsets per token tile
-// the lane's activation row of half h of a token tile (operand order: l%16)
-__device__ __forceinline__ int x_row(int h) { return MOE_XLINES ? line_row(h) : (lane_here() & 15); }
+constexpr int kXH = 2;  // activation offsets per token tile: rows line_row(0) and line_row(1)
+__device__ __forceinline__ int x_row(int h) { return line_row(h); }
 // in place: X becomes operand a, Y operand b
 __device__ __forceinline__ void lines_to_operands(u32x4 &X, u32x4 &Y) {
   const bool lo = (lane_id() & 8) == 0;
@@ -1681,8 +1675,7 @@ __device__ __forceinline__ void lines_to_operands(u32x4 &X, u32x4 &Y) {
 template <int NR, int NT>
 __device__ __forceinline__ void mfma_rows(const char *wbase, const unsigned (&woff)[NR][2], int K, const char *xbase,
                                           const unsigned (&xoff)[NT][kXH], f32x4 (&acc)[NR][NT]) {
-  const unsigned ch = line_chunk4() * 16u;                          // the lane's chunk of each row's line
-  const unsigned xq = MOE_XLINES ? ch : ((unsigned)lane_here() >> 4) * 16u;  // operand order: chunk kq
+  const unsigned ch = line_chunk4() * 16u;  // the lane's chunk of each row's line
   for (int k0 = 0; k0 < K; k0 += 64) {
     u32x4 w[NR][2], x[NT][2];
 #pragma unroll
@@ -1692,22 +1685,16 @@ __device__ __forceinline__ void mfma_rows(const char *wbase, const unsigned (&wo
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if constexpr (MOE_XLINES) {
-        x[t][0] = ld16(xbase, xoff[t][0] + (unsigned)k0 * 2u + xq);
-        x[t][1] = ld16(xbase, xoff[t][kXH - 1] + (unsigned)k0 * 2u + xq);
-      } else {  // chunks kq and 4 + kq of the token's line
-        x[t][0] = ld16(xbase, xoff[t][0] + (unsigned)k0 * 2u + xq);
-        x[t][1] = ld16(xbase, xoff[t][0] + (unsigned)k0 * 2u + xq + 64u);
-      }
+      x[t][0] = ld16(xbase, xoff[t][0] + (unsigned)k0 * 2u + ch);
+      x[t][1] = ld16(xbase, xoff[t][1] + (unsigned)k0 * 2u + ch);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     mfma_wait(w);
     mfma_wait(x);
 #pragma unroll
     for (int r = 0; r < NR; ++r) lines_to_operands(w[r][0], w[r][1]);
-    if constexpr (MOE_XLINES)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) lines_to_operands(x[t][0], x[t][1]);
+    for (int t = 0; t < NT; ++t) lines_to_operands(x[t][0], x[t][1]);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -1742,24 +1729,17 @@ __device__ __forceinline__ void mfma_rows_fp8x2(const char *wbase, const unsigne
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if constexpr (MOE_XLINES) {
-          const unsigned cb = ((unsigned)k0 + 64u * (unsigned)st) * 2u + xc;
-          x[st * NT + t][0] = ld16(xbase, xoff[t][0] + cb);
-          x[st * NT + t][1] = ld16(xbase, xoff[t][kXH - 1] + cb);
-        } else {
-          const unsigned c = (unsigned)k0 + 64u * (unsigned)st + ((unsigned)lane_here() >> 4) * 16u;
-          x[st * NT + t][0] = ld16(xbase, xoff[t][0] + c * 2u);
-          x[st * NT + t][1] = ld16(xbase, xoff[t][0] + (c + 8u) * 2u);
-        }
+        const unsigned cb = ((unsigned)k0 + 64u * (unsigned)st) * 2u + xc;
+        x[st * NT + t][0] = ld16(xbase, xoff[t][0] + cb);
+        x[st * NT + t][1] = ld16(xbase, xoff[t][1] + cb);
       }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     mfma_wait(w);
     mfma_wait(x);
 #pragma unroll
     for (int r = 0; r < NR; ++r) lines_to_operands(w[r][0], w[r][1]);
-    if constexpr (MOE_XLINES)
 #pragma unroll
-      for (int i = 0; i < 2 * NT; ++i) lines_to_operands(x[i][0], x[i][1]);
+    for (int i = 0; i < 2 * NT; ++i) lines_to_operands(x[i][0], x[i][1]);
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -1790,7 +1770,7 @@ __device__ __forceinline__ void mfma_rows_fp8_split(const char *wbase, const uns
   const bool hs = (lane_here() & 8) != 0;
   unsigned xs[NT];  // the lane's token row l%16 of each token tile
 #pragma unroll
-  for (int t = 0; t < NT; ++t) xs[t] = hs ? xoff[t][kXH - 1] : xoff[t][0];
+  for (int t = 0; t < NT; ++t) xs[t] = hs ? xoff[t][1] : xoff[t][0];
   for (int k0 = 0; k0 < K; k0 += 128) {
     u32x4 w[NR][2];
 #pragma unroll
@@ -1855,7 +1835,7 @@ __device__ __forceinline__ void with_token_tiles(int n, F &&f) {
 template <int AD, int ED>
 __device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L, int u, int jb) {
   dbg_delay(p, DLY_P1, u * 4096 + jb);
-  const int H = p->H, I = p->I, k = p->k, lane = lane_id();
+  const int H = p->H, I = p->I, k = p->k;
   const int *ulist = L.at<int>(p->o_ulist), *ucnt = L.at<int>(p->o_ucnt), *ustart = L.at<int>(p->o_ustart);
   const int *pl = L.at<int>(p->o_plist) + ustart[u];
   const int e = ulist[u], n = ucnt[u];
@@ -2316,7 +2296,7 @@ __device__ __forceinline__ void expert_down_gemv(KParams p, KLayer lp, const Lds
 template <int AD, int ED, bool SMALL>
 __device__ __forceinline__ void expert_down_units(KParams p, KLayer lp, const Lds &L, int pr0, int pr1, int ua, int ub,
                                                   int uc) {
-  const int I = p->I, B = p->B;
+  const int B = p->B;
   const int nsh = p->nsh, P = B * p->k, pstride = P + B * nsh;
   const int nrb = (pr1 - pr0) / kRowBlock;
   float *part = part_base<SMALL>(p, L);
