@@ -150,6 +150,7 @@ struct Params {
   int mfma_sh;            // general regime: the router and the shared expert go through MFMA tiles
   int rq;                 // K parts of each router MFMA tile, one workgroup each
   int steal;              // general regime: P1 share tails taken through CTRL_P1 counters
+  int tail_div;           // general regime: 1 / tail_div of each workgroup's P1 share is its stealable tail
   int p1_groups;          // general regime: P1 groups (each closed by a barrier), at most kP1Groups
   int p0_end;             // P0 task indices in [0, p0_end): router slices, then shared slices (VALU)
   int NSR;                // router K-slices
@@ -2504,14 +2505,14 @@ __device__ __forceinline__ void p1_claimed(KParams p, KLayer lp, const Lds &L, i
 #define MOE_P1_STEAL 4
 #endif
 #ifndef MOE_P1_TAIL_DIV
-#define MOE_P1_TAIL_DIV 4  // a quarter of each share is in its tail
+#define MOE_P1_TAIL_DIV 0  // 0: p->tail_div (a quarter of each share up to 16 tokens, a third above)
 #endif
 __device__ __forceinline__ void p1_share(KParams p, const Lds &L, int ia, int ib, int Clo, int Chi, int v, int &t0,
                                          int &tm, int &t1) {
   const int NW = p->G * kWaves;
   t0 = p1_task_at_cost(p, L, ia, ib, Clo + share_lo(Chi - Clo, v * kWaves, NW));
   t1 = p1_task_at_cost(p, L, ia, ib, Clo + share_lo(Chi - Clo, (v + 1) * kWaves, NW));
-  tm = t1 - (t1 - t0) / MOE_P1_TAIL_DIV;
+  tm = t1 - (t1 - t0) / (MOE_P1_TAIL_DIV > 0 ? MOE_P1_TAIL_DIV : p->tail_div);
 }
 template <int AD, int ED>
 __device__ __forceinline__ void p1_stealing(KParams p, KLayer lp, const Lds &L, int ia, int ib, int Clo, int Chi,
@@ -3458,6 +3459,9 @@ moe_status launch(const moe_layer_desc *d, const moe_layer_weights *layers, int 
     // P1 tail stealing: bf16 experts (fp8 tasks are half as long, and the
     // workspace atomics measured a little slower there)
     p.steal = (!small && !route_only && MOE_P1_STEAL > 0 && p.G <= kMaxStealG && d->expert == MOE_BF16) ? 1 : 0;
+    // the stealable tail: a quarter of a share up to 16 tokens, a third above
+    // (where a share holds fewer, longer MFMA tiles)
+    p.tail_div = B <= 16 ? 4 : 3;
     // the slices of a row are one workgroup's waves of one round: the shared
     // tasks start at a multiple of the workgroup's wave count, and the rounds
     // must fit the per-round slice counters and LDS slots (else every row is
