@@ -2369,10 +2369,21 @@ __device__ __forceinline__ void combine(KParams p, KLayer lp, const Lds &L, int 
     const int o = pr0 + ro;
     const int cs = part_cs<SMALL>(p);
     const float *pp = part + (size_t)(o - prb) * part_rs<SMALL>(p, pstride);
+    // a cell's partial sums are loaded 8 at a time before they are used (one
+    // at a time they were k + nsh dependent round trips); the sums keep
+    // their order
     float sh = 0.f;
     for (int hf = 0; hf < nsh; ++hf) sh += pp[(size_t)(P + t * nsh + hf) * cs];
     float rt = 0.f;
-    for (int i = 0; i < k; ++i) rt = fmaf(sel_w[t * k + i], pp[(size_t)(t * k + i) * cs], rt);
+    for (int i0 = 0; i0 < k; i0 += 8) {
+      float pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pv[j] = pp[(size_t)(t * k + min(i0 + j, k - 1)) * cs];
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (i0 + j < k) rt = fmaf(sel_w[t * k + i0 + j], pv[j], rt);
+    }
     // after a watchdog stop the rows are not trusted: NaN makes that visible in y
     const float v = poison ? __builtin_nanf("") : load_act<AD>(lp->x, (size_t)t * H + o) + sh + rt;
     if (pub) publish_act<AD>(lp->y, (size_t)t * H + o, v);
