@@ -40,14 +40,13 @@
 // atomics), so identical router rows give bit-identical logits and repeated
 // runs give identical outputs.
 //
-// Memory ordering across the 8 XCDs: every wave releases its stores at
-// workgroup scope and counts itself in LDS; the workgroup's last wave adds one
-// to the barrier's global counter, after an agent-scope release (L2
-// write-back) where plain stores must reach other XCDs (B > 2), or with none
-// where every value other workgroups read went out through device-coherent
-// stores (B <= 2, and the barrier between stack layers). One wave per
-// workgroup polls the counter, acquires at agent scope and raises an LDS flag
-// for the others. Weights are static and may be loaded before a barrier;
+// Memory ordering across the 8 XCDs: every value one workgroup writes for
+// others (x-hat, logits, shared and expert h, the next layer's x) goes out
+// through device-coherent stores, written through past the XCD's L2. A wave
+// arriving at a barrier waits for its own stores to complete and counts
+// itself in LDS; the workgroup's last wave adds one to the barrier's global
+// counter, with no L2 write-back. One wave per workgroup polls the counter,
+// acquires at agent scope and raises an LDS flag for the others. Weights are static and may be loaded before a barrier;
 // activations are read only after it (a compiler that hoisted an activation
 // load above a sync wait was one of the bugs found in the pages' review:
 // aiposthub.com article, section on how vLLM verifies AI-written kernels).
@@ -606,10 +605,12 @@ __device__ __forceinline__ long long rt_now() { return (long long)__builtin_amdg
 
 __device__ __forceinline__ unsigned *ctrl_word(KParams p, int w) { return p->ctrl + (size_t)w * kCtrlStride; }
 
-// Small regime: values other workgroups read after a barrier are written
-// with device-coherent stores (write-through past this XCD's L2), so the
-// barrier does not need an L2 write-back, which costs several microseconds
-// per workgroup while the memory system is streaming.
+// Values other workgroups read after a barrier are written with
+// device-coherent stores (write-through past this XCD's L2), so no barrier
+// needs an L2 write-back, which costs several microseconds per workgroup
+// while the memory system is streaming (a workgroup's last wave wrote back
+// 5-12 us after its router unit at 8 tokens, when the general regime still
+// used it).
 // +0 as -0 (equal in every comparison and product), so that all-zero bits
 // can mark a value not yet written
 __device__ __forceinline__ float nonzero_bits(float v) { return __float_as_uint(v) == 0u ? -0.0f : v; }
@@ -636,23 +637,6 @@ __device__ void bar_arrive_published(KParams p, SmemHead &sh, int b) {
     const int old = __hip_atomic_fetch_add(&sh.bar_cnt[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (old == kWaves - 1)
       __hip_atomic_fetch_add(ctrl_word(p, CTRL_BAR + b), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// A wave is done with the work barrier b waits for. Each wave first waits for
-// its own stores to reach the L2 (a workgroup-scope release does not wait for
-// them), so the last wave's L2 write-back covers every wave's stores.
-__device__ void bar_arrive(KParams p, SmemHead &sh, int b) {
-  dbg_delay(p, DLY_ARRIVE, b);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  if (lane_id() == 0) {
-    const int old = __hip_atomic_fetch_add(&sh.bar_cnt[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (old == kWaves - 1) {
-      // the whole workgroup's stores are in this XCD's L2: write them back for the other XCDs
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __hip_atomic_fetch_add(ctrl_word(p, CTRL_BAR + b), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
 }
 
@@ -914,6 +898,18 @@ __device__ __forceinline__ void publish16(void *q, const u32x4 &v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(q), "v"(v) : "memory");
 }
 
+// elements i .. i + 3 of an act-dtype array (i a multiple of 4), published
+// with one store
+template <int D> __device__ __forceinline__ void publish_act4(void *p, size_t i, const float (&v)[4]) {
+  if constexpr (D == DT_F32) {
+    publish16((float *)p + i, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+  } else {
+    const u32x2 w = {(uint32_t)f32_to_bf16(v[0]) | (uint32_t)f32_to_bf16(v[1]) << 16,
+                     (uint32_t)f32_to_bf16(v[2]) | (uint32_t)f32_to_bf16(v[3]) << 16};
+    asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"((uint16_t *)p + i), "v"(w) : "memory");
+  }
+}
+
 // General regime: workgroup t normalises token t into global memory, fp32
 // (the router's input) and in the act dtype (the FFNs'), published.
 template <int AD>
@@ -1029,7 +1025,7 @@ __device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, 
         if (NSR == 1) {
           dbg_delay(p, DLY_PUBLISH, e);
           if constexpr (XL) publish(lp->lg + (size_t)(t0 + t) * E + e, nonzero_bits(v + bias));
-          else lp->lg[(size_t)(t0 + t) * E + e] = v + bias;
+          else publish(lp->lg + (size_t)(t0 + t) * E + e, v + bias);
         } else {
           slice_slot(p, L, round, wave_id())[t0 + t] = v;
         }
@@ -1043,7 +1039,7 @@ __device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, 
       float sum = slice_slot(p, L, round, w0)[t];
       for (int s2 = 1; s2 < NSR; ++s2) sum += slice_slot(p, L, round, w0 + s2)[t];
       if constexpr (XL) publish(lp->lg + (size_t)t * E + e, nonzero_bits(sum + bias));
-      else lp->lg[(size_t)t * E + e] = sum + bias;
+      else publish(lp->lg + (size_t)t * E + e, sum + bias);
     }
   }
 }
@@ -1052,7 +1048,7 @@ __device__ __forceinline__ void router_task(KParams p, KLayer lp, const Lds &L, 
 template <int AD, bool XL>
 __device__ __forceinline__ void shared_h_out(KParams p, size_t i, float h) {
   if constexpr (XL) publish(p->hsh32 + i, round_act<AD>(h));
-  else store_act<AD>(p->hsbuf, i, h);
+  else publish_act<AD>(p->hsbuf, i, h);
 }
 
 // shared gate/up task tau = (pair j, slice s) of round `round`. Several
@@ -1449,9 +1445,7 @@ __device__ __forceinline__ void expert_gu_task(KParams p, KLayer lp, const Lds &
       }
       if (t < nt && lane_id() == 63) {
         const float h = silu_mul(g, uu);
-        // h in the act dtype (published in the small regime)
-        if constexpr (XL) publish_act<AD>(p->hbuf, (size_t)slot[t] * I + j, h);
-        else store_act<AD>(p->hbuf, (size_t)slot[t] * I + j, h);
+        publish_act<AD>(p->hbuf, (size_t)slot[t] * I + j, h);  // h in the act dtype, published
       }
     }
   });
@@ -1875,10 +1869,10 @@ __device__ __forceinline__ void mfma_gu_task(KParams p, KLayer lp, const Lds &L,
       const int c = 16 * t + r;
       if (c < n) {
         const int slot = pl[c];
+        float h[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          store_act<AD>(p->hbuf, (size_t)slot * I + 16 * jb + 4 * kq + i,
-                        silu_mul(acc[0][t][i] * late_scale(graw), acc[1][t][i] * late_scale(uraw)));
+        for (int i = 0; i < 4; ++i) h[i] = silu_mul(acc[0][t][i] * late_scale(graw), acc[1][t][i] * late_scale(uraw));
+        publish_act4<AD>(p->hbuf, (size_t)slot * I + 16 * jb + 4 * kq, h);
       }
     }
   });
@@ -2095,7 +2089,7 @@ __device__ __attribute__((noinline)) void router_mfma(KParams p_arg, KLayer lp_a
         if (e < E) {
           float sum = 0.f;
           for (int q2 = 0; q2 < RQ; ++q2) sum += p->rpart[((size_t)q2 * B + t) * E + e];
-          lp->lg[(size_t)t * E + e] = sum + (lp->rb ? lp->rb[e] : 0.f);
+          publish(lp->lg + (size_t)t * E + e, sum + (lp->rb ? lp->rb[e] : 0.f));
         }
       }
       if (tid == 0) __hip_atomic_store(ctrl_word(p, CTRL_RTILE + tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2151,7 +2145,7 @@ __device__ __attribute__((noinline)) void shared_gu_mfma(KParams p_arg, KLayer l
         g += red[(size_t)(w * 16 + jj) * B + t];
         u += red[(size_t)(w * 16 + 8 + jj) * B + t];
       }
-      store_act<AD>(p->hsbuf, (size_t)t * Is + 8 * j + jj, silu_mul(g, u));
+      publish_act<AD>(p->hsbuf, (size_t)t * Is + 8 * j + jj, silu_mul(g, u));
     }
     __syncthreads();
   }
@@ -2429,7 +2423,7 @@ __device__ __forceinline__ void p0_tasks(KParams p, KLayer lp, const Lds &L, int
     const int tau = p0_task(p, r, wg_id(p), wave_id());
     if (tau < 0 || tau >= end) break;
     if (tau >= nrt && !routed) {
-      if constexpr (!PUB) bar_arrive(p, sh, b0 + BAR_ROUTER);
+      if constexpr (!PUB) bar_arrive_published(p, sh, b0 + BAR_ROUTER);
       routed = true;
     }
     if (tau < nrt) router_task_any<AD, RD, PUB>(p, lp, L, tau, r);
@@ -2439,9 +2433,9 @@ __device__ __forceinline__ void p0_tasks(KParams p, KLayer lp, const Lds &L, int
     bar_arrive_published(p, sh, b0 + BAR_SHARED);
   } else {
     if constexpr (MSH) router_mfma<RD>(p, lp, L);
-    if (!routed) bar_arrive(p, sh, b0 + BAR_ROUTER);
+    if (!routed) bar_arrive_published(p, sh, b0 + BAR_ROUTER);
     if constexpr (MSH) shared_gu_mfma<AD>(p, lp, L);
-    bar_arrive(p, sh, b0 + BAR_SHARED);
+    bar_arrive_published(p, sh, b0 + BAR_SHARED);
   }
 }
 
@@ -2684,8 +2678,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
         bar_wait(p, sh, b0 + BAR_XHAT);
       }
       for (int tau = W, r = 0; tau < p->E * p->NSR; tau += NW, ++r) router_task_any<AD, RD, SMALL>(p, lp, L, tau, r);
-      if constexpr (SMALL) bar_arrive_published(p, sh, b0 + BAR_ROUTER);
-      else bar_arrive(p, sh, b0 + BAR_ROUTER);
+      bar_arrive_published(p, sh, b0 + BAR_ROUTER);
       bar_wait(p, sh, b0 + BAR_ROUTER);
       poisoned = err_word(p) != 0;
       if (wg_id(p) == 0)
@@ -2736,7 +2729,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
           const int hi = Clo + share_lo(Chi - Clo, (g + 1) * kWaves, NW);
           p1_claimed<AD, ED>(p, lp, L, p1_task_at_cost(p, L, ia, ib, lo), p1_task_at_cost(p, L, ia, ib, hi), gi);
         }
-        bar_arrive(p, sh, b0 + BAR_H + gi);
+        bar_arrive_published(p, sh, b0 + BAR_H + gi);
       }
 
       // P2: this workgroup's output rows, partial sums in global memory; the
