@@ -1699,6 +1699,52 @@ __device__ __forceinline__ void mfma_rows(const char *wbase, const unsigned (&wo
   }
 }
 
+// mfma_rows with S 64-column steps per wait, for short K ranges whose steps
+// would otherwise each be a round trip (K a multiple of 64; the last wait's
+// steps past K load step K - 64 again, passed through the wait and unused).
+// The MFMAs run step by step, so the results equal mfma_rows'.
+template <int NR, int NT, int S>
+__device__ __forceinline__ void mfma_rows_multi(const char *wbase, const unsigned (&woff)[NR][2], int K,
+                                                const char *xbase, const unsigned (&xoff)[NT][kXH],
+                                                f32x4 (&acc)[NR][NT]) {
+  const unsigned ch = line_chunk4() * 16u;
+  for (int k0 = 0; k0 < K; k0 += 64 * S) {
+    u32x4 w[S * NR][2], x[S * NT][2];
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+      const unsigned kb = (unsigned)min(k0 + 64 * st, K - 64) * 2u + ch;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        w[st * NR + r][0] = ld16_nt(wbase, woff[r][0] + kb);
+        w[st * NR + r][1] = ld16_nt(wbase, woff[r][1] + kb);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        x[st * NT + t][0] = ld16(xbase, xoff[t][0] + kb);
+        x[st * NT + t][1] = ld16(xbase, xoff[t][1] + kb);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    mfma_wait(w);
+    mfma_wait(x);
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+      if (k0 + 64 * st < K) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) lines_to_operands(w[st * NR + r][0], w[st * NR + r][1]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) lines_to_operands(x[st * NT + t][0], x[st * NT + t][1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[r][t] = mfma16(w[st * NR + r][h], x[st * NT + t][h], acc[r][t]);
+      }
+    }
+  }
+}
+
 // fp8 weights (up to 2 token tiles): the same product with two 64-column
 // steps per wait (K a multiple of 128), so that a row's 128 codes are one
 // line: chunks kq and 4 + kq feed steps 0 and 1, and the activation's
@@ -2000,50 +2046,54 @@ __device__ __attribute__((noinline)) void router_mfma(KParams p_arg, KLayer lp_a
       f32x4 acc[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // two 16-column blocks per wait
-      for (int blk = b0; blk < b1; blk += 2) {
-        const int blk2 = blk + 1 < b1 ? blk + 1 : blk;  // a lone last block loads itself twice, used once
-        const unsigned c[2] = {(unsigned)blk * 16u, (unsigned)blk2 * 16u};
-        u32x4 x[2][NT];
-        float wf[2][4];
+      // RB 16-column blocks per wait (a wave's share is 7 blocks at H = 7168
+      // and 4 K parts); blocks past b1 load block b1 - 1 again, unused
+      constexpr int RB = NT == 1 ? 8 : NT == 2 ? 4 : 2;
+      for (int blk = b0; blk < b1; blk += RB) {
+        unsigned c[RB];
+#pragma unroll
+        for (int h = 0; h < RB; ++h) c[h] = (unsigned)min(blk + h, b1 - 1) * 16u;
+        u32x4 x[RB][NT];
+        float wf[RB][4];
         if constexpr (RD == DT_F32) {
-          u32x4 w[2];
+          u32x4 w[RB];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) w[h] = ld16_nt(uni(wb), wo + c[h] * 4u);
+          for (int h = 0; h < RB; ++h) w[h] = ld16_nt(uni(wb), wo + c[h] * 4u);
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+          for (int h = 0; h < RB; ++h)
 #pragma unroll
             for (int t = 0; t < NT; ++t) x[h][t] = ld16(uni(xb), xo[t] + c[h] * 4u);
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          u32x4 wt[1][2] = {{w[0], w[1]}};
+          u32x4 wt[1][RB];
+#pragma unroll
+          for (int h = 0; h < RB; ++h) wt[0][h] = w[h];
           mfma_wait(wt);
           mfma_wait(x);
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
+          for (int h = 0; h < RB; ++h) {
             wf[h][0] = __uint_as_float(wt[0][h].x); wf[h][1] = __uint_as_float(wt[0][h].y);
             wf[h][2] = __uint_as_float(wt[0][h].z); wf[h][3] = __uint_as_float(wt[0][h].w);
           }
         } else {
-          u32x2 w[2];
+          u32x2 w[RB];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) w[h] = ld8_nt(uni(wb), wo + c[h] * 2u);
+          for (int h = 0; h < RB; ++h) w[h] = ld8_nt(uni(wb), wo + c[h] * 2u);
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+          for (int h = 0; h < RB; ++h)
 #pragma unroll
             for (int t = 0; t < NT; ++t) x[h][t] = ld16(uni(xb), xo[t] + c[h] * 4u);
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           mfma_wait2(w);
           mfma_wait(x);
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
+          for (int h = 0; h < RB; ++h) {
             wf[h][0] = bf_lo(w[h].x); wf[h][1] = bf_hi(w[h].x);
             wf[h][2] = bf_lo(w[h].y); wf[h][3] = bf_hi(w[h].y);
           }
         }
-        const int nh = blk2 != blk ? 2 : 1;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          if (h < nh) {
+        for (int h = 0; h < RB; ++h) {
+          if (blk + h < b1) {
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -2102,6 +2152,7 @@ __device__ __attribute__((noinline)) void router_mfma(KParams p_arg, KLayer lp_a
 // j is one 16-row A operand: gate rows [8j, 8j + 8) over up rows [8j, 8j + 8),
 // so that g and u of one h element land in the same tile; workgroup g takes
 // tiles g, g + G, ..., and its waves split K in 64-column steps.
+template <int NT> constexpr int kSharedSteps() { return NT == 1 ? 4 : NT == 2 ? 2 : 1; }
 __device__ __forceinline__ int shared_tile_row(int Is, int j, int r) { return r < 8 ? 8 * j + r : Is + 8 * j + r - 8; }
 __device__ __forceinline__ int shared_tile_k(int H, int w) { return share_lo(H / 64, w, kWaves) * 64; }
 
@@ -2126,7 +2177,8 @@ __device__ __attribute__((noinline)) void shared_gu_mfma(KParams p_arg, KLayer l
       f32x4 acc[1][NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mfma_rows<1, NT>(uni(wb), wo, k1 - k0, uni(xa), xo, acc);
+      // a wave's share is a few steps (7 at H = 7168): up to 4 per wait
+      mfma_rows_multi<1, NT, kSharedSteps<NT>()>(uni(wb), wo, k1 - k0, uni(xa), xo, acc);
       const int r = lane_here() & 15, kq = lane_here() >> 4;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
