@@ -2004,6 +2004,31 @@ __device__ __forceinline__ int router_unit_blk(KParams p, int q, int w) {
   return q0 + share_lo(q1 - q0, w, kWaves);
 }
 
+// Before the x-hat wait (general regime): one dword of every 128-byte line
+// of this wave's share of its workgroup's first router unit is loaded, so
+// that the unit's loads after the barrier find its lines in L2 instead of
+// waiting on HBM while the barrier is pending anyway. Router weights are
+// static, so loading them before a barrier is safe.
+template <int RD>
+__device__ __forceinline__ void router_touch(KParams p, KLayer lp) {
+  const int u = wg_id(p);
+  if (u >= router_units(p)) return;
+  const int tile = u / p->rq, q = u % p->rq, wv = wave_id();
+  const size_t lo = (size_t)router_unit_blk(p, q, wv) * 16 * dsz<RD>();
+  const size_t hi = (size_t)router_unit_blk(p, q, wv + 1) * 16 * dsz<RD>();
+  if (lo >= hi) return;
+  const size_t l0 = lo & ~(size_t)127;
+  const int nl = (int)((hi - l0 + 127) / 128);  // lines of each of the tile's 16 rows
+  const size_t row_bytes = (size_t)p->H * dsz<RD>();
+  for (int i = lane_id(); i < 16 * nl; i += 64) {
+    const int row = min(16 * tile + i % 16, p->E - 1);
+    const char *a = (const char *)lp->rw + (size_t)row * row_bytes + l0 + (size_t)128 * (i / 16);
+    unsigned v;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(a) : "memory");
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(v) : : "memory");
+  }
+}
+
 // Router tile: v_mfma_f32_16x16x4_f32 with lane l holding A[l%16][l/16] and
 // B[l/16][l%16] in fp32 (bf16 router weights widen exactly). In a 16-column
 // block lane l loads columns 4(l/16) .. 4(l/16)+3 of its expert row and of
@@ -2752,6 +2777,7 @@ __global__ void __launch_bounds__(kThreads, 1) moe_kernel(Params params) {
                            __HIP_MEMORY_SCOPE_AGENT);
       produce_xhat<AD>(p, lp, L);
       bar_arrive_published(p, sh, b0 + BAR_XHAT);
+      if constexpr (MSH) router_touch<RD>(p, lp);
       bar_wait(p, sh, b0 + BAR_XHAT);
 
       // P0: router slices, then shared gate/up
