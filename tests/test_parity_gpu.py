@@ -201,6 +201,22 @@ def test_mfma_partial_token_tiles(dev, B, expert, E, seed):
     log(f"partial token tiles B={B} ({expert}) max rel err {err:.2e}")
 
 
+@pytest.mark.parametrize("B,expert,router,seed", [(24, synth.BF16, synth.F32, 61), (24, synth.FP8, synth.BF16, 62),
+                                                   (40, synth.BF16, synth.F32, 63), (40, synth.FP8, synth.BF16, 64)])
+def test_mfma_start_two_and_three_token_tiles(dev, B, expert, router, seed):
+    """The MFMA start (router units and shared gate/up tiles, bf16
+    activations from 8 tokens when every workgroup owns >= 16 output rows)
+    with 2 and 3 token tiles, which load 4 and 2 router blocks and 2 and 1
+    shared steps per wait. At H=5120 a wave's K share is 5 shared steps and
+    2-3 router blocks, so a last wait also loads steps past its share's end
+    (loaded again, unused). fp32 and bf16 router weights. Every token vs the
+    oracle."""
+    w = small_workload(name="mfma_start", H=5120, E=16, k=4, I=256, Is=256, act=synth.BF16, router=router,
+                       expert=expert, shared=synth.BF16, seed=seed)
+    err = full_parity(w, B, dev, poison=True)
+    log(f"MFMA start B={B} ({expert}, router {router}) max rel err {err:.2e}")
+
+
 @pytest.mark.parametrize("case", ["max_experts_k32", "k1_no_shared", "k_equals_E", "max_hidden"])
 def test_envelope_edges(dev, case):
     """Edges of the envelope and degenerate layers, every token vs the oracle:
